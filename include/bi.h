@@ -1,0 +1,195 @@
+/*
+ * bi.h — batch-invariant dense contractions for AMD Instinct MI355X (gfx950).
+ *
+ * Every entry point computes each output row with a reduction order fixed by
+ * the operation's own shape parameters that do not count requests (K, the
+ * kernel size, the sequence length) and never by the batch dimension (M, G,
+ * N of the convolution, B of decode): the same request gives the same bits
+ * whether it is computed alone or inside any batch.  The method follows the
+ * persistent matmul of "Unmasking the True Culprit: Why Temperature=0 Doesn't
+ * Mean Deterministic LLM Inference" (section "Technical Deep Dive: Batch
+ * Invariant Kernels": fixed tile configuration per dtype, float32 tile
+ * accumulation, ascending K loop, no split-K), the per-sample Conv2d and
+ * batched matmul of "Batch-Invariant Kernel Design: Conv2d and Attention BMM"
+ * (sections "Kernel 1: Conv2d" and "Kernel 2: Attention BMM"), and the
+ * fixed-length split-KV decoding of the deterministic-inference handbook
+ * page (anrans.github.io, section "根源：浮点加法的顺序" and the list of
+ * batch-invariant rules after it).
+ *
+ * Conventions shared by every call
+ *   - Plain C ABI; all data pointers are DEVICE pointers; all strides are
+ *     int64 ELEMENT strides.  `stream` is a hipStream_t passed as void*
+ *     (NULL = the default stream).  Work is enqueued on that stream and the
+ *     library never synchronises.
+ *   - Ownership: the caller owns every buffer, outputs and workspaces
+ *     included.  The library allocates no device memory and keeps no mutable
+ *     global state (it caches the read-only compute-unit count per device).
+ *   - Dtypes: BI_F32 = IEEE binary32, BI_BF16 = bfloat16.  Accumulation is
+ *     always binary32.  bfloat16 outputs are the binary32 result rounded to
+ *     nearest-even, bit for bit the same as rounding the BI_F32 output.
+ *   - Errors: arguments are checked on the host before anything is enqueued;
+ *     a negative bi_status is returned and nothing runs.  A failed launch
+ *     returns BI_ERR_LAUNCH.  Faults inside a kernel surface at the caller's
+ *     next synchronisation.  No exception crosses the ABI.
+ *   - Outputs must not overlap inputs.
+ */
+#ifndef BI_H
+#define BI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { BI_F32 = 0, BI_BF16 = 1 } bi_dtype;
+
+typedef enum {
+    BI_OK = 0,
+    BI_ERR_NULL = -1,        /* a required pointer is NULL */
+    BI_ERR_SHAPE = -2,       /* negative or inconsistent sizes */
+    BI_ERR_DTYPE = -3,       /* dtype code not accepted by this entry point */
+    BI_ERR_LAYOUT = -4,      /* strides / alignment the kernels do not take */
+    BI_ERR_UNSUPPORTED = -5, /* valid request outside what is implemented */
+    BI_ERR_WORKSPACE = -6,   /* workspace NULL, too small or misaligned */
+    BI_ERR_LAUNCH = -7,      /* the HIP runtime refused a launch or query */
+    BI_ERR_DEVICE = -8       /* no usable gfx950 device is current */
+} bi_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* bi_status_string(int status);
+
+/*
+ * bi_mm — C[M,N] = A[M,K] @ B[K,N].
+ * Source: "Unmasking the True Culprit ..." section "Technical Deep Dive:
+ * Batch Invariant Kernels" (persistent matmul kernel and its host wrapper).
+ *
+ * A: element (i,k) at A[i*sAm + k*sAk]; B: (k,j) at B[k*sBk + j*sBn];
+ * C: (i,j) at C[i*sCm + j*sCn].  in_dtype is the dtype of A and B,
+ * out_dtype the dtype of C.
+ * Reduction: k ascending in fixed steps of the dtype's K tile; each output
+ * tile is owned by one workgroup from the first k to the last (no split-K,
+ * no atomics).  Row i of C depends only on row i of A, B, K and the dtypes.
+ * Layout accepted:
+ *   BI_BF16: sAk == 1, sAm % 8 == 0, A 16-byte aligned, K % 8 == 0;
+ *            B either K-contiguous (sBk == 1, sBn % 8 == 0) or N-contiguous
+ *            (sBn == 1, sBk % 8 == 0, N % 8 == 0), 16-byte aligned;
+ *            C with sCn == 1.
+ *   BI_F32:  any non-negative strides; C with sCn == 1.
+ * M == 0 or N == 0 is a no-op; K == 0 writes zeros.
+ */
+int bi_mm(int64_t M, int64_t N, int64_t K,
+          const void* A, int64_t sAm, int64_t sAk,
+          const void* B, int64_t sBk, int64_t sBn,
+          void* C, int64_t sCm, int64_t sCn,
+          int in_dtype, int out_dtype, void* stream);
+
+/*
+ * bi_addmm — C = A @ B + bias, bias [N] of in_dtype broadcast over rows
+ * (beta = alpha = 1, the only form the method registers).  The bias is
+ * widened to binary32 and added once, after the last K step, then the sum is
+ * rounded once to out_dtype.  bias == NULL gives bi_mm.
+ * Source: as bi_mm; the wrapper's bias argument and the addmm override in
+ * "Integration with PyTorch: The torch.Library Approach".
+ * Layout rules: as bi_mm; bias is contiguous and, for BI_BF16, 16-byte aligned.
+ */
+int bi_addmm(int64_t M, int64_t N, int64_t K,
+             const void* A, int64_t sAm, int64_t sAk,
+             const void* B, int64_t sBk, int64_t sBn,
+             const void* bias,
+             void* C, int64_t sCm, int64_t sCn,
+             int in_dtype, int out_dtype, void* stream);
+
+/*
+ * bi_bmm — C[g] = A[g] @ B[g] for g in [0, G).
+ * Source: "Batch-Invariant Kernel Design: Conv2d and Attention BMM", section
+ * "Kernel 2: Attention BMM": every batch element gets its own base pointers
+ * and the same ordered K reduction, so adding elements adds independent work.
+ * Slice g of the result is bit-identical to bi_mm on A[g], B[g] alone.
+ * Element strides sAg, sBg, sCg step between slices (0 broadcasts an operand).
+ * Layout rules per slice: as bi_mm, and for BI_BF16 sAg % 8 == sBg % 8 == 0.
+ */
+int bi_bmm(int64_t G, int64_t M, int64_t N, int64_t K,
+           const void* A, int64_t sAg, int64_t sAm, int64_t sAk,
+           const void* B, int64_t sBg, int64_t sBk, int64_t sBn,
+           void* C, int64_t sCg, int64_t sCm, int64_t sCn,
+           int in_dtype, int out_dtype, void* stream);
+
+/*
+ * bi_conv2d — non-transposed 2-D convolution, NCHW.
+ * Source: "Batch-Invariant VLAs", section "Replacing nn.Conv2d" (per-sample
+ * unfold, flattened-kernel product, bias), and "Batch-Invariant Kernel
+ * Design ...", section "Kernel 1: Conv2d" (stride, padding, dilation,
+ * groups).  Lowered to an explicit unfold into the workspace, laid out
+ * [n][g][location][k] with k = ci*Kh*Kw + kh*Kw + kw zero-padded to a
+ * multiple of 8, followed by the batched GEMM above with one slice per
+ * (sample, group): y[n, g*Cout/G + c, :] = Wg[c, :] @ U[n, g] + bias.
+ *
+ * x [N, Cin, H, W] contiguous; w [Cout, Cin/groups, Kh, Kw] contiguous;
+ * bias [Cout] or NULL; y [N, Cout, OH, OW] contiguous with
+ * OH = (H + 2*ph - dh*(Kh-1) - 1)/sh + 1 (and OW likewise).
+ * x, w, bias are in_dtype (BI_BF16 or BI_F32); y is out_dtype.
+ * ws: device workspace of at least bi_conv2d_workspace_bytes(...) bytes,
+ * 256-byte aligned, owned by the caller, contents undefined on return.
+ * Errors: BI_ERR_SHAPE if Cin or Cout is not divisible by groups or the
+ * output would be empty; BI_ERR_WORKSPACE if ws is too small.
+ */
+size_t bi_conv2d_workspace_bytes(int64_t N, int64_t Cin, int64_t H, int64_t W,
+                                 int64_t Cout, int64_t Kh, int64_t Kw,
+                                 int64_t sh, int64_t sw, int64_t ph, int64_t pw,
+                                 int64_t dh, int64_t dw, int64_t groups, int in_dtype);
+int bi_conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, const void* x,
+              int64_t Cout, int64_t Kh, int64_t Kw, const void* w, const void* bias,
+              int64_t sh, int64_t sw, int64_t ph, int64_t pw,
+              int64_t dh, int64_t dw, int64_t groups,
+              void* y, void* ws, size_t ws_bytes,
+              int in_dtype, int out_dtype, void* stream);
+
+/*
+ * bi_decode_attn — single-query attention per (b, h) over a KV cache,
+ * split into fixed-length chunks of bi_decode_chunk_tokens() tokens counted
+ * from position 0 (the last chunk may be shorter).
+ * Source: the deterministic-inference handbook page, section
+ * "根源：浮点加法的顺序" (flash-decoding experiment: per-chunk max, sum of
+ * exponentials and exp-weighted V sum, merged by the log-sum-exp rule) and
+ * its rule that split-KV must cut by a fixed length (2048 tokens for decode)
+ * rather than a fixed number of parts.
+ *
+ *   s_t = scale * (q . k_t);  per chunk c: m_c = max s_t, l_c = sum e^{s_t-m_c},
+ *   o_c = sum e^{s_t-m_c} v_t;  out = sum_c e^{m_c-M} o_c / sum_c e^{m_c-M} l_c,
+ *   M = max_c m_c, chunks merged in ascending order.
+ *
+ * q [B, H, D], k and v [B, H, S, D], out [B, H, D], all contiguous.
+ * in_dtype must be BI_BF16; out_dtype BI_F32 or BI_BF16.  D must be 64 or 128.
+ * ws: at least bi_decode_attn_workspace_bytes(B, H, S, D) bytes, 16-byte
+ * aligned; receives the per-chunk triples [B, H, nchunk, 2 + D] (binary32:
+ * m, l, o[D]) and is owned by the caller.
+ */
+size_t bi_decode_attn_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t D);
+int bi_decode_attn(int64_t B, int64_t H, int64_t S, int64_t D,
+                   const void* q, const void* k, const void* v, void* out,
+                   float scale, void* ws, size_t ws_bytes,
+                   int in_dtype, int out_dtype, void* stream);
+
+/* The fixed KV chunk length of bi_decode_attn (2048, the handbook's decode split). */
+int bi_decode_chunk_tokens(void);
+
+/*
+ * bi_softmax_rows — P[r, :] = softmax(scale * S[r, :]) for each row, in
+ * binary32: max, exponentials, their sum and the division, with one
+ * workgroup per row and a reduction tree fixed by `cols` alone (the
+ * row-per-program reduction of "Unmasking the True Culprit ...", section
+ * "Beyond Matrix Multiplication").  It is the glue between the two batched
+ * products of attention (S = Q @ K^T, P = softmax(scale * S), O = P @ V).
+ * S: binary32 with row stride ldS (unit column stride), 16-byte aligned with
+ * ldS % 4 == 0; P: out_dtype (BI_F32 or BI_BF16) with row stride ldP.
+ */
+int bi_softmax_rows(int64_t rows, int64_t cols, const void* S, int64_t ldS, float scale,
+                    void* P, int64_t ldP, int out_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BI_H */

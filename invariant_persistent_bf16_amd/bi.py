@@ -1,0 +1,210 @@
+"""Python binding of libbi.so (argument marshalling only).
+
+Each function has the name of the C entry point it calls and takes device
+torch tensors; torch supplies device memory and the current HIP stream, and
+every step of the computation runs in the library's HIP kernels.  There is no
+fallback: if the library is missing or refuses a call, an exception says so.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbi.so")
+
+BI_F32, BI_BF16 = 0, 1
+_i64, _vp, _int, _f32, _sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+_SIGS = {
+    "bi_status_string": (ctypes.c_char_p, [_int]),
+    "bi_mm": (_int, [_i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _int, _int, _vp]),
+    "bi_addmm": (_int, [_i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i64, _i64,
+                        _int, _int, _vp]),
+    "bi_bmm": (_int, [_i64, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64,
+                      _i64, _i64, _int, _int, _vp]),
+    "bi_conv2d_workspace_bytes": (_sz, [_i64] * 14 + [_int]),
+    "bi_conv2d": (_int, [_i64, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _vp] + [_i64] * 7 +
+                  [_vp, _vp, _sz, _int, _int, _vp]),
+    "bi_decode_attn_workspace_bytes": (_sz, [_i64] * 4),
+    "bi_decode_attn": (_int, [_i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _f32, _vp, _sz, _int, _int, _vp]),
+    "bi_decode_chunk_tokens": (_int, []),
+    "bi_softmax_rows": (_int, [_i64, _i64, _vp, _i64, _f32, _vp, _i64, _int, _vp]),
+}
+
+_lib = None
+
+
+class BIError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+        self.status = status
+
+
+def lib():
+    """The loaded libbi.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                              "(hipcc --offload-arch=gfx950); there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(status):
+    return lib().bi_status_string(int(status)).decode()
+
+
+def bi_status_string(status):
+    return status_string(status)
+
+
+def _dt(t):
+    if t.dtype == torch.float32:
+        return BI_F32
+    if t.dtype == torch.bfloat16:
+        return BI_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _tdt(code):
+    return torch.float32 if code == BI_F32 else torch.bfloat16
+
+
+def _p(t):
+    return _vp(t.data_ptr()) if t is not None else _vp(0)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return _vp(stream.cuda_stream)
+
+
+def _check(fn, rc):
+    if rc != 0:
+        raise BIError(fn, rc)
+
+
+def _out(shape, out_dtype, device, out):
+    if out is not None:
+        return out
+    return torch.empty(shape, dtype=_tdt(out_dtype), device=device)
+
+
+def bi_mm(A, B, out=None, out_dtype=None, stream=None):
+    """C = A @ B (A [M, K], B [K, N]; strided views allowed as the header states)."""
+    M, K = A.shape
+    N = B.shape[1]
+    od = _dt(A) if out_dtype is None else out_dtype
+    C = _out((M, N), od, A.device, out)
+    _check("bi_mm", lib().bi_mm(M, N, K, _p(A), A.stride(0), A.stride(1), _p(B), B.stride(0),
+                                B.stride(1), _p(C), C.stride(0), C.stride(1), _dt(A), _dt(C),
+                                _stream(stream)))
+    return C
+
+
+def bi_addmm(bias, A, B, out=None, out_dtype=None, stream=None):
+    """C = A @ B + bias (bias [N])."""
+    M, K = A.shape
+    N = B.shape[1]
+    od = _dt(A) if out_dtype is None else out_dtype
+    C = _out((M, N), od, A.device, out)
+    _check("bi_addmm", lib().bi_addmm(M, N, K, _p(A), A.stride(0), A.stride(1), _p(B), B.stride(0),
+                                      B.stride(1), _p(bias), _p(C), C.stride(0), C.stride(1),
+                                      _dt(A), _dt(C), _stream(stream)))
+    return C
+
+
+def bi_bmm(A, B, out=None, out_dtype=None, stream=None):
+    """C[g] = A[g] @ B[g] (A [G, M, K], B [G, K, N])."""
+    G, M, K = A.shape
+    N = B.shape[2]
+    od = _dt(A) if out_dtype is None else out_dtype
+    C = _out((G, M, N), od, A.device, out)
+    _check("bi_bmm", lib().bi_bmm(G, M, N, K, _p(A), A.stride(0), A.stride(1), A.stride(2),
+                                  _p(B), B.stride(0), B.stride(1), B.stride(2),
+                                  _p(C), C.stride(0), C.stride(1), C.stride(2),
+                                  _dt(A), _dt(C), _stream(stream)))
+    return C
+
+
+def conv_out_hw(H, W, Kh, Kw, stride, padding, dilation):
+    oh = (H + 2 * padding[0] - dilation[0] * (Kh - 1) - 1) // stride[0] + 1
+    ow = (W + 2 * padding[1] - dilation[1] * (Kw - 1) - 1) // stride[1] + 1
+    return oh, ow
+
+
+def bi_conv2d_workspace_bytes(x_shape, w_shape, stride=(1, 1), padding=(0, 0), dilation=(1, 1),
+                              groups=1, in_dtype=BI_BF16):
+    N, Cin, H, W = x_shape
+    Cout, _, Kh, Kw = w_shape
+    return lib().bi_conv2d_workspace_bytes(N, Cin, H, W, Cout, Kh, Kw, stride[0], stride[1],
+                                           padding[0], padding[1], dilation[0], dilation[1],
+                                           groups, in_dtype)
+
+
+def bi_conv2d(x, w, bias=None, stride=(1, 1), padding=(0, 0), dilation=(1, 1), groups=1,
+              out=None, out_dtype=None, workspace=None, stream=None):
+    """y = conv2d(x, w, bias) in NCHW via unfold + batched GEMM."""
+    N, Cin, H, W = x.shape
+    Cout, _, Kh, Kw = w.shape
+    OH, OW = conv_out_hw(H, W, Kh, Kw, stride, padding, dilation)
+    od = _dt(x) if out_dtype is None else out_dtype
+    y = _out((N, Cout, OH, OW), od, x.device, out)
+    need = bi_conv2d_workspace_bytes(x.shape, w.shape, stride, padding, dilation, groups, _dt(x))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check("bi_conv2d", lib().bi_conv2d(N, Cin, H, W, _p(x), Cout, Kh, Kw, _p(w), _p(bias),
+                                        stride[0], stride[1], padding[0], padding[1], dilation[0],
+                                        dilation[1], groups, _p(y), _p(workspace),
+                                        workspace.numel() * workspace.element_size(), _dt(x), _dt(y),
+                                        _stream(stream)))
+    return y
+
+
+def bi_decode_chunk_tokens():
+    return lib().bi_decode_chunk_tokens()
+
+
+def bi_decode_attn_workspace_bytes(B, H, S, D):
+    return lib().bi_decode_attn_workspace_bytes(B, H, S, D)
+
+
+def bi_decode_attn(q, k, v, scale, out=None, out_dtype=BI_F32, workspace=None, stream=None):
+    """Fixed-chunk split-KV decode attention: q [B,H,D], k, v [B,H,S,D] -> out [B,H,D]."""
+    B, H, S, D = k.shape
+    o = _out((B, H, D), out_dtype, q.device, out)
+    need = bi_decode_attn_workspace_bytes(B, H, S, D)
+    if workspace is None:
+        workspace = torch.empty(max(need // 4, 1), dtype=torch.float32, device=q.device)
+    _check("bi_decode_attn", lib().bi_decode_attn(B, H, S, D, _p(q), _p(k), _p(v), _p(o),
+                                                  float(scale), _p(workspace),
+                                                  workspace.numel() * workspace.element_size(),
+                                                  _dt(q), _dt(o), _stream(stream)))
+    return o
+
+
+def bi_softmax_rows(S, scale, out=None, out_dtype=BI_BF16, stream=None):
+    """P = softmax(scale * S) row-wise; S a float32 matrix [rows, cols]."""
+    rows, cols = S.shape
+    P = _out((rows, cols), out_dtype, S.device, out)
+    _check("bi_softmax_rows", lib().bi_softmax_rows(rows, cols, _p(S), S.stride(0), float(scale), _p(P),
+                                                    P.stride(0), _dt(P), _stream(stream)))
+    return P
+
+
+def attention(Q, K, V, scale, S_buf=None, P_buf=None, out=None, stream=None):
+    """Attention of flattened [G, T, D] operands in three launches:
+    S = bi_bmm(Q, K^T) (fp32), P = bi_softmax_rows(S, scale) (bf16), O = bi_bmm(P, V) (fp32)."""
+    G, T, D = Q.shape
+    S = bi_bmm(Q, K.transpose(1, 2), out=S_buf, out_dtype=BI_F32, stream=stream)
+    P = bi_softmax_rows(S.view(G * T, T), scale, out=None if P_buf is None else P_buf.view(G * T, T),
+                        out_dtype=_dt(Q), stream=stream)
+    return bi_bmm(P.view(G, T, T), V, out=out, out_dtype=BI_F32, stream=stream)

@@ -1,0 +1,376 @@
+// C-ABI entry points of the batch-invariant contraction library (declared in
+// include/bi.h).  Every argument is checked on the host before any HIP call,
+// so a rejected call touches neither the device nor the stream; accepted
+// calls enqueue kernels on the caller's stream and return without waiting.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "../../include/bi.h"
+#include "conv_pack.hpp"
+#include "decode.hpp"
+#include "gemm_bf16.hpp"
+#include "gemm_f32.hpp"
+#include "softmax.hpp"
+#include "internal.hpp"
+
+namespace bi {
+
+// ------------------------------------------------------------ device info
+// Per-device compute-unit count, read once (0 = not yet read, -1 = not gfx950).
+static std::atomic<int> g_cu_count[64];
+
+int device_cu_count(int* cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return BI_ERR_DEVICE;
+    if (dev < 0 || dev >= 64) return BI_ERR_DEVICE;
+    int n = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return BI_ERR_DEVICE;
+        n = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? prop.multiProcessorCount : -1;
+        if (n == 0) n = -1;
+        g_cu_count[dev].store(n, std::memory_order_relaxed);
+    }
+    if (n < 0) return BI_ERR_DEVICE;
+    *cus = n;
+    return BI_OK;
+}
+
+static int launch_status() { return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_LAUNCH; }
+
+static inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ------------------------------------------------------------------- GEMM
+int gemm_check(const GemmDesc& d) {
+    if (d.in_dtype != BI_F32 && d.in_dtype != BI_BF16) return BI_ERR_DTYPE;
+    if (d.out_dtype != BI_F32 && d.out_dtype != BI_BF16) return BI_ERR_DTYPE;
+    if (d.G1 < 0 || d.G2 < 1 || d.M < 0 || d.N < 0 || d.K < 0) return BI_ERR_SHAPE;
+    if (d.G1 == 0 || d.M == 0 || d.N == 0) return BI_OK;   // nothing to compute
+    if (!d.C) return BI_ERR_NULL;
+    if (d.K > 0 && (!d.A || !d.B)) return BI_ERR_NULL;
+    const int64_t strides[] = {d.sA1, d.sA2, d.sAm, d.sAk, d.sB1, d.sB2, d.sBk, d.sBn,
+                               d.sBias2, d.sC1, d.sC2, d.sCm, d.sCn};
+    for (int64_t s : strides)
+        if (s < 0) return BI_ERR_LAYOUT;
+    if (d.sCn != 1) return BI_ERR_LAYOUT;
+    const int osz = d.out_dtype == BI_BF16 ? 2 : 4;
+    if (!aligned(d.C, osz)) return BI_ERR_LAYOUT;
+    if (d.in_dtype == BI_BF16) {
+        if (d.K > 0) {
+            if (d.K % 8 != 0) return BI_ERR_LAYOUT;
+            if (d.sAk != 1 || (d.M > 1 && d.sAm % 8 != 0) || !aligned(d.A, 16)) return BI_ERR_LAYOUT;
+            if (d.sA1 % 8 != 0 || d.sA2 % 8 != 0) return BI_ERR_LAYOUT;
+            if (!aligned(d.B, 16) || d.sB1 % 8 != 0 || d.sB2 % 8 != 0) return BI_ERR_LAYOUT;
+            const bool kc = d.sBk == 1 && (d.N == 1 || d.sBn % 8 == 0);
+            const bool nc = d.sBn == 1 && d.sBk % 8 == 0 && d.N % 8 == 0;
+            if (!kc && !nc) return BI_ERR_LAYOUT;
+            // Row offsets inside one tile are 32-bit.
+            const int64_t lim = (1ll << 31) - 1;
+            if (d.sAm * G16_BM > lim || (kc ? d.sBn * G16_BN : d.sBk * G16_BK) > lim)
+                return BI_ERR_UNSUPPORTED;
+        }
+        if (d.bias && !aligned(d.bias, 2)) return BI_ERR_LAYOUT;
+    } else {
+        if (d.K > 0 && (!aligned(d.A, 4) || !aligned(d.B, 4))) return BI_ERR_LAYOUT;
+        if (d.bias && !aligned(d.bias, 4)) return BI_ERR_LAYOUT;
+    }
+    const int64_t bm = d.in_dtype == BI_BF16 ? G16_BM : G32_BM;
+    const int64_t bn = d.in_dtype == BI_BF16 ? G16_BN : G32_BN;
+    if (d.G1 > (1ll << 30) || d.G2 > (1ll << 30)) return BI_ERR_UNSUPPORTED;
+    const int64_t tiles = cdiv(d.M, bm) * cdiv(d.N, bn);
+    const int64_t slices = d.G1 * d.G2;
+    if (slices > (1ll << 30) || tiles > (1ll << 30) || tiles * slices > (1ll << 30))
+        return BI_ERR_UNSUPPORTED;
+    return BI_OK;
+}
+
+// Launch an already checked GEMM.  grid_override > 0 forces the persistent
+// grid size (used only to show that the result does not depend on it).
+int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override) {
+    if (d.G1 == 0 || d.M == 0 || d.N == 0) return BI_OK;
+    int cus = 0;
+    int rc = device_cu_count(&cus);
+    if (rc != BI_OK) return rc;
+    const bool out_bf16 = d.out_dtype == BI_BF16;
+    if (d.in_dtype == BI_BF16) {
+        GemmParams p;
+        p.A = (const uint16_t*)d.A; p.B = (const uint16_t*)d.B;
+        p.bias = (const uint16_t*)d.bias; p.C = d.C;
+        p.M = d.M; p.N = d.N; p.K = d.K;
+        p.sAm = d.sAm; p.sBk = d.sBk; p.sBn = d.sBn; p.sCm = d.sCm;
+        p.G2 = d.G2;
+        p.sA1 = d.sA1; p.sA2 = d.sA2; p.sB1 = d.sB1; p.sB2 = d.sB2;
+        p.sC1 = d.sC1; p.sC2 = d.sC2; p.sBias2 = d.sBias2;
+        p.tiles_m = (int)cdiv(d.M, G16_BM);
+        p.tiles_n = (int)cdiv(d.N, G16_BN);
+        p.tiles_per_slice = p.tiles_m * p.tiles_n;
+        p.total_tiles = (int)(p.tiles_per_slice * d.G1 * d.G2);
+        const int grid = grid_override > 0 ? grid_override : (p.total_tiles < cus ? p.total_tiles : cus);
+        const bool kc = d.K == 0 || (d.sBk == 1 && (d.N == 1 || d.sBn % 8 == 0));
+        if (kc) {
+            if (out_bf16) hipLaunchKernelGGL((gemm_bf16_persistent<true, 1>), dim3(grid), dim3(G16_THREADS), 0, st, p);
+            else          hipLaunchKernelGGL((gemm_bf16_persistent<true, 0>), dim3(grid), dim3(G16_THREADS), 0, st, p);
+        } else {
+            if (out_bf16) hipLaunchKernelGGL((gemm_bf16_persistent<false, 1>), dim3(grid), dim3(G16_THREADS), 0, st, p);
+            else          hipLaunchKernelGGL((gemm_bf16_persistent<false, 0>), dim3(grid), dim3(G16_THREADS), 0, st, p);
+        }
+    } else {
+        GemmF32Params p;
+        p.A = (const float*)d.A; p.B = (const float*)d.B; p.bias = (const float*)d.bias; p.C = d.C;
+        p.M = d.M; p.N = d.N; p.K = d.K;
+        p.sAm = d.sAm; p.sAk = d.sAk; p.sBk = d.sBk; p.sBn = d.sBn; p.sCm = d.sCm;
+        p.G2 = d.G2;
+        p.sA1 = d.sA1; p.sA2 = d.sA2; p.sB1 = d.sB1; p.sB2 = d.sB2;
+        p.sC1 = d.sC1; p.sC2 = d.sC2; p.sBias2 = d.sBias2;
+        p.tiles_m = (int)cdiv(d.M, G32_BM);
+        p.tiles_n = (int)cdiv(d.N, G32_BN);
+        p.tiles_per_slice = p.tiles_m * p.tiles_n;
+        p.total_tiles = (int)(p.tiles_per_slice * d.G1 * d.G2);
+        const int cap = 4 * cus;
+        const int grid = grid_override > 0 ? grid_override : (p.total_tiles < cap ? p.total_tiles : cap);
+        if (out_bf16) hipLaunchKernelGGL((gemm_f32_persistent<1>), dim3(grid), dim3(G32_THREADS), 0, st, p);
+        else          hipLaunchKernelGGL((gemm_f32_persistent<0>), dim3(grid), dim3(G32_THREADS), 0, st, p);
+    }
+    return launch_status();
+}
+
+GemmDesc mm_desc(int64_t M, int64_t N, int64_t K, const void* A, int64_t sAm, int64_t sAk,
+                 const void* B, int64_t sBk, int64_t sBn, const void* bias, void* C,
+                 int64_t sCm, int64_t sCn, int in_dtype, int out_dtype) {
+    GemmDesc d;
+    std::memset(&d, 0, sizeof(d));
+    d.G1 = 1; d.G2 = 1; d.M = M; d.N = N; d.K = K;
+    d.A = A; d.sAm = sAm; d.sAk = sAk;
+    d.B = B; d.sBk = sBk; d.sBn = sBn;
+    d.bias = bias; d.C = C; d.sCm = sCm; d.sCn = sCn;
+    d.in_dtype = in_dtype; d.out_dtype = out_dtype;
+    return d;
+}
+
+GemmDesc bmm_desc(int64_t G, int64_t M, int64_t N, int64_t K,
+                  const void* A, int64_t sAg, int64_t sAm, int64_t sAk,
+                  const void* B, int64_t sBg, int64_t sBk, int64_t sBn,
+                  void* C, int64_t sCg, int64_t sCm, int64_t sCn, int in_dtype, int out_dtype) {
+    GemmDesc d = mm_desc(M, N, K, A, sAm, sAk, B, sBk, sBn, nullptr, C, sCm, sCn, in_dtype, out_dtype);
+    d.G1 = G; d.sA1 = sAg; d.sB1 = sBg; d.sC1 = sCg;
+    return d;
+}
+
+// ------------------------------------------------------------------- conv
+int conv_geometry(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout, int64_t Kh,
+                  int64_t Kw, int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh,
+                  int64_t dw, int64_t groups, int in_dtype, ConvGeom* g, size_t* ws_bytes) {
+    if (in_dtype != BI_F32 && in_dtype != BI_BF16) return BI_ERR_DTYPE;
+    if (N < 0 || Cin < 1 || H < 1 || W < 1 || Cout < 1 || Kh < 1 || Kw < 1) return BI_ERR_SHAPE;
+    if (sh < 1 || sw < 1 || dh < 1 || dw < 1 || ph < 0 || pw < 0 || groups < 1) return BI_ERR_SHAPE;
+    if (Cin % groups != 0 || Cout % groups != 0) return BI_ERR_SHAPE;
+    const int64_t ohn = H + 2 * ph - dh * (Kh - 1) - 1, own = W + 2 * pw - dw * (Kw - 1) - 1;
+    if (ohn < 0 || own < 0) return BI_ERR_SHAPE;
+    ConvGeom c;
+    c.N = N; c.Cin = Cin; c.H = H; c.W = W; c.Cout = Cout; c.Kh = Kh; c.Kw = Kw;
+    c.sh = sh; c.sw = sw; c.ph = ph; c.pw = pw; c.dh = dh; c.dw = dw; c.groups = groups;
+    c.OH = ohn / sh + 1; c.OW = own / sw + 1; c.L = c.OH * c.OW;
+    c.cig = Cin / groups; c.cog = Cout / groups;
+    c.Kg = c.cig * Kh * Kw;
+    c.Kp = cdiv(c.Kg, 8) * 8;
+    const int64_t esz = in_dtype == BI_BF16 ? 2 : 4;
+    const int64_t wbytes = cdiv(Cout * c.Kp * esz, 256) * 256;
+    const int64_t ubytes = N * groups * c.L * c.Kp * esz;
+    if (g) *g = c;
+    if (ws_bytes) *ws_bytes = (size_t)(wbytes + ubytes);
+    return BI_OK;
+}
+
+}  // namespace bi
+
+using namespace bi;
+
+// ================================================================ C ABI
+extern "C" {
+
+const char* bi_status_string(int status) {
+    switch (status) {
+        case BI_OK: return "BI_OK";
+        case BI_ERR_NULL: return "BI_ERR_NULL: a required pointer is NULL";
+        case BI_ERR_SHAPE: return "BI_ERR_SHAPE: negative or inconsistent sizes";
+        case BI_ERR_DTYPE: return "BI_ERR_DTYPE: dtype not accepted by this entry point";
+        case BI_ERR_LAYOUT: return "BI_ERR_LAYOUT: strides or alignment not supported";
+        case BI_ERR_UNSUPPORTED: return "BI_ERR_UNSUPPORTED: request outside what is implemented";
+        case BI_ERR_WORKSPACE: return "BI_ERR_WORKSPACE: workspace NULL, too small or misaligned";
+        case BI_ERR_LAUNCH: return "BI_ERR_LAUNCH: the HIP runtime refused a launch";
+        case BI_ERR_DEVICE: return "BI_ERR_DEVICE: no usable gfx950 device is current";
+        default: return "unknown bi_status";
+    }
+}
+
+int bi_mm(int64_t M, int64_t N, int64_t K, const void* A, int64_t sAm, int64_t sAk,
+          const void* B, int64_t sBk, int64_t sBn, void* C, int64_t sCm, int64_t sCn,
+          int in_dtype, int out_dtype, void* stream) {
+    GemmDesc d = mm_desc(M, N, K, A, sAm, sAk, B, sBk, sBn, nullptr, C, sCm, sCn, in_dtype, out_dtype);
+    int rc = gemm_check(d);
+    if (rc != BI_OK) return rc;
+    return gemm_launch(d, (hipStream_t)stream, 0);
+}
+
+int bi_addmm(int64_t M, int64_t N, int64_t K, const void* A, int64_t sAm, int64_t sAk,
+             const void* B, int64_t sBk, int64_t sBn, const void* bias, void* C, int64_t sCm,
+             int64_t sCn, int in_dtype, int out_dtype, void* stream) {
+    GemmDesc d = mm_desc(M, N, K, A, sAm, sAk, B, sBk, sBn, bias, C, sCm, sCn, in_dtype, out_dtype);
+    int rc = gemm_check(d);
+    if (rc != BI_OK) return rc;
+    return gemm_launch(d, (hipStream_t)stream, 0);
+}
+
+int bi_bmm(int64_t G, int64_t M, int64_t N, int64_t K, const void* A, int64_t sAg, int64_t sAm,
+           int64_t sAk, const void* B, int64_t sBg, int64_t sBk, int64_t sBn, void* C, int64_t sCg,
+           int64_t sCm, int64_t sCn, int in_dtype, int out_dtype, void* stream) {
+    GemmDesc d = bmm_desc(G, M, N, K, A, sAg, sAm, sAk, B, sBg, sBk, sBn, C, sCg, sCm, sCn,
+                          in_dtype, out_dtype);
+    int rc = gemm_check(d);
+    if (rc != BI_OK) return rc;
+    return gemm_launch(d, (hipStream_t)stream, 0);
+}
+
+size_t bi_conv2d_workspace_bytes(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout,
+                                 int64_t Kh, int64_t Kw, int64_t sh, int64_t sw, int64_t ph,
+                                 int64_t pw, int64_t dh, int64_t dw, int64_t groups, int in_dtype) {
+    size_t bytes = 0;
+    if (conv_geometry(N, Cin, H, W, Cout, Kh, Kw, sh, sw, ph, pw, dh, dw, groups, in_dtype,
+                      nullptr, &bytes) != BI_OK)
+        return 0;
+    return bytes;
+}
+
+int bi_conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, const void* x, int64_t Cout,
+              int64_t Kh, int64_t Kw, const void* w, const void* bias, int64_t sh, int64_t sw,
+              int64_t ph, int64_t pw, int64_t dh, int64_t dw, int64_t groups, void* y, void* ws,
+              size_t ws_bytes, int in_dtype, int out_dtype, void* stream) {
+    ConvGeom g;
+    size_t need = 0;
+    int rc = conv_geometry(N, Cin, H, W, Cout, Kh, Kw, sh, sw, ph, pw, dh, dw, groups, in_dtype,
+                           &g, &need);
+    if (rc != BI_OK) return rc;
+    if (out_dtype != BI_F32 && out_dtype != BI_BF16) return BI_ERR_DTYPE;
+    if (N == 0) return BI_OK;
+    if (!x || !w || !y) return BI_ERR_NULL;
+    if (!ws) return BI_ERR_WORKSPACE;
+    if (ws_bytes < need || !aligned(ws, 256)) return BI_ERR_WORKSPACE;
+    const int64_t esz = in_dtype == BI_BF16 ? 2 : 4;
+    if (!aligned(x, esz) || !aligned(w, esz) || (bias && !aligned(bias, esz)) ||
+        !aligned(y, out_dtype == BI_BF16 ? 2 : 4))
+        return BI_ERR_LAYOUT;
+    // The GEMM over (sample, group) slices: A = packed weight, B = unfold (K-contiguous).
+    uint8_t* wp = (uint8_t*)ws;
+    uint8_t* u = wp + cdiv(Cout * g.Kp * esz, 256) * 256;
+    GemmDesc d;
+    std::memset(&d, 0, sizeof(d));
+    d.G1 = N; d.G2 = groups; d.M = g.cog; d.N = g.L; d.K = g.Kp;
+    d.A = wp; d.sA1 = 0; d.sA2 = g.cog * g.Kp; d.sAm = g.Kp; d.sAk = 1;
+    d.B = u; d.sB1 = groups * g.L * g.Kp; d.sB2 = g.L * g.Kp; d.sBk = 1; d.sBn = g.Kp;
+    d.bias = bias; d.sBias2 = g.cog;
+    d.C = y; d.sC1 = Cout * g.L; d.sC2 = g.cog * g.L; d.sCm = g.L; d.sCn = 1;
+    d.in_dtype = in_dtype; d.out_dtype = out_dtype;
+    rc = gemm_check(d);
+    if (rc != BI_OK) return rc;
+    int cus = 0;
+    rc = device_cu_count(&cus);
+    if (rc != BI_OK) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    const int64_t wchunks = Cout * (g.Kp / 8);
+    const int64_t uchunks = N * groups * g.L * (g.Kp / 8);
+    const int wgrid = (int)std::min<int64_t>(cdiv(wchunks, 256), 8 * cus);
+    const int ugrid = (int)std::min<int64_t>(cdiv(uchunks, 256), 64 * cus);
+    if (in_dtype == BI_BF16) {
+        hipLaunchKernelGGL((conv_pack_weight<uint16_t>), dim3(wgrid), dim3(256), 0, st,
+                           (const uint16_t*)w, (uint16_t*)wp, g);
+        hipLaunchKernelGGL((conv_unfold<uint16_t>), dim3(ugrid), dim3(256), 0, st,
+                           (const uint16_t*)x, (uint16_t*)u, g);
+    } else {
+        hipLaunchKernelGGL((conv_pack_weight<float>), dim3(wgrid), dim3(256), 0, st,
+                           (const float*)w, (float*)wp, g);
+        hipLaunchKernelGGL((conv_unfold<float>), dim3(ugrid), dim3(256), 0, st,
+                           (const float*)x, (float*)u, g);
+    }
+    rc = launch_status();
+    if (rc != BI_OK) return rc;
+    return gemm_launch(d, st, 0);
+}
+
+int bi_decode_chunk_tokens(void) { return DEC_CHUNK; }
+
+size_t bi_decode_attn_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t D) {
+    if (B < 0 || H < 0 || S < 1 || D < 1) return 0;
+    return (size_t)(B * H * cdiv(S, DEC_CHUNK) * (2 + D) * 4);
+}
+
+int bi_decode_attn(int64_t B, int64_t H, int64_t S, int64_t D, const void* q, const void* k,
+                   const void* v, void* out, float scale, void* ws, size_t ws_bytes,
+                   int in_dtype, int out_dtype, void* stream) {
+    if (in_dtype != BI_BF16) return BI_ERR_DTYPE;
+    if (out_dtype != BI_F32 && out_dtype != BI_BF16) return BI_ERR_DTYPE;
+    if (B < 0 || H < 0 || S < 1) return BI_ERR_SHAPE;
+    if (D != 64 && D != 128) return BI_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0) return BI_OK;
+    if (!q || !k || !v || !out) return BI_ERR_NULL;
+    if (!ws) return BI_ERR_WORKSPACE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+        !aligned(out, out_dtype == BI_BF16 ? 2 : 4))
+        return BI_ERR_LAYOUT;
+    const int64_t nchunk = cdiv(S, DEC_CHUNK);
+    if (ws_bytes < bi_decode_attn_workspace_bytes(B, H, S, D) || !aligned(ws, 16))
+        return BI_ERR_WORKSPACE;
+    if (B * H * nchunk > (1ll << 31) - 1 || B * H * D > (1ll << 40)) return BI_ERR_UNSUPPORTED;
+    int cus = 0;
+    int rc = device_cu_count(&cus);
+    if (rc != BI_OK) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    const int64_t BH = B * H;
+    const dim3 g1((unsigned)(BH * nchunk));
+    const dim3 g2((unsigned)cdiv(BH * D, 256));
+    float* wsf = (float*)ws;
+    if (D == 64) {
+        hipLaunchKernelGGL((decode_chunk_kernel<64>), g1, dim3(DEC_THREADS), 0, st,
+                           (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, wsf, S, (int)nchunk, scale);
+        if (out_dtype == BI_BF16) hipLaunchKernelGGL((decode_merge_kernel<64, 1>), g2, dim3(256), 0, st, wsf, out, BH, (int)nchunk);
+        else                      hipLaunchKernelGGL((decode_merge_kernel<64, 0>), g2, dim3(256), 0, st, wsf, out, BH, (int)nchunk);
+    } else {
+        hipLaunchKernelGGL((decode_chunk_kernel<128>), g1, dim3(DEC_THREADS), 0, st,
+                           (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, wsf, S, (int)nchunk, scale);
+        if (out_dtype == BI_BF16) hipLaunchKernelGGL((decode_merge_kernel<128, 1>), g2, dim3(256), 0, st, wsf, out, BH, (int)nchunk);
+        else                      hipLaunchKernelGGL((decode_merge_kernel<128, 0>), g2, dim3(256), 0, st, wsf, out, BH, (int)nchunk);
+    }
+    return launch_status();
+}
+
+int bi_softmax_rows(int64_t rows, int64_t cols, const void* S, int64_t ldS, float scale, void* P,
+                    int64_t ldP, int out_dtype, void* stream) {
+    if (out_dtype != BI_F32 && out_dtype != BI_BF16) return BI_ERR_DTYPE;
+    if (rows < 0 || cols < 0) return BI_ERR_SHAPE;
+    if (rows == 0 || cols == 0) return BI_OK;
+    if (!S || !P) return BI_ERR_NULL;
+    if ((rows > 1 && (ldS < cols || ldP < cols)) || ldS < 0 || ldP < 0) return BI_ERR_LAYOUT;
+    if (!aligned(S, 4) || !aligned(P, out_dtype == BI_BF16 ? 2 : 4)) return BI_ERR_LAYOUT;
+    int cus = 0;
+    int rc = device_cu_count(&cus);
+    if (rc != BI_OK) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    const dim3 grid((unsigned)std::min<int64_t>(rows, 1ll << 30));
+    const float* s = (const float*)S;
+    const bool ob = out_dtype == BI_BF16;
+    if (cols <= 4 * SM_THREADS) {
+        if (ob) hipLaunchKernelGGL((softmax_rows_kernel<4, 1>), grid, dim3(SM_THREADS), 0, st, s, ldS, scale, P, ldP, rows, cols);
+        else    hipLaunchKernelGGL((softmax_rows_kernel<4, 0>), grid, dim3(SM_THREADS), 0, st, s, ldS, scale, P, ldP, rows, cols);
+    } else if (cols <= 16 * SM_THREADS) {
+        if (ob) hipLaunchKernelGGL((softmax_rows_kernel<16, 1>), grid, dim3(SM_THREADS), 0, st, s, ldS, scale, P, ldP, rows, cols);
+        else    hipLaunchKernelGGL((softmax_rows_kernel<16, 0>), grid, dim3(SM_THREADS), 0, st, s, ldS, scale, P, ldP, rows, cols);
+    } else {
+        if (ob) hipLaunchKernelGGL((softmax_rows_kernel<0, 1>), grid, dim3(SM_THREADS), 0, st, s, ldS, scale, P, ldP, rows, cols);
+        else    hipLaunchKernelGGL((softmax_rows_kernel<0, 0>), grid, dim3(SM_THREADS), 0, st, s, ldS, scale, P, ldP, rows, cols);
+    }
+    return launch_status();
+}
+
+}  // extern "C"

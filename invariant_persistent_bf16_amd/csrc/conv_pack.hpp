@@ -1,0 +1,74 @@
+// Lowering of a 2-D convolution to the batched GEMM: the per-sample unfold of
+// "Batch-Invariant VLAs" (section "Replacing nn.Conv2d") and "Batch-Invariant
+// Kernel Design ..." (section "Kernel 1: Conv2d"), written out explicitly.
+//
+//   weight pack: Wp[co][k] = w[co][ci][kh][kw] with k = ci*Kh*Kw + kh*Kw + kw,
+//                zero for Kg <= k < Kp (Kg = Cin/G*Kh*Kw, Kp = Kg rounded up to 8)
+//   unfold:      U[n][g][l][k] = x[n][g*Cin/G + ci][oh*sh + kh*dh - ph][ow*sw + kw*dw - pw]
+//                (zero outside the image and for k >= Kg), l = oh*OW + ow
+//
+// U is stored K-contiguous per location, which is the layout the GEMM's B
+// operand reads directly; the product per (sample, group) is then
+// y[n, g*Cout/G : (g+1)*Cout/G, :] = Wp_g @ U[n][g]^T-view, written in NCHW.
+// Both kernels only move data; every arithmetic step stays in the GEMM.
+#pragma once
+
+#include "common.hpp"
+
+namespace bi {
+
+struct ConvGeom {
+    int64_t N, Cin, H, W, Cout, Kh, Kw, sh, sw, ph, pw, dh, dw, groups;
+    int64_t OH, OW, L, cig, cog, Kg, Kp;
+};
+
+// One thread per 8 consecutive k of one (co) row.
+template <typename T>
+__global__ void conv_pack_weight(const T* __restrict__ w, T* __restrict__ wp, ConvGeom g) {
+    const int64_t nchunk = g.Kp / 8;
+    const int64_t total = g.Cout * nchunk;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t co = i / nchunk, k0 = (i - co * nchunk) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int64_t k = k0 + e;
+            wp[co * g.Kp + k] = k < g.Kg ? w[co * g.Kg + k] : (T)0;
+        }
+    }
+}
+
+// One thread per 8 consecutive k of one (n, g, l) row of U.
+template <typename T>
+__global__ void conv_unfold(const T* __restrict__ x, T* __restrict__ u, ConvGeom g) {
+    const int64_t nchunk = g.Kp / 8;
+    const int64_t total = g.N * g.groups * g.L * nchunk;
+    const int64_t khw = g.Kh * g.Kw;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        int64_t r = i / nchunk;
+        const int64_t k0 = (i - r * nchunk) * 8;
+        const int64_t l = r % g.L;
+        r /= g.L;
+        const int64_t grp = r % g.groups;
+        const int64_t n = r / g.groups;
+        const int64_t oh = l / g.OW, ow = l - (l / g.OW) * g.OW;
+        T* dst = u + ((n * g.groups + grp) * g.L + l) * g.Kp + k0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int64_t k = k0 + e;
+            T v = (T)0;
+            if (k < g.Kg) {
+                const int64_t ci = k / khw, rem = k - (k / khw) * khw;
+                const int64_t kh = rem / g.Kw, kw = rem - (rem / g.Kw) * g.Kw;
+                const int64_t ih = oh * g.sh + kh * g.dh - g.ph;
+                const int64_t iw = ow * g.sw + kw * g.dw - g.pw;
+                if (ih >= 0 && ih < g.H && iw >= 0 && iw < g.W)
+                    v = x[((n * g.Cin + grp * g.cig + ci) * g.H + ih) * g.W + iw];
+            }
+            dst[e] = v;
+        }
+    }
+}
+
+}  // namespace bi

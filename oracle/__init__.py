@@ -74,9 +74,11 @@ def bf16_rne(x):
 
 
 def bf16_rne_array(a):
-    f = _load().oracle_bf16_rne
-    a = np.asarray(a, dtype=np.float64)
-    return np.array([f(float(v)) for v in a.ravel()], dtype=np.float64).reshape(a.shape)
+    """Nearest bfloat16 values of a float64 array, ties to even."""
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+    out = np.empty_like(a)
+    _load().oracle_bf16_rne_array(a.ctypes.data_as(_dp), out.ctypes.data_as(_dp), _i64(a.size))
+    return out
 
 
 def widen(t, i):

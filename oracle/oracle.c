@@ -453,3 +453,8 @@ void sim_decode_splits_f32(int64_t S, int64_t D, const float* q, const float* Kc
     for (int64_t d = 0; d < D; ++d) out[d] = num[d] / den;
     free(num); free(ms); free(ls); free(os); free(sc);
 }
+
+/* Element-wise oracle_bf16_rne over an array (tests round many values). */
+void oracle_bf16_rne_array(const double* x, double* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_bf16_rne(x[i]);
+}
