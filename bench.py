@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Benchmark of the batch-invariant contraction path on one MI355X.
+
+One step runs every operation of the path once, on inputs already resident
+in HBM (seeded synthetic data of the pages' workload shapes):
+  * addmm   bf16  X [8192, 4096] @ W [4096, 14336] + bias -> bf16   (the large GEMM)
+  * conv2d  bf16  SigLIP patch embedding, 32 images 3x224x224 -> [32, 1152, 16, 16]
+  * attention bf16, B=32, H=8, T=1024, D=128: S = Q K^T (fp32), softmax -> P (bf16),
+                O = P V (fp32)
+  * decode  bf16  q [256, 32, 64], K, V [256, 32, 8192, 64], 2048-token chunks -> fp32
+  * mm      fp32  X [200, 4096] @ W [4096, 256]
+The headline `value` is the addmm GEMM throughput in TFLOP/s (algorithmic
+2*M*N*K flops over the kernel's mean duration measured with HIP events on
+the launch stream); decode attention reports algorithmic HBM GB/s.  A
+bitwise batch-invariance check (row 0 of the GEMM at M=1 vs M=8192, request
+0 of decode at B=1 vs B=256) runs outside the timed region.  The CPU
+baseline is the reference oracle timed on a bounded row sample of the
+addmm workload on the host cores.
+
+Prints one JSON line.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+ADDMM = dict(M=8192, K=4096, N=14336)
+CONV_B = 32
+ATT = dict(B=32, H=8, T=1024, D=128)
+DEC = dict(B=256, H=32, S=8192, D=64)
+MM32 = dict(M=200, K=4096, N=256)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target host time of the oracle CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM traffic per launch measured by rocprofv3 counters (optional)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(every operation shards by request with no exchange; see DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from invariant_persistent_bf16_amd import bi
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bi.lib()
+    print(f"# device: {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
+
+    # ------------------------------------------------ inputs (resident in HBM)
+    W, bias, x0 = synth.addmm_shared()
+    Wd, bd = W.to(dev), bias.to(dev)
+    X = synth.addmm_batch(x0, ADDMM["M"], device=dev)
+    Y = torch.empty(ADDMM["M"], ADDMM["N"], dtype=torch.bfloat16, device=dev)
+
+    cw, cb, cx0 = synth.conv_shared()
+    cwd, cbd = cw.to(dev), cb.to(dev)
+    cx = synth.conv_batch(cx0, CONV_B, device=dev)
+    cy = torch.empty(CONV_B, 1152, 16, 16, dtype=torch.bfloat16, device=dev)
+    cws = torch.empty(bi.bi_conv2d_workspace_bytes(cx.shape, cw.shape, (14, 14)), dtype=torch.uint8,
+                      device=dev)
+
+    G = ATT["B"] * ATT["H"]
+    Q, Kt, V = synth.attn_batch(synth.attn_shared(), ATT["B"], device=dev)
+    Sb = torch.empty(G, ATT["T"], ATT["T"], dtype=torch.float32, device=dev)
+    Pb = torch.empty(G, ATT["T"], ATT["T"], dtype=torch.bfloat16, device=dev)
+    Ob = torch.empty(G, ATT["T"], ATT["D"], dtype=torch.float32, device=dev)
+    att_scale = float(torch.tensor(1 / math.sqrt(ATT["D"]), dtype=torch.float32))
+
+    dq0 = synth.decode_shared()
+    dq, dk, dv = synth.decode_batch(dq0, DEC["B"], device=dev)
+    dout = torch.empty(DEC["B"], DEC["H"], DEC["D"], dtype=torch.float32, device=dev)
+    dws = torch.empty(bi.bi_decode_attn_workspace_bytes(DEC["B"], DEC["H"], DEC["S"], DEC["D"]) // 4,
+                      dtype=torch.float32, device=dev)
+
+    mW, mX = synth.mm_inputs(Ms=(MM32["M"],))
+    mWd, mXd = mW.to(dev), mX[MM32["M"]].to(dev)
+    mY = torch.empty(MM32["M"], MM32["N"], dtype=torch.float32, device=dev)
+
+    # A plain device copy of known size, so HBM counters can be calibrated
+    # against it in a profiler run of this same command.
+    calib_src = torch.empty(256 << 20, dtype=torch.float32, device=dev)
+    calib_dst = torch.empty_like(calib_src)
+    calib_dst.copy_(calib_src)
+    del calib_src, calib_dst
+    torch.cuda.synchronize()
+
+    ops = {
+        "addmm": lambda: bi.bi_addmm(bd, X, Wd, out=Y),
+        "conv2d": lambda: bi.bi_conv2d(cx, cwd, cbd, stride=(14, 14), out=cy, workspace=cws),
+        "attention": lambda: (bi.bi_bmm(Q, Kt.transpose(1, 2), out=Sb),
+                              bi.bi_softmax_rows(Sb.view(G * ATT["T"], ATT["T"]), att_scale,
+                                                 out=Pb.view(G * ATT["T"], ATT["T"])),
+                              bi.bi_bmm(Pb, V, out=Ob)),
+        "decode": lambda: bi.bi_decode_attn(dq, dk, dv, 0.125, out=dout, workspace=dws),
+        "mm_fp32": lambda: bi.bi_mm(mXd, mWd, out=mY),
+    }
+    names = list(ops)
+
+    def step(events=None):
+        for i, n in enumerate(names):
+            if events is not None:
+                events[i][0].record()
+            ops[n]()
+            if events is not None:
+                events[i][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in names] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms = {n: sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)) / args.steps
+          for i, n in enumerate(names)}
+
+    flops = {
+        "addmm": 2.0 * ADDMM["M"] * ADDMM["N"] * ADDMM["K"],
+        "conv2d": 2.0 * CONV_B * 1152 * 256 * 588,
+        "attention": 2.0 * 2 * G * ATT["T"] * ATT["T"] * ATT["D"],
+        "decode": 2.0 * 2 * DEC["B"] * DEC["H"] * DEC["S"] * DEC["D"],
+        "mm_fp32": 2.0 * MM32["M"] * MM32["N"] * MM32["K"],
+    }
+    bytes_ = {
+        "addmm": 2.0 * (ADDMM["M"] * ADDMM["K"] + ADDMM["K"] * ADDMM["N"] + ADDMM["N"] +
+                        ADDMM["M"] * ADDMM["N"]),
+        "conv2d": 2.0 * (CONV_B * 3 * 224 * 224 + 1152 * 588 + 1152 + CONV_B * 1152 * 256),
+        "attention": G * (3 * ATT["T"] * ATT["D"] * 2 + ATT["T"] * ATT["T"] * (4 + 4 + 2 + 2) +
+                          ATT["T"] * ATT["D"] * 4),
+        "decode": DEC["B"] * DEC["H"] * (2 * DEC["S"] * DEC["D"] * 2 + DEC["D"] * 2 + DEC["D"] * 4),
+        "mm_fp32": 4.0 * (MM32["M"] * MM32["K"] + MM32["K"] * MM32["N"] + MM32["M"] * MM32["N"]),
+    }
+    detail = {}
+    for n in names:
+        t = ms[n] * 1e-3
+        detail[n] = {"ms": round(ms[n], 5), "TFLOP/s": round(flops[n] / t / 1e12, 2),
+                     "GB/s": round(bytes_[n] / t / 1e9, 1)}
+    detail["addmm"]["frac_bf16_peak"] = round(flops["addmm"] / (ms["addmm"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+    detail["decode"]["frac_hbm_peak"] = round(bytes_["decode"] / (ms["decode"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+    detail["mm_fp32"]["frac_fp32_mfma_peak"] = round(
+        flops["mm_fp32"] / (ms["mm_fp32"] * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4)
+
+    # ------------------------------------------- bitwise invariance (untimed)
+    y1 = bi.bi_addmm(bd, X[:1], Wd)
+    dq1, dk1, dv1 = dq[:1], dk[:1], dv[:1]
+    o1 = bi.bi_decode_attn(dq1, dk1, dv1, 0.125)
+    torch.cuda.synchronize()
+    bit_gemm = torch.equal(y1[0].view(torch.int16), Y[0].view(torch.int16))
+    bit_dec = torch.equal(o1[0].view(torch.int32), dout[0].view(torch.int32))
+
+    tflops = flops["addmm"] / (ms["addmm"] * 1e-3) / 1e12
+    dec_gbs = bytes_["decode"] / (ms["decode"] * 1e-3) / 1e9
+    traffic = None
+    try:
+        with open(args.traffic) as f:
+            tr = json.load(f)
+        traffic = tr.get("gemm_bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+
+    out = {
+        "metric": "batch-invariant GEMM TFLOP/s & % bf16 MFMA peak; decode-attn GB/s; bitwise match",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; shapes of the pages' workloads)",
+        "config": {"workload": "addmm bf16 M=8192 K=4096 N=14336 (+bias, bf16 out); one step also runs "
+                               "conv2d SigLIP B=32, attention B=32 H=8 T=1024 D=128, decode B=256 H=32 "
+                               "S=8192 D=64, mm fp32 M=200 K=4096 N=256",
+                   "global_batch": ADDMM["M"], "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+        "roofline_decode": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
+                            "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4)},
+        "decode_attn_GBps": round(dec_gbs, 1),
+        "bitwise_match": {"addmm_row0_M1_vs_M8192": bool(bit_gemm),
+                          "decode_req0_B1_vs_B256": bool(bit_dec)},
+        "ops": detail,
+    }
+
+    del X, Y, Q, Kt, V, Sb, Pb, Ob, dq, dk, dv
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(W, bias, x0, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(W, bias, x0, target_s):
+    """The fp64 oracle on a row sample of the addmm workload, on the host cores."""
+    import torch
+
+    import oracle
+    import synth
+
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    Xs = synth.addmm_batch(x0, 4096, device="cpu")
+    rows, t, r = 0, 0.0, 16
+    while t < target_s and rows + r <= Xs.shape[0]:
+        sel = list(range(rows, rows + r))
+        t0 = time.perf_counter()
+        oracle.mm(Xs, W, bias, rows=sel)
+        t += time.perf_counter() - t0
+        rows += r
+        r = min(max(r, int(r * max(1.0, (target_s - t) / max(t, 1e-3) * 0.5))), 512)
+    flops = 2.0 * rows * ADDMM["K"] * ADDMM["N"]
+    return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{rows} rows of the addmm workload (K=4096, N=14336, fp64 loops), {t:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -103,7 +103,7 @@ int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override) {
         p.sAm = d.sAm; p.sBk = d.sBk; p.sBn = d.sBn; p.sCm = d.sCm;
         p.G2 = d.G2;
         p.sA1 = d.sA1; p.sA2 = d.sA2; p.sB1 = d.sB1; p.sB2 = d.sB2;
-        p.sC1 = d.sC1; p.sC2 = d.sC2; p.sBias2 = d.sBias2;
+        p.sC1 = d.sC1; p.sC2 = d.sC2; p.sBias2 = d.sBias2; p.bias_rows = d.bias_rows;
         p.tiles_m = (int)cdiv(d.M, G16_BM);
         p.tiles_n = (int)cdiv(d.N, G16_BN);
         p.tiles_per_slice = p.tiles_m * p.tiles_n;
@@ -124,7 +124,7 @@ int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override) {
         p.sAm = d.sAm; p.sAk = d.sAk; p.sBk = d.sBk; p.sBn = d.sBn; p.sCm = d.sCm;
         p.G2 = d.G2;
         p.sA1 = d.sA1; p.sA2 = d.sA2; p.sB1 = d.sB1; p.sB2 = d.sB2;
-        p.sC1 = d.sC1; p.sC2 = d.sC2; p.sBias2 = d.sBias2;
+        p.sC1 = d.sC1; p.sC2 = d.sC2; p.sBias2 = d.sBias2; p.bias_rows = d.bias_rows;
         p.tiles_m = (int)cdiv(d.M, G32_BM);
         p.tiles_n = (int)cdiv(d.N, G32_BN);
         p.tiles_per_slice = p.tiles_m * p.tiles_n;
@@ -270,7 +270,7 @@ int bi_conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, const void* x, int64
     d.G1 = N; d.G2 = groups; d.M = g.cog; d.N = g.L; d.K = g.Kp;
     d.A = wp; d.sA1 = 0; d.sA2 = g.cog * g.Kp; d.sAm = g.Kp; d.sAk = 1;
     d.B = u; d.sB1 = groups * g.L * g.Kp; d.sB2 = g.L * g.Kp; d.sBk = 1; d.sBn = g.Kp;
-    d.bias = bias; d.sBias2 = g.cog;
+    d.bias = bias; d.sBias2 = g.cog; d.bias_rows = 1;
     d.C = y; d.sC1 = Cout * g.L; d.sC2 = g.cog * g.L; d.sCm = g.L; d.sCn = 1;
     d.in_dtype = in_dtype; d.out_dtype = out_dtype;
     rc = gemm_check(d);

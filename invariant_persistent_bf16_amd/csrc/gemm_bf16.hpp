@@ -46,7 +46,7 @@ constexpr int G16_LDS_BYTES = 4 * G16_STAGE_BYTES;     // {A, B} x 2 stages: 128
 struct GemmParams {
     const uint16_t* A;     // element (i, k) at A[i*sAm + k]
     const uint16_t* B;     // element (k, j) at B[k*sBk + j*sBn]
-    const uint16_t* bias;  // [N] or nullptr
+    const uint16_t* bias;  // [N] (or [M] if bias_rows) or nullptr
     void* C;               // element (i, j) at C[i*sCm + j]
     int64_t M, N, K;
     int64_t sAm, sBk, sBn, sCm;
@@ -55,6 +55,7 @@ struct GemmParams {
     int64_t G2;
     int64_t sA1, sA2, sB1, sB2, sC1, sC2, sBias2;
     int tiles_m, tiles_n, tiles_per_slice, total_tiles;
+    int bias_rows;         // 1: bias indexed by row (conv output channel), 0: by column
 };
 
 // Physical 16-byte chunk of logical chunk c in LDS row r.
@@ -230,12 +231,13 @@ gemm_bf16_persistent(GemmParams p) {
         // ---- epilogue: + bias (binary32, once), round once, store
         void* Cb = (OUT_BF16 ? (void*)((uint16_t*)p.C + s1 * p.sC1 + s2 * p.sC2)
                              : (void*)((float*)p.C + s1 * p.sC1 + s2 * p.sC2));
+        const uint16_t* bb = p.bias ? p.bias + s2 * p.sBias2 : nullptr;
         float bv[4];
 #pragma unroll
         for (int in = 0; in < 4; ++in) {
             int64_t col = n0 + wn * 128 + in * 32 + (lane & 31);
             col = col < p.N ? col : p.N - 1;
-            bv[in] = p.bias ? bf16_to_f32(p.bias[s2 * p.sBias2 + col]) : 0.0f;
+            bv[in] = (bb && !p.bias_rows) ? bf16_to_f32(bb[col]) : 0.0f;
         }
 #pragma unroll
         for (int im = 0; im < 4; ++im)
@@ -246,7 +248,8 @@ gemm_bf16_persistent(GemmParams p) {
                 for (int r = 0; r < 16; ++r) {
                     const int64_t row = m0 + wm * 128 + im * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                     if (row < p.M && col < p.N) {
-                        const float v = p.bias ? acc[im][in][r] + bv[in] : acc[im][in][r];
+                        float v = acc[im][in][r];
+                        if (bb) v += p.bias_rows ? bf16_to_f32(bb[row]) : bv[in];
                         store_out<OUT_BF16>(Cb, row * p.sCm + col, v);
                     }
                 }

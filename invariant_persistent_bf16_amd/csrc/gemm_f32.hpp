@@ -25,13 +25,14 @@ constexpr int G32_GROUP_M = 8;
 struct GemmF32Params {
     const float* A;     // (i, k) at A[i*sAm + k*sAk]
     const float* B;     // (k, j) at B[k*sBk + j*sBn]
-    const float* bias;  // [N] or nullptr
+    const float* bias;  // [N] (or [M] if bias_rows) or nullptr
     void* C;            // (i, j) at C[i*sCm + j]
     int64_t M, N, K;
     int64_t sAm, sAk, sBk, sBn, sCm;
     int64_t G2;
     int64_t sA1, sA2, sB1, sB2, sC1, sC2, sBias2;
     int tiles_m, tiles_n, tiles_per_slice, total_tiles;
+    int bias_rows;      // 1: bias indexed by row (conv output channel), 0: by column
 };
 
 template <int OUT_BF16>
@@ -136,12 +137,14 @@ gemm_f32_persistent(GemmF32Params p) {
         void* Cb = (OUT_BF16 ? (void*)((uint16_t*)p.C + s1 * p.sC1 + s2 * p.sC2)
                              : (void*)((float*)p.C + s1 * p.sC1 + s2 * p.sC2));
         const int64_t col = n0 + wn * 32 + (lane & 31);
-        const float bv = (p.bias && col < p.N) ? p.bias[s2 * p.sBias2 + col] : 0.0f;
+        const float* bb = p.bias ? p.bias + s2 * p.sBias2 : nullptr;
+        const float bv = (bb && !p.bias_rows && col < p.N) ? bb[col] : 0.0f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int64_t row = m0 + wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
             if (row < p.M && col < p.N) {
-                const float v = p.bias ? acc[r] + bv : acc[r];
+                float v = acc[r];
+                if (bb) v += p.bias_rows ? bb[row] : bv;
                 store_out<OUT_BF16>(Cb, row * p.sCm + col, v);
             }
         }

@@ -14,6 +14,7 @@ struct GemmDesc {
     const void* A; int64_t sA1, sA2, sAm, sAk;
     const void* B; int64_t sB1, sB2, sBk, sBn;
     const void* bias; int64_t sBias2;
+    int bias_rows;   // bias broadcast along columns (0, addmm) or rows (1, conv)
     void* C; int64_t sC1, sC2, sCm, sCn;
     int in_dtype, out_dtype;
 };

@@ -70,3 +70,14 @@ def bitwise_equal(a, b):
     if a.dtype == torch.bfloat16:
         return torch.equal(a.view(torch.int16), b.view(torch.int16))
     return torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def assert_within_dot_bound(got, ref, mag, K, what=""):
+    """Forward error bound of a binary32 sum of K products (exact products, as
+    bf16 x bf16 is exact in binary32): |got - ref| <= gamma_K * sum_k |a_k b_k|,
+    gamma_K = K u / (1 - K u), u = 2^-24."""
+    u = 2.0 ** -24
+    gamma = K * u / (1 - K * u)
+    err = np.abs(np.asarray(got) - np.asarray(ref))
+    bound = gamma * np.asarray(mag)
+    assert np.all(err <= bound), f"{what}: error {err.max():.3e} exceeds gamma_K bound"

@@ -12,8 +12,8 @@ import torch
 
 import oracle
 import synth
-from helpers import (assert_bf16_is_rne_of, assert_bf16_rounding, assert_parity, bitwise_equal,
-                     to64)
+from helpers import (assert_bf16_is_rne_of, assert_bf16_rounding, assert_parity,
+                     assert_within_dot_bound, bitwise_equal, to64)
 
 pytestmark = pytest.mark.gpu
 
@@ -77,7 +77,7 @@ def test_bf16_closed_forms_exact():
 
 @pytest.mark.parametrize("b_layout", ["n_contig", "k_contig"])
 def test_bf16_small_integers_bitwise_equal_oracle(b_layout):
-    M, N, K = 260, 300, 1024
+    M, N, K = 260, 304, 1024
     A = synth.randint((M, K), -4, 4, seed=8, dtype=torch.bfloat16)
     B = synth.randint((K, N), -4, 4, seed=9, dtype=torch.bfloat16)
     if b_layout == "k_contig":
@@ -152,8 +152,13 @@ def test_linspace_batch_dependence_shape():
     o2 = bi.bi_mm(a, b, out_dtype=bi.BI_F32)
     _sync()
     assert bitwise_equal(o1[0], o2[0])
-    ref = oracle.mm(a[:1].cpu(), b.cpu())
-    assert_parity(to64(o1), ref, "linspace row 0")
+    # The sums cancel almost completely (row 0 of a is ~-100 throughout, each
+    # column of b runs from -100 to 100), so the relative error of the result
+    # is unbounded; the binary32 dot-product bound gamma_K * sum |a||b| holds.
+    a0, bc = a[:1].cpu(), b.cpu()
+    ref = oracle.mm(a0, bc)
+    mag = oracle.mm(a0.abs(), bc.abs())
+    assert_within_dot_bound(to64(o1), ref, mag, K=D)
 
 
 # ------------------------------------------------------------------- bmm
