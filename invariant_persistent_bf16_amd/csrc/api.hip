@@ -67,10 +67,11 @@ int gemm_check(const GemmDesc& d) {
             const bool kc = d.sBk == 1 && (d.N == 1 || d.sBn % 8 == 0);
             const bool nc = d.sBn == 1 && d.sBk % 8 == 0 && d.N % 8 == 0;
             if (!kc && !nc) return BI_ERR_LAYOUT;
-            // Row offsets inside one tile are 32-bit.
-            const int64_t lim = (1ll << 31) - 1;
+            // Byte offsets inside one tile are 32-bit buffer offsets below 2^31.
+            const int64_t lim = (1ll << 30) - 512;
             if (d.sAm * G16_BM > lim || (kc ? d.sBn * G16_BN : d.sBk * G16_BK) > lim)
                 return BI_ERR_UNSUPPORTED;
+            if (d.sCm * 128 > lim) return BI_ERR_UNSUPPORTED;   // 32-bit epilogue offsets
         }
         if (d.bias && !aligned(d.bias, 2)) return BI_ERR_LAYOUT;
     } else {
@@ -79,7 +80,7 @@ int gemm_check(const GemmDesc& d) {
     }
     const int64_t bm = d.in_dtype == BI_BF16 ? G16_BM : G32_BM;
     const int64_t bn = d.in_dtype == BI_BF16 ? G16_BN : G32_BN;
-    if (d.G1 > (1ll << 30) || d.G2 > (1ll << 30)) return BI_ERR_UNSUPPORTED;
+    if (d.G1 > (1ll << 30) || d.G2 > (1ll << 30) || d.K > (1ll << 30)) return BI_ERR_UNSUPPORTED;
     const int64_t tiles = cdiv(d.M, bm) * cdiv(d.N, bn);
     const int64_t slices = d.G1 * d.G2;
     if (slices > (1ll << 30) || tiles > (1ll << 30) || tiles * slices > (1ll << 30))
