@@ -48,8 +48,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target host time of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
-                    help="HBM traffic per launch measured by rocprofv3 counters (optional)")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "gemm_bf16_addmm_M8192_traffic.txt"),
+                    help="HBM-side bytes per GEMM launch measured with rocprofv3 counters")
     return ap.parse_args()
 
 
@@ -180,13 +180,7 @@ def main():
 
     tflops = flops["addmm"] / (ms["addmm"] * 1e-3) / 1e12
     dec_gbs = bytes_["decode"] / (ms["decode"] * 1e-3) / 1e9
-    traffic = None
-    try:
-        with open(args.traffic) as f:
-            tr = json.load(f)
-        traffic = tr.get("gemm_bytes_per_launch")
-    except (OSError, ValueError):
-        pass
+    traffic = gemm_traffic(args.traffic)
 
     out = {
         "metric": "batch-invariant GEMM TFLOP/s & % bf16 MFMA peak; decode-attn GB/s; bitwise match",
@@ -222,6 +216,21 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def gemm_traffic(path):
+    """Counter-measured bytes per GEMM launch, or None if the kernel source
+    changed since the counters were taken (or no record exists)."""
+    import hashlib
+    try:
+        rec = dict(line.split(":", 1) for line in open(path) if ":" in line and not line.startswith("#"))
+        src = b"".join(open(os.path.join(ROOT, "invariant_persistent_bf16_amd", "csrc", f), "rb").read()
+                       for f in ("gemm_bf16.hpp", "common.hpp"))
+        if hashlib.sha256(src).hexdigest() != rec["source_sha256"].strip():
+            return None
+        return int(rec["bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(W, bias, x0, target_s):
     """The fp64 oracle on a row sample of the addmm workload, on the host cores."""
     import torch
@@ -230,7 +239,7 @@ def cpu_baseline(W, bias, x0, target_s):
     import synth
 
     cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
-    Xs = synth.addmm_batch(x0, 4096, device="cpu")
+    Xs = synth.addmm_batch(x0, 8192, device="cpu")
     rows, t, r = 0, 0.0, 16
     while t < target_s and rows + r <= Xs.shape[0]:
         sel = list(range(rows, rows + r))
