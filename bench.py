@@ -209,11 +209,70 @@ def main():
         "ops": detail,
     }
 
+    out["invariance_cost"] = invariance_cost(Wd, bd, x0, dq, dk, dv, Y)
+
     del X, Y, Q, Kt, V, Sb, Pb, Ob, dq, dk, dv
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(W, bias, x0, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def _time_ms(fn, iters=20):
+    import torch
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def invariance_cost(Wd, bd, x0, dq, dk, dv, Y):
+    """Untimed extra: the invariant kernels against batch-size-tuned variants
+    (split-K for the GEMM filling the CUs, split-KV by load for decode) at the
+    batch sizes where they differ, plus an HBM read-rate probe."""
+    import torch
+
+    import synth
+    from invariant_persistent_bf16_amd import bi, bi_bench
+
+    dev = Wd.device
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    res = {"addmm": {}, "decode": {}}
+    K, N = ADDMM["K"], ADDMM["N"]
+    for M in (1, 64, 200, 2048):
+        X = synth.addmm_batch(x0, M, device=dev)
+        s = bi_bench.splitk_policy(M, N, K, 0)
+        ws = torch.empty(max(1, s * M * N), dtype=torch.float32, device=dev)
+        yv = Y[:M]
+        ti = _time_ms(lambda: bi.bi_addmm(bd, X, Wd, out=yv))
+        ts = _time_ms(lambda: bi_bench.addmm_splitk(bd, X, Wd, s, out=yv, workspace=ws))
+        res["addmm"][str(M)] = {"invariant_us": round(ti * 1e3, 2), "splitk_us": round(ts * 1e3, 2),
+                                "splits": s, "invariant_over_splitk": round(ti / ts, 3)}
+    H, S, D = DEC["H"], DEC["S"], DEC["D"]
+    for B in (1, 16, 64):
+        q, k, v = dq[:B], dk[:B], dv[:B]
+        s = bi_bench.decode_splits_policy(B, cus)
+        o = torch.empty(B, H, D, dtype=torch.float32, device=dev)
+        ws = torch.empty(bi_bench.lib().bi_bench_decode_attn_splits_workspace_bytes(B, H, S, D, s) // 4 + 1,
+                         dtype=torch.float32, device=dev)
+        wsf = torch.empty(bi.bi_decode_attn_workspace_bytes(B, H, S, D) // 4 + 1, dtype=torch.float32,
+                          device=dev)
+        tf = _time_ms(lambda: bi.bi_decode_attn(q, k, v, 0.125, out=o, workspace=wsf))
+        tl = _time_ms(lambda: bi_bench.decode_attn_splits(q, k, v, 0.125, s, out=o, workspace=ws))
+        gbs = B * H * 2 * S * D * 2 / 1e9
+        res["decode"][str(B)] = {"fixed_chunk_us": round(tf * 1e3, 2), "by_load_us": round(tl * 1e3, 2),
+                                 "splits_by_load": s, "fixed_GBps": round(gbs / (tf * 1e-3), 1),
+                                 "fixed_over_by_load": round(tf / tl, 3)}
+    sink = torch.empty(65536, dtype=torch.int32, device=dev)
+    tp = _time_ms(lambda: bi_bench.read_probe(dk, sink), iters=5)
+    res["hbm_read_probe_GBps"] = round(dk.numel() * 2 / (tp * 1e-3) / 1e9, 1)
+    return res
 
 
 def gemm_traffic(path):

@@ -1,0 +1,97 @@
+/*
+ * bi_bench.h — benchmark and test variants of the bi_* operations (libbi_bench.so).
+ *
+ * NOT part of the product interface.  These entry points exist to measure the
+ * cost of batch invariance and to show that the invariance tests can tell a
+ * batch-dependent schedule apart: they implement the batch-size-dependent
+ * splits that the deterministic-inference handbook page (anrans.github.io,
+ * section "根源：浮点加法的顺序") describes as the cause of batch dependence, and
+ * a grid override for the invariant GEMM.  libbi_bench.so also exports every
+ * bi.h entry point.  Conventions (device pointers, element strides, void*
+ * stream, bi_status return codes, caller-owned workspaces) are those of bi.h.
+ */
+#ifndef BI_BENCH_H
+#define BI_BENCH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "bi.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * bi_bench_gemm_grid — the invariant GEMM of bi_bmm (with an optional column
+ * bias, as bi_addmm) launched on a forced persistent grid of `grid`
+ * workgroups (1 <= grid <= 65535).  Its results must equal bi_bmm's bit for
+ * bit at any grid: the tile arithmetic does not depend on which workgroup
+ * runs a tile.
+ */
+int bi_bench_gemm_grid(int64_t G, int64_t M, int64_t N, int64_t K,
+                       const void* A, int64_t sAg, int64_t sAm, int64_t sAk,
+                       const void* B, int64_t sBg, int64_t sBk, int64_t sBn,
+                       const void* bias,
+                       void* C, int64_t sCg, int64_t sCm, int64_t sCn,
+                       int in_dtype, int out_dtype, int grid, void* stream);
+
+/*
+ * bi_bench_splitk_policy — the number of K splits a batch-size-tuned GEMM
+ * would pick for an M x N x K product.
+ *   rule 0: fill the compute units: splits = clamp(CUs / tiles, 1, 16),
+ *           tiles = ceil(M/256) * ceil(N/256), reduced until K splits evenly
+ *           into multiples of 64 (needs a current device);
+ *   rule 1: the handbook's simulation: 4 if M < 64 else 1.
+ * Returns the split count (>= 1) or a negative bi_status.
+ */
+int bi_bench_splitk_policy(int64_t M, int64_t N, int64_t K, int rule);
+
+/* Workspace of bi_bench_addmm_splitk: splits * M * N binary32 partial sums. */
+size_t bi_bench_addmm_splitk_workspace_bytes(int64_t M, int64_t N, int splits);
+
+/*
+ * bi_bench_addmm_splitk — C = A @ B + bias with K cut into `splits` equal
+ * parts (K % (8 * splits) == 0): each part is an independent invariant GEMM
+ * into ws, then the parts are added in part order and the bias is added.
+ * Layout rules: those of bi_addmm.  A different split count gives different
+ * bits: this is the batch-dependent schedule the invariant path forbids.
+ */
+int bi_bench_addmm_splitk(int64_t M, int64_t N, int64_t K,
+                          const void* A, int64_t sAm, int64_t sAk,
+                          const void* B, int64_t sBk, int64_t sBn,
+                          const void* bias,
+                          void* C, int64_t sCm, int64_t sCn,
+                          int in_dtype, int out_dtype, int splits,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* The handbook's load-based split count: max(1, min(64, sms / B)). */
+int bi_bench_decode_splits_policy(int64_t B, int sms);
+
+size_t bi_bench_decode_attn_splits_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t D,
+                                                   int splits);
+
+/*
+ * bi_bench_decode_attn_splits — decode attention with the KV sequence cut
+ * into `splits` equal parts (S % splits == 0, S / splits a multiple of 8)
+ * instead of fixed 2048-token chunks.  Parts longer than 2048 tokens are
+ * computed as 2048-token pieces merged inside the part, then the parts are
+ * merged in order.  Arguments as bi_decode_attn.
+ */
+int bi_bench_decode_attn_splits(int64_t B, int64_t H, int64_t S, int64_t D,
+                                const void* q, const void* k, const void* v, void* out,
+                                float scale, void* ws, size_t ws_bytes,
+                                int in_dtype, int out_dtype, int splits, void* stream);
+
+/*
+ * bi_bench_read_probe — streams `bytes` (a multiple of 16) from `p` with
+ * 16-byte loads and writes one reduction word per workgroup to `sink`
+ * (at least 4 * 65536 bytes), to measure the achievable HBM read rate.
+ */
+int bi_bench_read_probe(const void* p, size_t bytes, void* sink, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BI_BENCH_H */

@@ -1,0 +1,110 @@
+"""ctypes binding of libbi_bench.so (benchmark / test variants, include/bi_bench.h).
+
+Marshalling only, like bi.py.  Not part of the product path: these calls
+exist to measure the cost of batch invariance and to show that the tests
+detect a batch-dependent reduction order.
+"""
+import ctypes
+import os
+
+import torch
+
+from . import bi as _bi
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbi_bench.so")
+_i64, _vp, _int, _f32, _sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+_SIGS = {
+    "bi_bench_gemm_grid": (_int, [_i64] * 4 + [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _vp,
+                                             _i64, _i64, _i64, _int, _int, _int, _vp]),
+    "bi_bench_splitk_policy": (_int, [_i64, _i64, _i64, _int]),
+    "bi_bench_addmm_splitk_workspace_bytes": (_sz, [_i64, _i64, _int]),
+    "bi_bench_addmm_splitk": (_int, [_i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i64,
+                                     _i64, _int, _int, _int, _vp, _sz, _vp]),
+    "bi_bench_decode_splits_policy": (_int, [_i64, _int]),
+    "bi_bench_decode_attn_splits_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _int]),
+    "bi_bench_decode_attn_splits": (_int, [_i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _f32, _vp, _sz,
+                                           _int, _int, _int, _vp]),
+    "bi_bench_read_probe": (_int, [_vp, _sz, _vp, _vp]),
+}
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+_p, _dt, _stream, _check = _bi._p, _bi._dt, _bi._stream, _bi._check
+
+
+def gemm_grid(A, B, grid, bias=None, out=None, out_dtype=None, stream=None):
+    """The invariant batched GEMM (A [G,M,K] or [M,K]) on a forced grid."""
+    squeeze = A.dim() == 2
+    if squeeze:
+        A, B = A.unsqueeze(0), B.unsqueeze(0)
+    G, M, K = A.shape
+    N = B.shape[2]
+    od = _dt(A) if out_dtype is None else out_dtype
+    C = out if out is not None else torch.empty((G, M, N), dtype=_bi._tdt(od), device=A.device)
+    if C.dim() == 2:
+        C = C.unsqueeze(0)
+    _check("bi_bench_gemm_grid", lib().bi_bench_gemm_grid(
+        G, M, N, K, _p(A), A.stride(0), A.stride(1), A.stride(2), _p(B), B.stride(0), B.stride(1),
+        B.stride(2), _p(bias), _p(C), C.stride(0), C.stride(1), C.stride(2), _dt(A), _dt(C), grid,
+        _stream(stream)))
+    return C[0] if squeeze else C
+
+
+def splitk_policy(M, N, K, rule=0):
+    r = lib().bi_bench_splitk_policy(M, N, K, rule)
+    if r < 0:
+        raise _bi.BIError("bi_bench_splitk_policy", r)
+    return r
+
+
+def addmm_splitk(bias, A, B, splits, out=None, out_dtype=None, workspace=None, stream=None):
+    M, K = A.shape
+    N = B.shape[1]
+    od = _dt(A) if out_dtype is None else out_dtype
+    C = out if out is not None else torch.empty((M, N), dtype=_bi._tdt(od), device=A.device)
+    need = lib().bi_bench_addmm_splitk_workspace_bytes(M, N, splits)
+    if workspace is None:
+        workspace = torch.empty(max(need // 4, 1), dtype=torch.float32, device=A.device)
+    _check("bi_bench_addmm_splitk", lib().bi_bench_addmm_splitk(
+        M, N, K, _p(A), A.stride(0), A.stride(1), _p(B), B.stride(0), B.stride(1), _p(bias), _p(C),
+        C.stride(0), C.stride(1), _dt(A), _dt(C), splits, _p(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return C
+
+
+def decode_splits_policy(B, sms):
+    return lib().bi_bench_decode_splits_policy(B, sms)
+
+
+def decode_attn_splits(q, k, v, scale, splits, out=None, out_dtype=_bi.BI_F32, workspace=None,
+                       stream=None):
+    B, H, S, D = k.shape
+    o = out if out is not None else torch.empty((B, H, D), dtype=_bi._tdt(out_dtype), device=q.device)
+    need = lib().bi_bench_decode_attn_splits_workspace_bytes(B, H, S, D, splits)
+    if workspace is None:
+        workspace = torch.empty(max(need // 4, 1), dtype=torch.float32, device=q.device)
+    _check("bi_bench_decode_attn_splits", lib().bi_bench_decode_attn_splits(
+        B, H, S, D, _p(q), _p(k), _p(v), _p(o), float(scale), _p(workspace),
+        workspace.numel() * workspace.element_size(), _dt(q), _dt(o), splits, _stream(stream)))
+    return o
+
+
+def read_probe(buf, sink, stream=None):
+    _check("bi_bench_read_probe", lib().bi_bench_read_probe(
+        _p(buf), buf.numel() * buf.element_size(), _p(sink), _stream(stream)))

@@ -18,7 +18,7 @@ FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
 
 LIBS = {
     "libbi.so": ["csrc/api.hip"],
-    "libbi_bench.so": ["csrc/bench_api.hip"],
+    "libbi_bench.so": ["csrc/api.hip", "csrc/bench_api.hip"],
 }
 
 

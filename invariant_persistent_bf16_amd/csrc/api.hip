@@ -334,12 +334,12 @@ int bi_decode_attn(int64_t B, int64_t H, int64_t S, int64_t D, const void* q, co
     float* wsf = (float*)ws;
     if (D == 64) {
         hipLaunchKernelGGL((decode_chunk_kernel<64>), g1, dim3(DEC_THREADS), 0, st,
-                           (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, wsf, S, (int)nchunk, scale);
+                           (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, wsf, S, (int)nchunk, DEC_CHUNK, scale);
         if (out_dtype == BI_BF16) hipLaunchKernelGGL((decode_merge_kernel<64, 1>), g2, dim3(256), 0, st, wsf, out, BH, (int)nchunk);
         else                      hipLaunchKernelGGL((decode_merge_kernel<64, 0>), g2, dim3(256), 0, st, wsf, out, BH, (int)nchunk);
     } else {
         hipLaunchKernelGGL((decode_chunk_kernel<128>), g1, dim3(DEC_THREADS), 0, st,
-                           (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, wsf, S, (int)nchunk, scale);
+                           (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, wsf, S, (int)nchunk, DEC_CHUNK, scale);
         if (out_dtype == BI_BF16) hipLaunchKernelGGL((decode_merge_kernel<128, 1>), g2, dim3(256), 0, st, wsf, out, BH, (int)nchunk);
         else                      hipLaunchKernelGGL((decode_merge_kernel<128, 0>), g2, dim3(256), 0, st, wsf, out, BH, (int)nchunk);
     }

@@ -1,0 +1,223 @@
+// Benchmark / test variants (include/bi_bench.h).  They reuse the product
+// kernels; what they add is a batch-size-dependent choice (split-K for the
+// GEMM, split count by load for decode) or a forced launch grid.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+
+#include "../../include/bi_bench.h"
+#include "decode.hpp"
+#include "gemm_bf16.hpp"
+#include "gemm_f32.hpp"
+#include "internal.hpp"
+
+namespace bi {
+
+// Sum of `splits` partial products in part order, then + bias, then round.
+template <int OUT_BF16, int BIAS_BF16>
+__global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits, int64_t M, int64_t N,
+                                     const void* __restrict__ bias, void* __restrict__ C, int64_t sCm) {
+    const int64_t MN = M * N;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < MN;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        float v = part[i];
+        for (int s = 1; s < splits; ++s) v += part[s * MN + i];
+        const int64_t r = i / N, c = i - (i / N) * N;
+        if (bias) v += BIAS_BF16 ? bf16_to_f32(((const uint16_t*)bias)[c]) : ((const float*)bias)[c];
+        store_out<OUT_BF16>(C, r * sCm + c, v);
+    }
+}
+
+// Two-level merge: the `nsub` piece triples of each part are merged in piece
+// order, then the parts in part order (nsub == 1: one flat merge).
+template <int D, int OUT_BF16>
+__global__ void decode_merge_parts_kernel(const float* __restrict__ ws, void* __restrict__ out,
+                                          int64_t BH, int parts, int nsub) {
+    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (i >= BH * D) return;
+    const int64_t bh = i / D;
+    const int d = (int)(i - bh * D);
+    const float* tp = ws + bh * (int64_t)parts * nsub * (2 + D);
+    float Mall = -INFINITY;
+    float pm[64], pl[64], po[64];
+    for (int p = 0; p < parts; ++p) {
+        const float* t = tp + (int64_t)p * nsub * (2 + D);
+        float m = t[0];
+        for (int s = 1; s < nsub; ++s) m = fmaxf(m, t[s * (2 + D)]);
+        float l = 0.0f, o = 0.0f;
+        for (int s = 0; s < nsub; ++s) {
+            const float w = expf(t[s * (2 + D)] - m);
+            l = fmaf(w, t[s * (2 + D) + 1], l);
+            o = fmaf(w, t[s * (2 + D) + 2 + d], o);
+        }
+        pm[p] = m; pl[p] = l; po[p] = o;
+        Mall = fmaxf(Mall, m);
+    }
+    float num = 0.0f, den = 0.0f;
+    for (int p = 0; p < parts; ++p) {
+        const float w = expf(pm[p] - Mall);
+        num = fmaf(w, po[p], num);
+        den = fmaf(w, pl[p], den);
+    }
+    store_out<OUT_BF16>(out, i, num / den);
+}
+
+__global__ void read_probe_kernel(const u32x4_t* __restrict__ p, int64_t n16, uint32_t* __restrict__ sink) {
+    uint32_t acc = 0;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n16;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const u32x4_t v = __builtin_nontemporal_load(p + i);
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+    for (int o = 32; o >= 1; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o, 64);
+    if (threadIdx.x == 0) sink[blockIdx.x] = acc;
+}
+
+static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace bi
+
+using namespace bi;
+
+extern "C" {
+
+int bi_bench_gemm_grid(int64_t G, int64_t M, int64_t N, int64_t K, const void* A, int64_t sAg,
+                       int64_t sAm, int64_t sAk, const void* B, int64_t sBg, int64_t sBk,
+                       int64_t sBn, const void* bias, void* C, int64_t sCg, int64_t sCm,
+                       int64_t sCn, int in_dtype, int out_dtype, int grid, void* stream) {
+    if (grid < 1 || grid > 65535) return BI_ERR_UNSUPPORTED;
+    GemmDesc d;
+    std::memset(&d, 0, sizeof(d));
+    d.G1 = G; d.G2 = 1; d.M = M; d.N = N; d.K = K;
+    d.A = A; d.sA1 = sAg; d.sAm = sAm; d.sAk = sAk;
+    d.B = B; d.sB1 = sBg; d.sBk = sBk; d.sBn = sBn;
+    d.bias = bias; d.C = C; d.sC1 = sCg; d.sCm = sCm; d.sCn = sCn;
+    d.in_dtype = in_dtype; d.out_dtype = out_dtype;
+    int rc = gemm_check(d);
+    if (rc != BI_OK) return rc;
+    return gemm_launch(d, (hipStream_t)stream, grid);
+}
+
+int bi_bench_splitk_policy(int64_t M, int64_t N, int64_t K, int rule) {
+    if (M < 1 || N < 1 || K < 1) return BI_ERR_SHAPE;
+    if (rule == 1) return (M < 64 && K % (8 * 4) == 0) ? 4 : 1;
+    if (rule != 0) return BI_ERR_UNSUPPORTED;
+    int cus = 0;
+    int rc = device_cu_count(&cus);
+    if (rc != BI_OK) return rc;
+    const int64_t tiles = cdiv(M, G16_BM) * cdiv(N, G16_BN);
+    int s = (int)std::max<int64_t>(1, std::min<int64_t>(16, cus / tiles));
+    while (s > 1 && K % (64 * s) != 0) --s;
+    return s;
+}
+
+size_t bi_bench_addmm_splitk_workspace_bytes(int64_t M, int64_t N, int splits) {
+    if (M < 0 || N < 0 || splits < 1) return 0;
+    return (size_t)(splits * M * N * 4);
+}
+
+int bi_bench_addmm_splitk(int64_t M, int64_t N, int64_t K, const void* A, int64_t sAm, int64_t sAk,
+                          const void* B, int64_t sBk, int64_t sBn, const void* bias, void* C,
+                          int64_t sCm, int64_t sCn, int in_dtype, int out_dtype, int splits,
+                          void* ws, size_t ws_bytes, void* stream) {
+    if (splits < 1 || splits > 64) return BI_ERR_UNSUPPORTED;
+    if (K % (8 * splits) != 0) return BI_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return BI_OK;
+    if (!C) return BI_ERR_NULL;
+    if (!ws || ws_bytes < bi_bench_addmm_splitk_workspace_bytes(M, N, splits) || ((uintptr_t)ws % 16))
+        return BI_ERR_WORKSPACE;
+    if (sCn != 1 || sCm < N) return BI_ERR_LAYOUT;
+    const int64_t Ks = K / splits;
+    const int64_t esz = in_dtype == BI_BF16 ? 2 : 4;
+    // Part s is slice s of a batched product over K offsets s*Ks.
+    GemmDesc d;
+    std::memset(&d, 0, sizeof(d));
+    d.G1 = splits; d.G2 = 1; d.M = M; d.N = N; d.K = Ks;
+    d.A = A; d.sA1 = Ks * sAk; d.sAm = sAm; d.sAk = sAk;
+    d.B = B; d.sB1 = Ks * sBk; d.sBk = sBk; d.sBn = sBn;
+    d.C = ws; d.sC1 = M * N; d.sCm = N; d.sCn = 1;
+    d.in_dtype = in_dtype; d.out_dtype = BI_F32;
+    (void)esz;
+    int rc = gemm_check(d);
+    if (rc != BI_OK) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    rc = gemm_launch(d, st, 0);
+    if (rc != BI_OK) return rc;
+    const int grid = (int)std::min<int64_t>(cdiv(M * N, 256), 65535);
+    const bool ob = out_dtype == BI_BF16, bb = in_dtype == BI_BF16;
+    if (ob && bb)   hipLaunchKernelGGL((splitk_reduce_kernel<1, 1>), dim3(grid), dim3(256), 0, st, (const float*)ws, splits, M, N, bias, C, sCm);
+    else if (ob)    hipLaunchKernelGGL((splitk_reduce_kernel<1, 0>), dim3(grid), dim3(256), 0, st, (const float*)ws, splits, M, N, bias, C, sCm);
+    else if (bb)    hipLaunchKernelGGL((splitk_reduce_kernel<0, 1>), dim3(grid), dim3(256), 0, st, (const float*)ws, splits, M, N, bias, C, sCm);
+    else            hipLaunchKernelGGL((splitk_reduce_kernel<0, 0>), dim3(grid), dim3(256), 0, st, (const float*)ws, splits, M, N, bias, C, sCm);
+    return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_LAUNCH;
+}
+
+int bi_bench_decode_splits_policy(int64_t B, int sms) {
+    if (B < 1 || sms < 1) return BI_ERR_SHAPE;
+    return (int)std::max<int64_t>(1, std::min<int64_t>(64, sms / B));
+}
+
+size_t bi_bench_decode_attn_splits_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t D,
+                                                   int splits) {
+    if (B < 0 || H < 0 || S < 1 || D < 1 || splits < 1 || S % splits) return 0;
+    const int64_t L = S / splits;
+    const int64_t nsub = L > DEC_CHUNK ? cdiv(L, DEC_CHUNK) : 1;
+    return (size_t)(B * H * splits * nsub * (2 + D) * 4);
+}
+
+int bi_bench_decode_attn_splits(int64_t B, int64_t H, int64_t S, int64_t D, const void* q,
+                                const void* k, const void* v, void* out, float scale, void* ws,
+                                size_t ws_bytes, int in_dtype, int out_dtype, int splits,
+                                void* stream) {
+    if (in_dtype != BI_BF16) return BI_ERR_DTYPE;
+    if (out_dtype != BI_F32 && out_dtype != BI_BF16) return BI_ERR_DTYPE;
+    if (B < 0 || H < 0 || S < 1) return BI_ERR_SHAPE;
+    if (D != 64 && D != 128) return BI_ERR_UNSUPPORTED;
+    if (splits < 1 || splits > 64 || S % splits) return BI_ERR_UNSUPPORTED;
+    const int64_t L = S / splits;
+    if (L % 8) return BI_ERR_UNSUPPORTED;
+    if (L > DEC_CHUNK && L % DEC_CHUNK) return BI_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0) return BI_OK;
+    if (!q || !k || !v || !out) return BI_ERR_NULL;
+    if (!ws || ws_bytes < bi_bench_decode_attn_splits_workspace_bytes(B, H, S, D, splits) ||
+        ((uintptr_t)ws % 16))
+        return BI_ERR_WORKSPACE;
+    int cus = 0;
+    int rc = device_cu_count(&cus);
+    if (rc != BI_OK) return rc;
+    const int piece = (int)std::min<int64_t>(L, DEC_CHUNK);
+    const int nsub = (int)(L / piece);
+    const int64_t BH = B * H;
+    const int npieces = splits * nsub;
+    hipStream_t st = (hipStream_t)stream;
+    float* wsf = (float*)ws;
+    const dim3 g1((unsigned)(BH * npieces)), g2((unsigned)cdiv(BH * D, 256));
+    if (D == 64) {
+        hipLaunchKernelGGL((decode_chunk_kernel<64>), g1, dim3(DEC_THREADS), 0, st,
+                           (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, wsf, S, npieces, piece, scale);
+        if (out_dtype == BI_BF16) hipLaunchKernelGGL((decode_merge_parts_kernel<64, 1>), g2, dim3(256), 0, st, wsf, out, BH, splits, nsub);
+        else                      hipLaunchKernelGGL((decode_merge_parts_kernel<64, 0>), g2, dim3(256), 0, st, wsf, out, BH, splits, nsub);
+    } else {
+        hipLaunchKernelGGL((decode_chunk_kernel<128>), g1, dim3(DEC_THREADS), 0, st,
+                           (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, wsf, S, npieces, piece, scale);
+        if (out_dtype == BI_BF16) hipLaunchKernelGGL((decode_merge_parts_kernel<128, 1>), g2, dim3(256), 0, st, wsf, out, BH, splits, nsub);
+        else                      hipLaunchKernelGGL((decode_merge_parts_kernel<128, 0>), g2, dim3(256), 0, st, wsf, out, BH, splits, nsub);
+    }
+    return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_LAUNCH;
+}
+
+int bi_bench_read_probe(const void* p, size_t bytes, void* sink, void* stream) {
+    if (!p || !sink) return BI_ERR_NULL;
+    if (bytes % 16 || ((uintptr_t)p % 16)) return BI_ERR_LAYOUT;
+    int cus = 0;
+    int rc = device_cu_count(&cus);
+    if (rc != BI_OK) return rc;
+    const int64_t n16 = (int64_t)(bytes / 16);
+    const int grid = (int)std::min<int64_t>(std::max<int64_t>(1, cdiv(n16, 256)), std::min(65536, 16 * cus));
+    hipLaunchKernelGGL(read_probe_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream,
+                       (const u32x4_t*)p, n16, (uint32_t*)sink);
+    return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -33,11 +33,14 @@ constexpr int DEC_WAVES = 8;
 constexpr int DEC_THREADS = DEC_WAVES * 64;
 constexpr int DEC_TOK_PER_WAVE = DEC_CHUNK / DEC_WAVES;   // 256
 
+// `chunk` is the chunk length in tokens (a multiple of 8, at most DEC_CHUNK);
+// the product path always passes DEC_CHUNK.  Wave w of chunk c owns tokens
+// [c*chunk + w*chunk/8, c*chunk + (w+1)*chunk/8).
 template <int D>
 __global__ void __launch_bounds__(DEC_THREADS)
 decode_chunk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                     const uint16_t* __restrict__ v, float* __restrict__ ws,
-                    int64_t S, int nchunk, float scale) {
+                    int64_t S, int nchunk, int chunk, float scale) {
     constexpr int LPT = D / 8;               // lanes per token
     constexpr int TPI = 64 / LPT;            // tokens per wave-wide load
     constexpr int NI = DEC_TOK_PER_WAVE / TPI;
@@ -54,8 +57,10 @@ decode_chunk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     const int tg = lane / LPT;               // token slot within a load
     const int64_t bh = blockIdx.x / nchunk;
     const int c = blockIdx.x - (int)(bh * nchunk);
-    const int64_t t0 = (int64_t)c * DEC_CHUNK + wave * DEC_TOK_PER_WAVE + tg;
-    const int64_t t_end = min(S, (int64_t)(c + 1) * DEC_CHUNK);
+    const int tw = chunk / DEC_WAVES;                       // tokens of this wave
+    const int64_t w0 = (int64_t)c * chunk + (int64_t)wave * tw;
+    const int64_t t0 = w0 + tg;
+    const int64_t t_end = min(S, w0 + tw);
 
     const uint16_t* kb = k + (bh * S) * D + sub * 8;
     const uint16_t* vb = v + (bh * S) * D + sub * 8;

@@ -1,0 +1,119 @@
+"""GPU checks of the benchmark variants (libbi_bench.so).
+
+* The invariant GEMM gives the same bits on any persistent grid (1, 7, 256
+  workgroups): which workgroup runs a tile does not enter the arithmetic.
+* Negative controls: a batch-size-tuned split-K GEMM and a load-based split-KV
+  decode are correct (they match the oracle) but NOT batch invariant, and
+  reproduce on the GPU the patterns the deterministic-inference handbook
+  prints for its CPU experiments (section "根源：浮点加法的顺序"): split-K by M
+  gives row 0 equal to "alone" for M = 8, 63 and different for M = 64, 200;
+  splits by load (132 units) give request 0 equal to batch 1 only at B = 1.
+  This shows the invariance tests can see a changed reduction order.
+"""
+import json
+import os
+
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import assert_parity, bitwise_equal, to64
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from invariant_persistent_bf16_amd import bi
+    from invariant_persistent_bf16_amd import bi_bench
+DEV = "cuda"
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.mark.parametrize("b_layout", ["n_contig", "k_contig"])
+def test_gemm_grid_independent(b_layout):
+    M, N, K = 600, 776, 320
+    A = synth.randn((M, K), seed=1, dtype=torch.bfloat16).to(DEV)
+    B = synth.randn((K, N), seed=2, dtype=torch.bfloat16).to(DEV)
+    if b_layout == "k_contig":
+        B = B.t().contiguous().t()
+    bias = synth.randn((N,), seed=3, dtype=torch.bfloat16).to(DEV)
+    ref = bi.bi_addmm(bias, A, B, out_dtype=bi.BI_F32)
+    outs = [bi_bench.gemm_grid(A, B, g, bias=bias, out_dtype=bi.BI_F32) for g in (1, 7, 256, 1000)]
+    torch.cuda.synchronize()
+    for g, o in zip((1, 7, 256, 1000), outs):
+        assert bitwise_equal(o, ref), f"grid {g} changed the result"
+
+
+def test_fp32_gemm_grid_independent():
+    A = synth.randn((130, 300), seed=4).to(DEV)
+    B = synth.randn((300, 200), seed=5).to(DEV)
+    ref = bi.bi_mm(A, B)
+    outs = [bi_bench.gemm_grid(A, B, g) for g in (1, 3, 64)]
+    torch.cuda.synchronize()
+    assert all(bitwise_equal(o, ref) for o in outs)
+
+
+def test_splitk_handbook_rule_pattern_on_gpu():
+    g = json.load(open(os.path.join(GOLDEN, "handbook_splitk_gemm.json")))
+    W, bias, x0 = synth.addmm_shared(N=2048)
+    Wd, bd = W.to(DEV), bias.to(DEV)
+    alone_X = x0.to(DEV)
+    alone = bi_bench.addmm_splitk(bd, alone_X, Wd, bi_bench.splitk_policy(1, 2048, 4096, rule=1),
+                                  out_dtype=bi.BI_F32)
+    got = []
+    for M in g["batches"]:
+        X = synth.addmm_batch(x0, M, device=DEV)
+        s = bi_bench.splitk_policy(M, 2048, 4096, rule=1)
+        C = bi_bench.addmm_splitk(bd, X, Wd, s, out_dtype=bi.BI_F32)
+        torch.cuda.synchronize()
+        got.append(bitwise_equal(C[0], alone[0]))
+        assert_parity(to64(C[:4]), oracle.mm(X[:4].cpu(), W, bias), f"split-K M={M}")
+    assert got == g["row0_equals_alone_by_batch"]
+    # The invariant kernel on the same inputs: always equal.
+    inv_alone = bi.bi_addmm(bd, alone_X, Wd, out_dtype=bi.BI_F32)
+    for M in g["batches"]:
+        X = synth.addmm_batch(x0, M, device=DEV)
+        C = bi.bi_addmm(bd, X, Wd, out_dtype=bi.BI_F32)
+        torch.cuda.synchronize()
+        assert bitwise_equal(C[0], inv_alone[0])
+
+
+def test_splitk_fill_policy_breaks_invariance_at_full_shape():
+    W, bias, x0 = synth.addmm_shared()
+    Wd, bd = W.to(DEV), bias.to(DEV)
+    s1 = bi_bench.splitk_policy(1, 14336, 4096, rule=0)
+    s8k = bi_bench.splitk_policy(8192, 14336, 4096, rule=0)
+    assert s1 > 1 and s8k == 1
+    c1 = bi_bench.addmm_splitk(bd, x0.to(DEV), Wd, s1, out_dtype=bi.BI_F32)
+    X = synth.addmm_batch(x0, 8192, device=DEV)
+    c8k = bi_bench.addmm_splitk(bd, X, Wd, s8k, out_dtype=bi.BI_F32)
+    inv = bi.bi_addmm(bd, X, Wd, out_dtype=bi.BI_F32)
+    torch.cuda.synchronize()
+    assert not bitwise_equal(c1[0], c8k[0]), "the negative control should change row 0"
+    assert bitwise_equal(c8k, inv), "one split is the invariant kernel"
+    assert_parity(to64(c1), oracle.mm(x0, W, bias), "split-K M=1")
+
+
+def test_decode_by_load_pattern_on_gpu():
+    g = json.load(open(os.path.join(GOLDEN, "handbook_decode_splits.json")))
+    q, k, v = synth.decode_shared(H=4)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    splits = [bi_bench.decode_splits_policy(b, 132) for b in g["batches"]]
+    assert splits == g["splits_by_load"]
+    outs = [bi_bench.decode_attn_splits(qd, kd, vd, 0.125, s) for s in splits]
+    fixed = bi.bi_decode_attn(qd, kd, vd, 0.125)
+    torch.cuda.synchronize()
+    got = [bitwise_equal(o, outs[0]) for o in outs]
+    assert got == g["equal_to_batch1_by_load"]
+    ref = oracle.decode(q, k, v, 0.125)
+    for s, o in zip(splits, outs):
+        assert_parity(to64(o), ref, f"decode {s} splits")
+    # Four equal parts of 2048 are the invariant path's chunks: same bits.
+    assert bitwise_equal(bi_bench.decode_attn_splits(qd, kd, vd, 0.125, 4), fixed)
+
+
+def test_read_probe_runs():
+    buf = torch.zeros(1 << 24, dtype=torch.uint8, device=DEV)
+    sink = torch.empty(65536, dtype=torch.int32, device=DEV)
+    bi_bench.read_probe(buf, sink)
+    torch.cuda.synchronize()
