@@ -72,6 +72,8 @@ int gemm_check(const GemmDesc& d) {
             if (d.sAm * G16_BM > lim || (kc ? d.sBn * G16_BN : d.sBk * G16_BK) > lim)
                 return BI_ERR_UNSUPPORTED;
             if (d.sCm * 128 > lim) return BI_ERR_UNSUPPORTED;   // 32-bit epilogue offsets
+            // The K advance is a 32-bit scalar byte offset.
+            if ((d.K + 64) * (kc ? 1 : d.sBk) * 2 > lim) return BI_ERR_UNSUPPORTED;
         }
         if (d.bias && !aligned(d.bias, 2)) return BI_ERR_LAYOUT;
     } else {

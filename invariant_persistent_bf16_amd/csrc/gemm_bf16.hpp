@@ -19,21 +19,28 @@
 //
 // Hardware mapping.  A 256x256 output tile per workgroup of 4 waves (2x2),
 // each wave owning 128x128 = 4x4 MFMA blocks of 32x32 (256 binary32
-// accumulators per lane, held in AGPRs).  Operand tiles of 64 K-elements are
-// copied HBM -> LDS by buffer_load_dwordx4 ... lds (no staging registers;
-// a lane whose 16 bytes fall outside the operand gets an out-of-range offset
-// and the hardware writes zeros), double buffered (2 x 64 KiB).
-// LDS holds [A stage 0 | A stage 1 | B stage 0 | B stage 1], 32 KiB each.
-//   * A, and a K-contiguous B: LDS rows of 128 bytes (64 K values of one M row
-//     or N column); the eight 16-byte chunks of row r sit at chunk c ^ s(r),
-//     s(r) = (r ^ r>>3) & 7, so the 16-byte fragment reads of neighbouring
-//     lanes fall in distinct banks.  Fragments are ds_read_b128.
+// accumulators per lane, held in AGPRs).  K advances in steps of 32 through a
+// 4-stage LDS ring (4 x (16 + 16) KiB): operand tiles are copied HBM -> LDS by
+// buffer_load_dwordx4 ... lds (no staging registers; a lane whose 16 bytes
+// fall outside the operand gets an out-of-range offset and the hardware
+// writes zeros), three steps ahead of their use, so the copy latency is
+// covered by three steps of MFMA work.  The fragments of step k+1 are read
+// from LDS into a second register set while the 32 MFMAs of step k run
+// (explicit one-to-one interleave), so each step waits only for a copy issued
+// three steps earlier.
+//   * A, and a K-contiguous B: LDS rows of 64 bytes (32 K values of one M row
+//     or N column); the four 16-byte chunks of row r sit at chunk c ^ f(r),
+//     f(r) = (r >> 2) & 3, so 16 lanes reading 16 consecutive rows hit 16
+//     distinct 16-byte bank groups.  Fragments are ds_read_b128.
 //   * an N-contiguous B (a [K, N] weight): LDS rows of 512 bytes (256 N values
 //     of one K row), chunk c of row k at c ^ 4(k & 3).  Fragments are built by
 //     two ds_read_b64_tr_b16 (gfx950's transposing LDS read: within a group of
 //     16 lanes, lane t receives element t%4 of the 8 bytes addressed by lanes
 //     4j + t/4, j = 0..3), giving each lane 8 consecutive K values of its N
 //     column: the MFMA B operand, without a VALU transpose.
+// LDS fragment reads are issued as inline assembly and waited for
+// explicitly at the top of each step, so that the compiler does not order
+// them behind the copies still in flight into other stages.
 // The persistent grid is min(tiles, compute units); workgroup w is renumbered
 // so that the 8 XCDs (which receive workgroups round-robin) each work on a
 // compact 2-D block of tiles, sharing A and B panels in that XCD's L2.
@@ -47,12 +54,15 @@ namespace bi {
 
 constexpr int G16_BM = 256;
 constexpr int G16_BN = 256;
-constexpr int G16_BK = 64;
+constexpr int G16_BK = 32;
 constexpr int G16_THREADS = 256;
 constexpr int G16_GROUP_M = 8;
-constexpr int G16_STAGE_BYTES = G16_BM * G16_BK * 2;   // one operand tile: 32 KiB
-constexpr int G16_LDS_BYTES = 4 * G16_STAGE_BYTES;     // {A, B} x 2 stages: 128 KiB
-constexpr uint32_t G16_OOB = 0x80000000u;              // buffer offset that reads as zero
+constexpr int G16_NSTAGE = 4;
+constexpr int G16_STAGE_BYTES = G16_BM * G16_BK * 2;              // one operand tile: 16 KiB
+constexpr int G16_B_BASE = G16_NSTAGE * G16_STAGE_BYTES;          // B stages after the A stages
+constexpr int G16_LDS_BYTES = 2 * G16_NSTAGE * G16_STAGE_BYTES;   // 128 KiB
+constexpr int G16_DMA_PER_TILE = 8;                               // per wave: 4 for A, 4 for B
+constexpr uint32_t G16_OOB = 0x80000000u;                         // buffer offset that reads as zero
 constexpr int32_t G16_RECORDS = 0x7fffffff;
 
 struct GemmParams {
@@ -71,9 +81,11 @@ struct GemmParams {
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+typedef int v2i32_t __attribute__((ext_vector_type(2)));
 
+__device__ __forceinline__ uint32_t g16_lds_addr(const void* p) {
+    return (uint32_t)(size_t)((const __attribute__((address_space(3))) uint8_t*)p);
+}
 // Buffer descriptor of a wave-uniform base address (kept in SGPRs).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t g16_rsrc(const void* base) {
     const uint64_t v = (uint64_t)base;
@@ -82,23 +94,40 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t g16_rsrc(const void* base) {
     void* u = (void*)(((uint64_t)hi << 32) | lo);
     return __builtin_amdgcn_make_buffer_rsrc(u, (short)0, G16_RECORDS, 0x00020000);
 }
-// 64 lanes x 16 bytes: lane L's bytes [base + voff, +16) land at lds + 16 L.
-__device__ __forceinline__ void g16_dma(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, 0, 0, 0);
+// 64 lanes x 16 bytes: lane L's bytes [base + soff + voff, +16) land at lds + 16 L.
+__device__ __forceinline__ void g16_dma(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, soff, 0, 0);
 }
-__device__ __forceinline__ int g16_swz(int r) { return (r ^ (r >> 3)) & 7; }
-
-// Scheduling hint for one 16-MFMA slice: one MFMA, then one LDS read, NDS
-// times; then the remaining MFMAs (orders instructions only).
-template <int NDS>
-__device__ __forceinline__ void g16_interleave() {
-#pragma unroll
-    for (int q = 0; q < NDS; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+template <int OFF>
+__device__ __forceinline__ u32x4_t g16_read128(uint32_t addr) {
+    u32x4_t r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+template <int OFF>
+__device__ __forceinline__ v2i32_t g16_read_tr(uint32_t addr) {
+    v2i32_t r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+// s_waitcnt with vmcnt <= V and lgkmcnt == 0 (gfx9 encoding; expcnt free).
+template <int V>
+__device__ __forceinline__ void g16_wait_vm_lgkm0() {
+    __builtin_amdgcn_s_waitcnt((V & 15) | (7 << 4) | ((V >> 4) << 14));
+}
+template <int I, int N, typename F>
+__device__ __forceinline__ void g16_static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        g16_static_for<I + 1, N>(f);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 16 - NDS, 0);
 }
+
+// One step's MFMA operands: [kk][im] of A and [kk][in] of B.
+struct G16Frags {
+    u32x4_t a[2][4];
+    u32x4_t b[2][4];
+};
 
 template <bool B_KCONTIG, int OUT_BF16>
 __global__ void __launch_bounds__(G16_THREADS, 1)
@@ -111,32 +140,36 @@ gemm_bf16_persistent(GemmParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int nk = (int)((p.K + G16_BK - 1) / G16_BK);
-    const int K32 = (int)p.K;   // the host bounds K below 2^31
+    const int K32 = (int)p.K;   // the host bounds K below 2^30
 
     const int grid = gridDim.x;
     const int w = blockIdx.x;
     const int wr = (grid % 8 == 0) ? (w % 8) * (grid / 8) + (w / 8) : w;
 
-    // Per-lane LDS fragment bases (see load_frags).
-    const uint8_t* a_fb[4];
-    const uint8_t* b_fb[4];
+    // ---- per-lane LDS fragment addresses (stage 0; stages add 16 KiB each)
+    //  A row r = R0 + 32 im, R0 = 128 wm + lane%32: f(r) = f(R0), so chunk
+    //  (2kk + lane/32) ^ f(r) = x ^ 2kk with x = lane/32 ^ f(R0).
+    //  N-contiguous B: K row kk*16 + 8(g/2) + 4hr + z (z = li/4, k&3 = z),
+    //  chunk (16wn + 4in + y) ^ 4z = 16wn + 4(in ^ z) + y.
+    const uint32_t lds0 = g16_lds_addr(smem);
+    uint32_t a_fb[2], b_fb[4];
     {
         const int R0 = wm * 128 + (lane & 31);
-        const int x = (lane >> 5) ^ g16_swz(R0);
+        const int x = (lane >> 5) ^ ((R0 >> 2) & 3);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) a_fb[j] = smem + R0 * 128 + ((x ^ (2 * j)) << 4);
+        for (int kk = 0; kk < 2; ++kk) a_fb[kk] = lds0 + R0 * 64 + ((x ^ (2 * kk)) << 4);
         if constexpr (B_KCONTIG) {
             const int N0 = wn * 128 + (lane & 31);
-            const int xb = (lane >> 5) ^ g16_swz(N0);
+            const int xb = (lane >> 5) ^ ((N0 >> 2) & 3);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                b_fb[j] = smem + 2 * G16_STAGE_BYTES + N0 * 128 + ((xb ^ (2 * j)) << 4);
+            for (int kk = 0; kk < 2; ++kk) b_fb[kk] = lds0 + G16_B_BASE + N0 * 64 + ((xb ^ (2 * kk)) << 4);
+            b_fb[2] = b_fb[3] = 0;
         } else {
             const int g = lane >> 4, li = lane & 15, z = li >> 2;
             const int y = 2 * (g & 1) + ((li & 3) >> 1);
 #pragma unroll
             for (int in = 0; in < 4; ++in)
-                b_fb[in] = smem + 2 * G16_STAGE_BYTES + (8 * (g >> 1) + z) * 512 +
+                b_fb[in] = lds0 + G16_B_BASE + (8 * (g >> 1) + z) * 512 +
                            (16 * wn + 4 * (in ^ z) + y) * 16 + (li & 1) * 8;
         }
     }
@@ -157,34 +190,87 @@ gemm_bf16_persistent(GemmParams p) {
         if constexpr (B_KCONTIG) Bb = p.B + s1 * p.sB1 + s2 * p.sB2 + n0 * p.sBn;
         else                     Bb = p.B + s1 * p.sB1 + s2 * p.sB2 + n0;
 
-        // ---- DMA source offsets (bytes, relative to the k-tile base; 32-bit,
-        // the host guarantees every in-tile offset is below 2^31).  They are
-        // recomputed in every K step from two per-lane values (cheaper than
-        // keeping sixteen offsets live through the K loop).
-        // A (and K-contiguous B): wave w, copy i covers LDS rows 64w + 8i + lane/8;
-        // the lane writes physical chunk lane&7, i.e. logical chunk
-        // (lane&7) ^ s(row) = (lane&7) ^ (lane/8) ^ i.
-        // N-contiguous B: copy i covers K rows 16w + 2i + lane/32; the lane
-        // writes physical chunk lane&31 of that row, i.e. logical chunk
-        // (lane&31) ^ 4(krow&3) (krow&3 = 2(i&1) + lane/32), clamped to the
-        // last valid 8 columns.
-        const int r_lo = lane >> 3;
-        const int u_lo = (lane & 7) ^ r_lo;
-        const int a_row0 = 64 * wave + r_lo;
-        const int a_rows_left = (int)min<int64_t>(p.M - m0 - a_row0, 1 << 20);
-        const int a_rowstep = (int)p.sAm * 16;                 // bytes per 8 rows
-        const int a_base = a_row0 * (int)p.sAm * 2;
-        int b_rows_left = 0, b_rowstep = 0, b_base = 0, ncl = 0;
-        const int bn_krow0 = 16 * wave + (lane >> 5);
-        if constexpr (B_KCONTIG) {
-            b_rows_left = (int)min<int64_t>(p.N - n0 - a_row0, 1 << 20);
-            b_rowstep = (int)p.sBn * 16;
-            b_base = a_row0 * (int)p.sBn * 2;
-        } else {
-            b_rowstep = (int)p.sBk * 4;                         // bytes per 2 K rows
-            b_base = bn_krow0 * (int)p.sBk * 2;
-            ncl = (int)min<int64_t>(p.N - 8 - n0, 248);
+        // ---- DMA source offsets: per-lane 32-bit byte offsets from the tile's
+        // base, fixed for the tile (out-of-range rows already turned into the
+        // zero-reading offset); each K step adds a uniform byte offset through
+        // the instruction's scalar offset.  The host bounds every offset below 2^31.
+        // A (and K-contiguous B): wave w, copy j covers LDS rows 64w + 16j + lane/4;
+        // the lane writes physical chunk lane&3, i.e. logical chunk
+        // (lane&3) ^ f(row) = (lane&3) ^ ((lane>>4)&3).
+        // N-contiguous B: copy j covers K rows 8w + 2j + lane/32; the lane writes
+        // physical chunk lane&31 of that row, i.e. logical chunk
+        // (lane&31) ^ 4(krow&3), columns clamped to the last valid 8.
+        const int a_u = (lane & 3) ^ ((lane >> 4) & 3);
+        const int a_row0 = 64 * wave + (lane >> 2);
+        uint32_t a_off[4], b_off[4];
+        {
+            const int64_t a_rows_left = p.M - m0 - a_row0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                a_off[j] = a_rows_left > 16 * j ? (uint32_t)(((a_row0 + 16 * j) * (int)p.sAm + a_u * 8) * 2) : G16_OOB;
+            if constexpr (B_KCONTIG) {
+                const int64_t b_rows_left = p.N - n0 - a_row0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    b_off[j] = b_rows_left > 16 * j ? (uint32_t)(((a_row0 + 16 * j) * (int)p.sBn + a_u * 8) * 2) : G16_OOB;
+            } else {
+                const int ncl = (int)min<int64_t>(p.N - 8 - n0, 248);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int krow = 8 * wave + 2 * j + (lane >> 5);
+                    const int col = min(((lane & 31) ^ (4 * (krow & 3))) << 3, ncl);
+                    b_off[j] = (uint32_t)((krow * (int)p.sBk + col) * 2);
+                }
+            }
         }
+        const int a_u8 = a_u * 8;
+        const int bn_krow0 = 8 * wave + (lane >> 5);
+        const __amdgpu_buffer_rsrc_t rsA = g16_rsrc(Ab), rsB = g16_rsrc(Bb);
+        const uint32_t kstepB = B_KCONTIG ? 2u * G16_BK : (uint32_t)(2 * G16_BK * p.sBk);
+
+        // DMA copy j (0..7: 0..3 for A, 4..7 for B) of K tile kt into stage st;
+        // lanes past K read zeros.
+        auto dma = [&](int kt, int st, auto jc) {
+            constexpr int j = decltype(jc)::value;
+            const int kleft = K32 - kt * G16_BK;
+            if constexpr (j < 4) {
+                g16_dma(rsA, smem + st * G16_STAGE_BYTES + (wave * 4 + j) * 1024,
+                        a_u8 < kleft ? a_off[j] : G16_OOB, (uint32_t)kt * (2u * G16_BK));
+            } else if constexpr (B_KCONTIG) {
+                g16_dma(rsB, smem + G16_B_BASE + st * G16_STAGE_BYTES + (wave * 4 + j - 4) * 1024,
+                        a_u8 < kleft ? b_off[j - 4] : G16_OOB, (uint32_t)kt * kstepB);
+            } else {
+                g16_dma(rsB, smem + G16_B_BASE + st * G16_STAGE_BYTES + (wave * 4 + j - 4) * 1024,
+                        bn_krow0 + 2 * (j - 4) < kleft ? b_off[j - 4] : G16_OOB, (uint32_t)kt * kstepB);
+            }
+        };
+        // LDS read r (0..23) of the fragments of stage ST into F:
+        //  0..7 A [kk = r/4][im = r%4]; 8..23 B: K-contiguous [kk][in] (8..15),
+        //  N-contiguous [kk][in] half hr ((r-8) = kk*8 + in*2 + hr).
+        auto lds_read = [&](G16Frags& F, auto stc, auto rc) {
+            constexpr int ST = decltype(stc)::value, r = decltype(rc)::value;
+            if constexpr (r < 8) {
+                constexpr int kk = r / 4, im = r % 4;
+                F.a[kk][im] = g16_read128<ST * G16_STAGE_BYTES + im * 2048>(a_fb[kk]);
+            } else if constexpr (B_KCONTIG) {
+                if constexpr (r < 16) {
+                    constexpr int kk = (r - 8) / 4, in = (r - 8) % 4;
+                    F.b[kk][in] = g16_read128<ST * G16_STAGE_BYTES + in * 2048>(b_fb[kk]);
+                }
+            } else {
+                constexpr int q = r - 8, kk = q / 8, in = (q % 8) / 2, hr = q % 2;
+                const v2i32_t h = g16_read_tr<ST * G16_STAGE_BYTES + kk * 8192 + hr * 2048>(b_fb[in]);
+                F.b[kk][in][2 * hr] = (uint32_t)h[0];
+                F.b[kk][in][2 * hr + 1] = (uint32_t)h[1];
+            }
+        };
+        // Make the fragment registers of F depend on the preceding wait.
+        auto fence_frags = [&](G16Frags& F) {
+            asm volatile("" : "+v"(F.a[0][0]), "+v"(F.a[0][1]), "+v"(F.a[0][2]), "+v"(F.a[0][3]),
+                              "+v"(F.a[1][0]), "+v"(F.a[1][1]), "+v"(F.a[1][2]), "+v"(F.a[1][3]),
+                              "+v"(F.b[0][0]), "+v"(F.b[0][1]), "+v"(F.b[0][2]), "+v"(F.b[0][3]),
+                              "+v"(F.b[1][0]), "+v"(F.b[1][1]), "+v"(F.b[1][2]), "+v"(F.b[1][3]));
+        };
 
         f32x16_t acc[4][4];
 #pragma unroll
@@ -194,125 +280,57 @@ gemm_bf16_persistent(GemmParams p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[im][in][r] = 0.0f;
 
-        auto issue_tile = [&](int kt, int stage) {
-            const int64_t k0 = (int64_t)kt * G16_BK;
-            uint8_t* sA = smem + stage * G16_STAGE_BYTES;
-            uint8_t* sB = smem + (2 + stage) * G16_STAGE_BYTES;
-            const int kleft = min(K32 - (int)k0, G16_BK);   // K values left in this tile
-            int ab = a_base, ul = u_lo;
-            asm volatile("" : "+v"(ab), "+v"(ul));          // recompute offsets in this step
-            const __amdgpu_buffer_rsrc_t ra = g16_rsrc(Ab + k0);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int c8 = (ul ^ i) << 3;
-                const bool ok = a_rows_left > 8 * i && c8 < kleft;
-                g16_dma(ra, sA + (wave * 8 + i) * 1024, ok ? (uint32_t)(ab + i * a_rowstep + c8 * 2) : G16_OOB);
-            }
-            int bb0 = b_base;
-            asm volatile("" : "+v"(bb0));
-            if constexpr (B_KCONTIG) {
-                const __amdgpu_buffer_rsrc_t rb = g16_rsrc(Bb + k0);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int c8 = (ul ^ i) << 3;
-                    const bool ok = b_rows_left > 8 * i && c8 < kleft;
-                    g16_dma(rb, sB + (wave * 8 + i) * 1024, ok ? (uint32_t)(bb0 + i * b_rowstep + c8 * 2) : G16_OOB);
-                }
-            } else {
-                const __amdgpu_buffer_rsrc_t rb = g16_rsrc(Bb + k0 * p.sBk);
-                const int p31 = lane & 31, hi = lane >> 5;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int col = min((p31 ^ (4 * (2 * (i & 1) + hi))) << 3, ncl);
-                    const bool ok = bn_krow0 + 2 * i < kleft;
-                    g16_dma(rb, sB + (wave * 8 + i) * 1024, ok ? (uint32_t)(bb0 + i * b_rowstep + col * 2) : G16_OOB);
-                }
-            }
-        };
+        G16Frags F0, F1;
+        constexpr int NREAD = B_KCONTIG ? 16 : 24;
 
-        // Fragment loads from LDS.  Every address is one of eight per-lane
-        // bases plus a compile-time offset (stage, kk, im / hr):
-        //  A row r = R0 + 32 im, R0 = 128 wm + lane%32: s(r) = s(R0) ^ 4(im&1),
-        //  so chunk (2kk + lane/32) ^ s(r) = x ^ 2(kk ^ 2(im&1)), x = lane/32 ^ s(R0).
-        //  N-contiguous B: K row kk*16 + 8(g/2) + 4hr + z (z = li/4, so k&3 = z),
-        //  chunk (16wn + 4in + y) ^ 4z = 16wn + 4(in ^ z) + y.
-        auto load_a = [&](int stage, int kk, u32x4_t (&af)[4]) {
-#pragma unroll
-            for (int im = 0; im < 4; ++im)
-                af[im] = *(const u32x4_t*)(a_fb[kk ^ (2 * (im & 1))] + stage * G16_STAGE_BYTES + im * 4096);
-        };
-        auto load_b = [&](int stage, int kk, u32x4_t (&bfr)[4]) {
-            if constexpr (B_KCONTIG) {
-#pragma unroll
-                for (int in = 0; in < 4; ++in)
-                    bfr[in] = *(const u32x4_t*)(b_fb[kk ^ (2 * (in & 1))] + stage * G16_STAGE_BYTES + in * 4096);
-            } else {
-#pragma unroll
-                for (int in = 0; in < 4; ++in) {
-                    v4i16_t h[2];
-#pragma unroll
-                    for (int hr = 0; hr < 2; ++hr)
-                        h[hr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_v4i16_t*)(b_fb[in] + stage * G16_STAGE_BYTES + kk * 8192 + hr * 2048));
-                    bfr[in] = __builtin_bit_cast(u32x4_t, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        // One K step kt (stage ST = kt % 4): wait for step kt+1's copy and for
+        // the reads of step kt's fragments, barrier, then 32 MFMAs on
+        // step kt's fragments, each followed by one memory instruction: first
+        // the LDS reads of step kt+1's fragments, then the 8 copies of step
+        // kt+4 into stage ST (its data now lives in registers).  Copies and reads past
+        // the last step are harmless (zeros into an unused stage, reads of an
+        // unused stage) and keep the step a single straight-line block.
+        auto step = [&](int kt, auto stc) {
+            constexpr int ST = decltype(stc)::value;
+            G16Frags& cur = (ST & 1) ? F1 : F0;
+            G16Frags& nxt = (ST & 1) ? F0 : F1;
+            g16_wait_vm_lgkm0<2 * G16_DMA_PER_TILE>();
+            __builtin_amdgcn_s_barrier();
+            fence_frags(cur);
+            __builtin_amdgcn_sched_barrier(0);
+            g16_static_for<0, 32>([&](auto ic) {
+                constexpr int i = decltype(ic)::value;
+                constexpr int kk = i / 16, im = (i / 4) % 4, in = i % 4;
+                acc[im][in] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    as_bf16x8(cur.a[kk][im]), as_bf16x8(cur.b[kk][in]), acc[im][in], 0, 0, 0);
+                if constexpr (i < NREAD) {
+                    lds_read(nxt, std::integral_constant<int, (ST + 1) % 4>{}, std::integral_constant<int, i>{});
+                } else if constexpr (i - NREAD < 8) {
+                    dma(kt + 4, ST, std::integral_constant<int, i - NREAD>{});
                 }
-            }
-        };
-        auto mfma_slice = [&](const u32x4_t (&af)[4], const u32x4_t (&bfr)[4]) {
-#pragma unroll
-            for (int im = 0; im < 4; ++im)
-#pragma unroll
-                for (int in = 0; in < 4; ++in)
-                    acc[im][in] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        as_bf16x8(af[im]), as_bf16x8(bfr[in]), acc[im][in], 0, 0, 0);
-        };
-
-        // K loop.  Per K step of 64: the DMA of the next tile is issued, then
-        // four 16-wide K slices run, the fragments of slice kk+1 being read
-        // from LDS while the 16 MFMAs of slice kk execute.  With an
-        // N-contiguous B all B fragments of the step are read before the DMA
-        // is issued (the transposing reads must not be ordered after an LDS
-        // DMA the compiler cannot tell apart from them).
-        if (nk > 0) {
-            issue_tile(0, 0);
-            __builtin_amdgcn_s_waitcnt(0);     // DMA into LDS complete (vmcnt 0)
-            __syncthreads();
-            for (int kt = 0; kt < nk; ++kt) {
-                const int st = kt & 1;
-                u32x4_t af[2][4];
-                if constexpr (B_KCONTIG) {
-                    u32x4_t bfr[2][4];
-                    load_a(st, 0, af[0]);
-                    load_b(st, 0, bfr[0]);
-                    if (kt + 1 < nk) issue_tile(kt + 1, st ^ 1);
-#pragma unroll
-                    for (int kk = 0; kk < G16_BK / 16; ++kk) {
-                        if (kk + 1 < G16_BK / 16) {
-                            load_a(st, kk + 1, af[(kk + 1) & 1]);
-                            load_b(st, kk + 1, bfr[(kk + 1) & 1]);
-                        }
-                        mfma_slice(af[kk & 1], bfr[kk & 1]);
-                        if (kk + 1 < G16_BK / 16) g16_interleave<8>();
-                    }
-                } else {
-                    u32x4_t bfr[G16_BK / 16][4];
-                    load_a(st, 0, af[0]);
-#pragma unroll
-                    for (int kk = 0; kk < G16_BK / 16; ++kk) load_b(st, kk, bfr[kk]);
-                    if (kt + 1 < nk) issue_tile(kt + 1, st ^ 1);
-#pragma unroll
-                    for (int kk = 0; kk < G16_BK / 16; ++kk) {
-                        if (kk + 1 < G16_BK / 16) load_a(st, kk + 1, af[(kk + 1) & 1]);
-                        mfma_slice(af[kk & 1], bfr[kk]);
-                        if (kk + 1 < G16_BK / 16) g16_interleave<4>();
-                    }
-                }
-                // Keep every MFMA of the step ahead of the wait for the DMA.
                 __builtin_amdgcn_sched_barrier(0);
-                __builtin_amdgcn_s_waitcnt(0);
-                __syncthreads();
-            }
+            });
+        };
+
+        // Prologue: copies of steps 0..3 into stages 0..3, wait for step 0,
+        // read its fragments.
+        g16_static_for<0, 4>([&](auto sc) {
+            g16_static_for<0, 8>([&](auto jc) { dma(decltype(sc)::value, decltype(sc)::value, jc); });
+        });
+        g16_wait_vm_lgkm0<3 * G16_DMA_PER_TILE>();
+        __builtin_amdgcn_s_barrier();
+        g16_static_for<0, NREAD>([&](auto rc) { lds_read(F0, std::integral_constant<int, 0>{}, rc); });
+
+        for (int kt = 0; kt < nk; kt += 4) {
+            step(kt, std::integral_constant<int, 0>{});
+            if (kt + 1 < nk) step(kt + 1, std::integral_constant<int, 1>{});
+            if (kt + 2 < nk) step(kt + 2, std::integral_constant<int, 2>{});
+            if (kt + 3 < nk) step(kt + 3, std::integral_constant<int, 3>{});
         }
+        // Drain every copy (including the ones past the last step) and every
+        // read before the next tile reuses the stages.
+        g16_wait_vm_lgkm0<0>();
+        __builtin_amdgcn_s_barrier();
 
         // ---- epilogue: + bias (binary32, once), round once, store.
         // Addresses: a wave-uniform base (this wave's 128x128 block) plus
