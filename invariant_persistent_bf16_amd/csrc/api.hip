@@ -71,7 +71,7 @@ int gemm_check(const GemmDesc& d) {
             const int64_t lim = (1ll << 30) - 512;
             if (d.sAm * G16_BM > lim || (kc ? d.sBn * G16_BN : d.sBk * G16_BK) > lim)
                 return BI_ERR_UNSUPPORTED;
-            if (d.sCm * 128 > lim) return BI_ERR_UNSUPPORTED;   // 32-bit epilogue offsets
+            if ((d.sCm * 128 + 128) * osz > lim) return BI_ERR_UNSUPPORTED;   // 32-bit epilogue offsets
             // The K advance is a 32-bit scalar byte offset.
             if ((d.K + 64) * (kc ? 1 : d.sBk) * 2 > lim) return BI_ERR_UNSUPPORTED;
         }
@@ -113,13 +113,19 @@ int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override) {
         p.total_tiles = (int)(p.tiles_per_slice * d.G1 * d.G2);
         const int grid = grid_override > 0 ? grid_override : (p.total_tiles < cus ? p.total_tiles : cus);
         const bool kc = d.K == 0 || (d.sBk == 1 && (d.N == 1 || d.sBn % 8 == 0));
+        const int osz = out_bf16 ? 2 : 4;
+        const int vel = 16 / osz;   // elements per 16-byte chunk
+        const bool cvec = aligned(d.C, 16) && d.N % vel == 0 && d.sCm % vel == 0 && d.sC1 % vel == 0 &&
+                          d.sC2 % vel == 0;
+        void (*kern)(GemmParams);
         if (kc) {
-            if (out_bf16) hipLaunchKernelGGL((gemm_bf16_persistent<true, 1>), dim3(grid), dim3(G16_THREADS), 0, st, p);
-            else          hipLaunchKernelGGL((gemm_bf16_persistent<true, 0>), dim3(grid), dim3(G16_THREADS), 0, st, p);
+            if (out_bf16) kern = cvec ? gemm_bf16_persistent<true, 1, true> : gemm_bf16_persistent<true, 1, false>;
+            else          kern = cvec ? gemm_bf16_persistent<true, 0, true> : gemm_bf16_persistent<true, 0, false>;
         } else {
-            if (out_bf16) hipLaunchKernelGGL((gemm_bf16_persistent<false, 1>), dim3(grid), dim3(G16_THREADS), 0, st, p);
-            else          hipLaunchKernelGGL((gemm_bf16_persistent<false, 0>), dim3(grid), dim3(G16_THREADS), 0, st, p);
+            if (out_bf16) kern = cvec ? gemm_bf16_persistent<false, 1, true> : gemm_bf16_persistent<false, 1, false>;
+            else          kern = cvec ? gemm_bf16_persistent<false, 0, true> : gemm_bf16_persistent<false, 0, false>;
         }
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(G16_THREADS), 0, st, p);
     } else {
         GemmF32Params p;
         p.A = (const float*)d.A; p.B = (const float*)d.B; p.bias = (const float*)d.bias; p.C = d.C;

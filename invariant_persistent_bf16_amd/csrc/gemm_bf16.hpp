@@ -60,7 +60,9 @@ constexpr int G16_GROUP_M = 8;
 constexpr int G16_NSTAGE = 4;
 constexpr int G16_STAGE_BYTES = G16_BM * G16_BK * 2;              // one operand tile: 16 KiB
 constexpr int G16_B_BASE = G16_NSTAGE * G16_STAGE_BYTES;          // B stages after the A stages
-constexpr int G16_LDS_BYTES = 2 * G16_NSTAGE * G16_STAGE_BYTES;   // 128 KiB
+constexpr int G16_RING_BYTES = 2 * G16_NSTAGE * G16_STAGE_BYTES;  // 128 KiB
+constexpr int G16_BIAS_BYTES = 2 * G16_BM * 4;                    // one tile's row and column bias, binary32
+constexpr int G16_LDS_BYTES = G16_RING_BYTES + 2 * G16_BIAS_BYTES; // + 4 KiB (double buffered)
 constexpr int G16_DMA_PER_TILE = 8;                               // per wave: 4 for A, 4 for B
 constexpr uint32_t G16_OOB = 0x80000000u;                         // buffer offset that reads as zero
 constexpr int32_t G16_RECORDS = 0x7fffffff;
@@ -82,6 +84,17 @@ struct GemmParams {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef int v2i32_t __attribute__((ext_vector_type(2)));
+typedef uint32_t v2u32_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two binary32 values -> two bfloat16 (low half = a), round to nearest even.
+// gfx950's v_cvt_pk_bf16_f32; it agrees bit for bit with the software rule
+// f32_to_bf16_rne on all 2^32 inputs (NaN quieting and subnormals included).
+__device__ __forceinline__ uint32_t g16_pack_bf16(float a, float b) {
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
 
 __device__ __forceinline__ uint32_t g16_lds_addr(const void* p) {
     return (uint32_t)(size_t)((const __attribute__((address_space(3))) uint8_t*)p);
@@ -115,6 +128,25 @@ template <int V>
 __device__ __forceinline__ void g16_wait_vm_lgkm0() {
     __builtin_amdgcn_s_waitcnt((V & 15) | (7 << 4) | ((V >> 4) << 14));
 }
+// The memory instruction issued after MFMA i of a step: r (0..31) = LDS
+// fragment read r, 32 + j = copy j, -1 = none.  The copies are spread over
+// the step (one after every fourth MFMA) so that the four waves' copies do
+// not reach the texture path in one burst.
+#ifndef G16_SLOT_PATTERN
+#define G16_SLOT_PATTERN 1
+#endif
+template <bool B_KCONTIG>
+constexpr int g16_slot(int i) {
+    const int nread = B_KCONTIG ? 16 : 24;
+    if (G16_SLOT_PATTERN == 0) return i < nread ? i : (i - nread < 8 ? 32 + i - nread : -1);
+    if (G16_SLOT_PATTERN == 1) {
+        if (!B_KCONTIG) return i % 4 == 3 ? 32 + i / 4 : i - i / 4;
+        return i % 4 == 2 ? 32 + i / 4 : (i % 4 < 2 ? 2 * (i / 4) + i % 4 : -1);
+    }
+    if (!B_KCONTIG) return i % 4 == 0 ? 32 + i / 4 : i - i / 4 - 1;
+    return i % 4 == 0 ? 32 + i / 4 : (i % 4 < 3 ? 2 * (i / 4) + i % 4 - 1 : -1);
+}
+
 template <int I, int N, typename F>
 __device__ __forceinline__ void g16_static_for(F&& f) {
     if constexpr (I < N) {
@@ -129,7 +161,9 @@ struct G16Frags {
     u32x4_t b[2][4];
 };
 
-template <bool B_KCONTIG, int OUT_BF16>
+// CVEC: C allows 16-byte row stores (C aligned to 16 bytes; N, sCm, sC1, sC2
+// multiples of 16 bytes' worth of elements); otherwise element stores.
+template <bool B_KCONTIG, int OUT_BF16, bool CVEC>
 __global__ void __launch_bounds__(G16_THREADS, 1)
 gemm_bf16_persistent(GemmParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[G16_LDS_BYTES];
@@ -174,7 +208,8 @@ gemm_bf16_persistent(GemmParams p) {
         }
     }
 
-    for (int tile = wr; tile < p.total_tiles; tile += grid) {
+    int ti = 0;   // tiles done by this workgroup (bias staging buffer parity)
+    for (int tile = wr; tile < p.total_tiles; tile += grid, ++ti) {
         // ---- tile coordinates (scheduling only; no effect on arithmetic)
         const int s = tile / p.tiles_per_slice;
         const int t = tile - s * p.tiles_per_slice;
@@ -272,6 +307,24 @@ gemm_bf16_persistent(GemmParams p) {
                               "+v"(F.b[1][0]), "+v"(F.b[1][1]), "+v"(F.b[1][2]), "+v"(F.b[1][3]));
         };
 
+        // Bias of the tile, staged in LDS as binary32 after the prologue's wait
+        // (the load is older than the copies that wait covers): a row part
+        // [256] and a column part [256].  The part not in use holds -0.0,
+        // which added to any binary32 value x gives x exactly (-0 and NaN
+        // included), so the epilogue adds both parts without branching and
+        // each output still gets exactly one bias addition.  Entries past N
+        // (or M) repeat the last valid one and are never stored.
+        const uint16_t* bb = p.bias ? p.bias + s2 * p.sBias2 : nullptr;
+        float* bias_lds = (float*)(smem + G16_RING_BYTES + (ti & 1) * G16_BIAS_BYTES);
+        float brow_t = -0.0f, bcol_t = -0.0f;
+        if (bb) {
+            const int64_t b0 = p.bias_rows ? m0 : n0;
+            const int64_t nb = (p.bias_rows ? p.M : p.N) - b0;
+            const float b = bf16_to_f32(bb[b0 + min<int64_t>(tid, nb - 1)]);
+            if (p.bias_rows) brow_t = b;
+            else             bcol_t = b;
+        }
+
         f32x16_t acc[4][4];
 #pragma unroll
         for (int im = 0; im < 4; ++im)
@@ -302,11 +355,12 @@ gemm_bf16_persistent(GemmParams p) {
                 constexpr int i = decltype(ic)::value;
                 constexpr int kk = i / 16, im = (i / 4) % 4, in = i % 4;
                 acc[im][in] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    as_bf16x8(cur.a[kk][im]), as_bf16x8(cur.b[kk][in]), acc[im][in], 0, 0, 0);
-                if constexpr (i < NREAD) {
-                    lds_read(nxt, std::integral_constant<int, (ST + 1) % 4>{}, std::integral_constant<int, i>{});
-                } else if constexpr (i - NREAD < 8) {
-                    dma(kt + 4, ST, std::integral_constant<int, i - NREAD>{});
+                    as_bf16x8(cur.b[kk][in]), as_bf16x8(cur.a[kk][im]), acc[im][in], 0, 0, 0);
+                constexpr int slot = g16_slot<B_KCONTIG>(i);
+                if constexpr (slot >= 0 && slot < 32) {
+                    lds_read(nxt, std::integral_constant<int, (ST + 1) % 4>{}, std::integral_constant<int, slot>{});
+                } else if constexpr (slot >= 32) {
+                    dma(kt + 4, ST, std::integral_constant<int, slot - 32>{});
                 }
                 __builtin_amdgcn_sched_barrier(0);
             });
@@ -318,6 +372,8 @@ gemm_bf16_persistent(GemmParams p) {
             g16_static_for<0, 8>([&](auto jc) { dma(decltype(sc)::value, decltype(sc)::value, jc); });
         });
         g16_wait_vm_lgkm0<3 * G16_DMA_PER_TILE>();
+        bias_lds[tid] = brow_t;
+        bias_lds[G16_BM + tid] = bcol_t;
         __builtin_amdgcn_s_barrier();
         g16_static_for<0, NREAD>([&](auto rc) { lds_read(F0, std::integral_constant<int, 0>{}, rc); });
 
@@ -333,48 +389,120 @@ gemm_bf16_persistent(GemmParams p) {
         __builtin_amdgcn_s_barrier();
 
         // ---- epilogue: + bias (binary32, once), round once, store.
-        // Addresses: a wave-uniform base (this wave's 128x128 block) plus
-        // 32-bit lane offsets (the host bounds 128 * sCm below 2^31).
+        // The MFMAs take the B fragment as their first operand, so block
+        // (im, in) holds C^T: lane l, register 4g + j is C[row im*32 + l%32]
+        // [col in*32 + 8g + 4(l/32) + j], four consecutive columns of one row.
+        // CVEC: each wave stages its 128x128 block through its own 32 KiB of
+        // the (now idle) LDS ring, 16-byte chunks of row r at chunk ^ (r mod
+        // chunks per row) so that neither side conflicts, then writes whole
+        // rows with 16-byte stores (one instruction = 8 full 128-byte lines
+        // for bfloat16); binary32 goes in two halves of 64 rows.  Otherwise:
+        // one buffer store per element.
+        // Bounds without branches: the buffer's record count ends at the last
+        // valid element of this wave's block, so rows past M fall outside it,
+        // and a lane whose columns are past N stores at the out-of-range
+        // offset; out-of-range buffer stores are dropped.  The host bounds
+        // 128 * sCm * 4 below 2^31 and, with CVEC, makes N a multiple of the
+        // 16-byte chunk, so a chunk is all valid or all not.
         {
             using OutT = typename std::conditional<OUT_BF16 != 0, uint16_t, float>::type;
+            constexpr int ESZ = (int)sizeof(OutT);
             const int64_t row_w = m0 + wm * 128, col_w = n0 + wn * 128;
             OutT* Cw = (OutT*)p.C + s1 * p.sC1 + s2 * p.sC2 + row_w * p.sCm + col_w;
             const int sCm = (int)p.sCm;
             const int rows_valid = (int)min<int64_t>(p.M - row_w, 128);
             const int cols_valid = (int)min<int64_t>(p.N - col_w, 128);
-            // An opaque copy of the lane id keeps every epilogue value below
-            // from being computed before the K loop (where it would stay live).
-            int lane_e = lane;
-            asm volatile("" : "+v"(lane_e));
-            const int lrow = 4 * (lane_e >> 5), lcol = lane_e & 31;
-            const uint16_t* bb = p.bias ? p.bias + s2 * p.sBias2 : nullptr;
-            const bool brow = bb && p.bias_rows, bcol = bb && !p.bias_rows;
-            float bv[4];
+            if (rows_valid > 0 && cols_valid > 0) {
+                // An opaque copy of the lane id keeps every epilogue value below
+                // from being computed before the K loop (where it would stay live).
+                int lane_e = lane;
+                asm volatile("" : "+v"(lane_e));
+                const int lrow = lane_e & 31, lh = lane_e >> 5, lcol = 4 * lh;
+                const float* brow_w = bias_lds + wm * 128;
+                const float* bcol_w = bias_lds + G16_BM + wn * 128;
+                const uint64_t cv = (uint64_t)Cw;
+                const uint32_t clo = __builtin_amdgcn_readfirstlane((uint32_t)cv);
+                const uint32_t chi = __builtin_amdgcn_readfirstlane((uint32_t)(cv >> 32));
+                const int nrec = __builtin_amdgcn_readfirstlane(((rows_valid - 1) * sCm + cols_valid) * ESZ);
+                const __amdgpu_buffer_rsrc_t rsC = __builtin_amdgcn_make_buffer_rsrc(
+                    (void*)(((uint64_t)chi << 32) | clo), (short)0, nrec, 0x00020000);
+                // The lane's bias values, read before any staging write.
+                float brv[4];
+                f32x4_t bcv[16];
 #pragma unroll
-            for (int in = 0; in < 4; ++in) {
-                const int cc = min(in * 32 + lcol, cols_valid - 1);
-                bv[in] = bcol ? bf16_to_f32(bb[col_w + cc]) : 0.0f;
-            }
+                for (int im = 0; im < 4; ++im) brv[im] = brow_w[im * 32 + lrow];
 #pragma unroll
-            for (int im = 0; im < 4; ++im)
+                for (int q = 0; q < 16; ++q) bcv[q] = *(const f32x4_t*)(bcol_w + (q / 4) * 32 + 8 * (q % 4) + lcol);
+                // Block (im, in), group g with bias added, in binary32.
+                auto value = [&](auto imc, auto qc) {
+                    constexpr int im = decltype(imc)::value;
+                    constexpr int q = decltype(qc)::value, in = q / 4, g = q % 4;
+                    f32x4_t v = {acc[im][in][4 * g], acc[im][in][4 * g + 1],
+                                 acc[im][in][4 * g + 2], acc[im][in][4 * g + 3]};
+                    v += brv[im];
+                    v += bcv[q];
+                    return v;
+                };
+                if constexpr (CVEC) {
+                    constexpr int PASSES = OUT_BF16 ? 1 : 2;
+                    constexpr int ROWB = 128 * ESZ;       // bytes of one staged row
+                    constexpr int NCH = ROWB / 16;        // 16-byte chunks per row
+                    constexpr int RPP = 128 / PASSES;     // rows per pass
+                    constexpr int RPI = 64 / NCH;         // rows per read instruction
+                    uint8_t* stg = smem + wave * (G16_RING_BYTES / 4);
+                    const int t = lane_e % NCH, rsub = lane_e / NCH;
+                    const bool col_ok = t * (16 / ESZ) < cols_valid;
+                    g16_static_for<0, PASSES>([&](auto pc) {
+                        constexpr int ps = decltype(pc)::value;
+                        g16_static_for<0, 4 / PASSES>([&](auto ic) {
+                            constexpr int im = ps * (4 / PASSES) + decltype(ic)::value;
+                            const int r = (im % (4 / PASSES)) * 32 + lrow;
+                            g16_static_for<0, 16>([&](auto qc) {
+                                constexpr int in = decltype(qc)::value / 4, g = decltype(qc)::value % 4;
+                                const f32x4_t v = value(std::integral_constant<int, im>{}, qc);
+                                if constexpr (OUT_BF16) {
+                                    const int c = in * 4 + g;
+                                    const v2u32_t w = {g16_pack_bf16(v[0], v[1]), g16_pack_bf16(v[2], v[3])};
+                                    *(v2u32_t*)(stg + r * ROWB + ((c ^ (r & (NCH - 1))) << 4) + 8 * lh) = w;
+                                } else {
+                                    const int c = in * 8 + 2 * g + lh;
+                                    *(f32x4_t*)(stg + r * ROWB + ((c ^ (r & (NCH - 1))) << 4)) = v;
+                                }
+                            });
+                        });
+                        g16_static_for<0, RPP / RPI>([&](auto jc) {
+                            constexpr int i = decltype(jc)::value;
+                            const int r = i * RPI + rsub;
+                            const u32x4_t d = *(const u32x4_t*)(stg + r * ROWB + ((t ^ (r & (NCH - 1))) << 4));
+                            const uint32_t off = col_ok ? (uint32_t)((ps * RPP + r) * sCm * ESZ + t * 16) : G16_OOB;
+                            __builtin_amdgcn_raw_buffer_store_b128(d, rsC, (int)off, 0, 0);
+                        });
+                    });
+                } else {
+                    g16_static_for<0, 4>([&](auto imc) {
+                        constexpr int im = decltype(imc)::value;
+                        const int vrow = ((im * 32 + lrow) * sCm) * ESZ;
+                        g16_static_for<0, 16>([&](auto qc) {
+                            constexpr int in = decltype(qc)::value / 4, g = decltype(qc)::value % 4;
+                            const f32x4_t v = value(imc, qc);
+                            const int col = in * 32 + 8 * g + lcol;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int rr = im * 32 + 8 * (r >> 2) + (r & 3) + lrow;
-                    if (rr < rows_valid) {
-                        const float rb = brow ? bf16_to_f32(bb[row_w + rr]) : 0.0f;
-#pragma unroll
-                        for (int in = 0; in < 4; ++in) {
-                            const int cc = in * 32 + lcol;
-                            if (cc < cols_valid) {
-                                float v = acc[im][in][r];
-                                if (bb) v += brow ? rb : bv[in];
-                                if constexpr (OUT_BF16) Cw[rr * sCm + cc] = f32_to_bf16_rne(v);
-                                else                    Cw[rr * sCm + cc] = v;
+                            for (int j = 0; j < 4; ++j) {
+                                const uint32_t off = col + j < cols_valid ? (uint32_t)(vrow + (col + j) * ESZ) : G16_OOB;
+                                if constexpr (OUT_BF16)
+                                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)g16_pack_bf16(v[j], 0.0f), rsC,
+                                                                          (int)off, 0, 0);
+                                else
+                                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[j]), rsC, (int)off, 0, 0);
                             }
-                        }
-                    }
+                        });
+                    });
                 }
+            }
         }
+        // Every wave has read its staged block (its stores consumed the reads)
+        // before the next tile's copies overwrite the ring.
+        if constexpr (CVEC) __builtin_amdgcn_s_barrier();
     }
 }
 
