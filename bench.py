@@ -44,7 +44,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target host time of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -49,6 +49,44 @@ def test_bf16_addmm_parity_ragged(M, N, K, b_layout):
     assert_bf16_rounding(C16, ref, "addmm bf16 out")
 
 
+@pytest.mark.parametrize("case", ["n_mod8_is_4", "n_odd_kcontig", "padded_ldc", "misaligned_c"])
+def test_bf16_epilogue_paths_same_bits(case):
+    # The output layout picks the epilogue (16-byte row stores staged through
+    # LDS, or element stores): values must not depend on it, and both must
+    # match the oracle, including the ragged row and column tails.
+    M, N, K = {"n_mod8_is_4": (300, 260, 192), "n_odd_kcontig": (129, 301, 136),
+               "padded_ldc": (200, 256, 72), "misaligned_c": (77, 264, 64)}[case]
+    A = synth.randn((M, K), seed=M, dtype=torch.bfloat16)
+    if N % 8:   # an N-contiguous B needs N % 8 == 0
+        B = synth.randn((N, K), seed=N, dtype=torch.bfloat16, scale=0.1).t()
+    else:
+        B = synth.randn((K, N), seed=N, dtype=torch.bfloat16, scale=0.1)
+    bias = synth.randn((N,), seed=K, dtype=torch.bfloat16, scale=0.1)
+    ref = oracle.mm(A, B, bias)
+    Ad, Bd, bd = A.to(DEV), B.to(DEV), bias.to(DEV)
+    outs = {}
+    for od, tdt in ((bi.BI_F32, torch.float32), (bi.BI_BF16, torch.bfloat16)):
+        plain = bi.bi_addmm(bd, Ad, Bd, out_dtype=od)
+        if case == "padded_ldc":
+            buf = torch.full((M, N + 4), 7.0, dtype=tdt, device=DEV)
+            odd = buf[:, :N]
+        elif case == "misaligned_c":
+            buf = torch.full((M * N + 1,), 7.0, dtype=tdt, device=DEV)
+            odd = buf[1:].view(M, N)
+        else:
+            buf, odd = None, torch.empty((M, N), dtype=tdt, device=DEV)
+        bi.bi_addmm(bd, Ad, Bd, out=odd, out_dtype=od)
+        _sync()
+        assert bitwise_equal(plain, odd), f"{case}: epilogue path changed the bits ({tdt})"
+        if case == "padded_ldc":
+            assert torch.all(buf[:, N:] == 7.0), "padding columns were written"
+        if case == "misaligned_c":
+            assert buf[0].item() == 7.0, "element before C was written"
+        outs[od] = plain
+    assert_parity(to64(outs[bi.BI_F32]), ref, f"epilogue {case}")
+    assert_bf16_is_rne_of(outs[bi.BI_BF16], outs[bi.BI_F32], f"epilogue {case} bf16")
+
+
 def test_bf16_layouts_give_identical_bits():
     # The two B layouts feed the same MFMA chain: results must match bit for bit.
     M, N, K = 130, 264, 320
