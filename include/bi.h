@@ -178,12 +178,17 @@ int bi_decode_chunk_tokens(void);
 /*
  * bi_softmax_rows — P[r, :] = softmax(scale * S[r, :]) for each row, in
  * binary32: max, exponentials, their sum and the division, with one
- * workgroup per row and a reduction tree fixed by `cols` alone (the
+ * wave per row and a reduction tree fixed by `cols` alone (the
  * row-per-program reduction of "Unmasking the True Culprit ...", section
  * "Beyond Matrix Multiplication").  It is the glue between the two batched
  * products of attention (S = Q @ K^T, P = softmax(scale * S), O = P @ V).
- * S: binary32 with row stride ldS (unit column stride), 16-byte aligned with
- * ldS % 4 == 0; P: out_dtype (BI_F32 or BI_BF16) with row stride ldP.
+ * S: binary32 with row stride ldS (unit column stride), 4-byte aligned;
+ * P: out_dtype (BI_F32 or BI_BF16) with row stride ldP, element aligned.
+ * Rows that are 16-byte aligned (8-byte for a bfloat16 P) with cols, ldS
+ * and ldP multiples of 4 are read and written with vector accesses; the
+ * result bits are the same either way.  rows == 0 or cols == 0: nothing.
+ * Errors: BI_ERR_DTYPE, BI_ERR_SHAPE (negative sizes), BI_ERR_NULL,
+ * BI_ERR_LAYOUT (ld < cols with rows > 1, misaligned), BI_ERR_DEVICE.
  */
 int bi_softmax_rows(int64_t rows, int64_t cols, const void* S, int64_t ldS, float scale,
                     void* P, int64_t ldP, int out_dtype, void* stream);

@@ -366,19 +366,23 @@ int bi_softmax_rows(int64_t rows, int64_t cols, const void* S, int64_t ldS, floa
     int rc = device_cu_count(&cus);
     if (rc != BI_OK) return rc;
     hipStream_t st = (hipStream_t)stream;
-    const dim3 grid((unsigned)std::min<int64_t>(rows, 1ll << 30));
+    const dim3 grid((unsigned)std::min<int64_t>((rows + 3) / 4, 1ll << 30));
     const float* s = (const float*)S;
     const bool ob = out_dtype == BI_BF16;
-    if (cols <= 4 * SM_THREADS) {
-        if (ob) hipLaunchKernelGGL((softmax_rows_kernel<4, 1>), grid, dim3(SM_THREADS), 0, st, s, ldS, scale, P, ldP, rows, cols);
-        else    hipLaunchKernelGGL((softmax_rows_kernel<4, 0>), grid, dim3(SM_THREADS), 0, st, s, ldS, scale, P, ldP, rows, cols);
-    } else if (cols <= 16 * SM_THREADS) {
-        if (ob) hipLaunchKernelGGL((softmax_rows_kernel<16, 1>), grid, dim3(SM_THREADS), 0, st, s, ldS, scale, P, ldP, rows, cols);
-        else    hipLaunchKernelGGL((softmax_rows_kernel<16, 0>), grid, dim3(SM_THREADS), 0, st, s, ldS, scale, P, ldP, rows, cols);
-    } else {
-        if (ob) hipLaunchKernelGGL((softmax_rows_kernel<0, 1>), grid, dim3(SM_THREADS), 0, st, s, ldS, scale, P, ldP, rows, cols);
-        else    hipLaunchKernelGGL((softmax_rows_kernel<0, 0>), grid, dim3(SM_THREADS), 0, st, s, ldS, scale, P, ldP, rows, cols);
-    }
+    const bool vec = cols % 4 == 0 && aligned(S, 16) && (rows == 1 || ldS % 4 == 0) &&
+                     aligned(P, ob ? 8 : 16) && (rows == 1 || ldP % 4 == 0);
+    const int nch = cols <= 1024 ? 4 : cols <= 4096 ? 16 : 0;
+    typedef void (*Kern)(const float*, int64_t, float, void*, int64_t, int64_t, int64_t);
+    // [nch 4/16/0][vec][out_bf16]
+    static const Kern kerns[3][2][2] = {
+        {{softmax_rows_kernel<4, false, 0>, softmax_rows_kernel<4, false, 1>},
+         {softmax_rows_kernel<4, true, 0>, softmax_rows_kernel<4, true, 1>}},
+        {{softmax_rows_kernel<16, false, 0>, softmax_rows_kernel<16, false, 1>},
+         {softmax_rows_kernel<16, true, 0>, softmax_rows_kernel<16, true, 1>}},
+        {{softmax_rows_kernel<0, false, 0>, softmax_rows_kernel<0, false, 1>},
+         {softmax_rows_kernel<0, true, 0>, softmax_rows_kernel<0, true, 1>}}};
+    const Kern k = kerns[nch == 4 ? 0 : nch == 16 ? 1 : 2][vec ? 1 : 0][ob ? 1 : 0];
+    hipLaunchKernelGGL(k, grid, dim3(SM_THREADS), 0, st, s, ldS, scale, P, ldP, rows, cols);
     return launch_status();
 }
 

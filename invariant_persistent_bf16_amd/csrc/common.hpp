@@ -28,6 +28,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// Two binary32 values -> two bfloat16 (a in the low half), round to nearest
+// even.  gfx950's v_cvt_pk_bf16_f32; it agrees bit for bit with
+// f32_to_bf16_rne on all 2^32 inputs (NaN quieting and subnormals included).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 // Output element store in the requested dtype (0 = binary32, 1 = bfloat16).
 template <int OUT_BF16>
 __device__ __forceinline__ void store_out(void* base, int64_t idx, float v) {

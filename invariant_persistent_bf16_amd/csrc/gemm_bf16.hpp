@@ -85,16 +85,6 @@ struct GemmParams {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef int v2i32_t __attribute__((ext_vector_type(2)));
 typedef uint32_t v2u32_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-// Two binary32 values -> two bfloat16 (low half = a), round to nearest even.
-// gfx950's v_cvt_pk_bf16_f32; it agrees bit for bit with the software rule
-// f32_to_bf16_rne on all 2^32 inputs (NaN quieting and subnormals included).
-__device__ __forceinline__ uint32_t g16_pack_bf16(float a, float b) {
-    const f32x2_t v = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-}
 
 __device__ __forceinline__ uint32_t g16_lds_addr(const void* p) {
     return (uint32_t)(size_t)((const __attribute__((address_space(3))) uint8_t*)p);
@@ -462,7 +452,7 @@ gemm_bf16_persistent(GemmParams p) {
                                 const f32x4_t v = value(std::integral_constant<int, im>{}, qc);
                                 if constexpr (OUT_BF16) {
                                     const int c = in * 4 + g;
-                                    const v2u32_t w = {g16_pack_bf16(v[0], v[1]), g16_pack_bf16(v[2], v[3])};
+                                    const v2u32_t w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
                                     *(v2u32_t*)(stg + r * ROWB + ((c ^ (r & (NCH - 1))) << 4) + 8 * lh) = w;
                                 } else {
                                     const int c = in * 8 + 2 * g + lh;
@@ -490,7 +480,7 @@ gemm_bf16_persistent(GemmParams p) {
                             for (int j = 0; j < 4; ++j) {
                                 const uint32_t off = col + j < cols_valid ? (uint32_t)(vrow + (col + j) * ESZ) : G16_OOB;
                                 if constexpr (OUT_BF16)
-                                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)g16_pack_bf16(v[j], 0.0f), rsC,
+                                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pack_bf16x2(v[j], 0.0f), rsC,
                                                                           (int)off, 0, 0);
                                 else
                                     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[j]), rsC, (int)off, 0, 0);

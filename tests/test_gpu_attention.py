@@ -48,6 +48,26 @@ def test_stage2_softmax_parity(cols):
     assert torch.equal(P16.view(torch.int16), P32.to(torch.bfloat16).view(torch.int16))
 
 
+@pytest.mark.parametrize("cols", [1020, 1024, 1023, 4096, 4097, 6000])
+def test_stage2_softmax_vector_and_element_paths_same_bits(cols):
+    # Rows read with 16-byte loads (aligned) and with element loads (the same
+    # rows one float off alignment) share one reduction tree: same bits.
+    rows = 40
+    S = synth.randn((rows, cols), seed=cols + 11, scale=3.0)
+    buf = torch.empty(rows * cols + 4, dtype=torch.float32, device=DEV)
+    aligned = buf[:rows * cols].view(rows, cols)
+    shifted = buf[1:1 + rows * cols].view(rows, cols)
+    outs = []
+    for view in (aligned, shifted):
+        view.copy_(S.to(DEV))
+        outs.append((bi.bi_softmax_rows(view, SCALE, out_dtype=bi.BI_F32),
+                     bi.bi_softmax_rows(view, SCALE, out_dtype=bi.BI_BF16)))
+        torch.cuda.synchronize()
+    assert bitwise_equal(outs[0][0], outs[1][0]), "binary32 P depends on the load path"
+    assert bitwise_equal(outs[0][1], outs[1][1]), "bfloat16 P depends on the load path"
+    assert_parity(to64(outs[0][0]), oracle.softmax_rows(S, SCALE), f"softmax cols={cols}")
+
+
 def test_stage2_softmax_strided_rows_and_row_invariance():
     S = synth.randn((300, 1100), seed=5, scale=4.0)
     Sd = S.to(DEV)
