@@ -292,7 +292,28 @@ int bi_conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, const void* x, int64
     const int64_t uchunks = N * groups * g.L * (g.Kp / 8);
     const int wgrid = (int)std::min<int64_t>(cdiv(wchunks, 256), 8 * cus);
     const int ugrid = (int)std::min<int64_t>(cdiv(uchunks, 256), 64 * cus);
-    if (in_dtype == BI_BF16) {
+    const int64_t lim32 = (1ll << 31) - 1;
+    const bool idx32 = N * Cin * H * W <= lim32 && N * groups * g.L * g.Kp <= lim32 && Cout * g.Kp <= lim32 &&
+                       g.OH * sh + (Kh - 1) * dh <= lim32 && g.OW * sw + (Kw - 1) * dw <= lim32 &&
+                       N * Cin <= lim32 / std::max<int64_t>(H * W, 1);
+    if (idx32) {
+        ConvGeom32 g32;
+        g32.N = (int)N; g32.Cin = (int)Cin; g32.H = (int)H; g32.W = (int)W; g32.Cout = (int)Cout;
+        g32.Kh = (int)Kh; g32.Kw = (int)Kw; g32.sh = (int)sh; g32.sw = (int)sw; g32.ph = (int)ph; g32.pw = (int)pw;
+        g32.dh = (int)dh; g32.dw = (int)dw; g32.groups = (int)groups; g32.OW = (int)g.OW; g32.L = (int)g.L;
+        g32.cig = (int)g.cig; g32.Kg = (int)g.Kg; g32.Kp = (int)g.Kp;
+        if (in_dtype == BI_BF16) {
+            hipLaunchKernelGGL((conv_pack_weight32<uint16_t>), dim3(wgrid), dim3(256), 0, st,
+                               (const uint16_t*)w, (uint16_t*)wp, g32);
+            hipLaunchKernelGGL((conv_unfold32<uint16_t>), dim3(ugrid), dim3(256), 0, st,
+                               (const uint16_t*)x, (uint16_t*)u, g32);
+        } else {
+            hipLaunchKernelGGL((conv_pack_weight32<float>), dim3(wgrid), dim3(256), 0, st,
+                               (const float*)w, (float*)wp, g32);
+            hipLaunchKernelGGL((conv_unfold32<float>), dim3(ugrid), dim3(256), 0, st,
+                               (const float*)x, (float*)u, g32);
+        }
+    } else if (in_dtype == BI_BF16) {
         hipLaunchKernelGGL((conv_pack_weight<uint16_t>), dim3(wgrid), dim3(256), 0, st,
                            (const uint16_t*)w, (uint16_t*)wp, g);
         hipLaunchKernelGGL((conv_unfold<uint16_t>), dim3(ugrid), dim3(256), 0, st,

@@ -22,6 +22,80 @@ struct ConvGeom {
     int64_t OH, OW, L, cig, cog, Kg, Kp;
 };
 
+// The same geometry in 32-bit fields, for shapes whose every index (input,
+// unfold and packed-weight elements) is below 2^31.
+struct ConvGeom32 {
+    int N, Cin, H, W, Cout, Kh, Kw, sh, sw, ph, pw, dh, dw, groups;
+    int OW, L, cig, Kg, Kp;
+};
+
+template <typename T>
+__device__ __forceinline__ void store8(T* dst, const T (&v)[8]) {
+    if constexpr (sizeof(T) == 2) {
+        u32x4_t w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (uint32_t)v[2 * e] | ((uint32_t)v[2 * e + 1] << 16);
+        *(u32x4_t*)dst = w;
+    } else {
+        *(f32x4_t*)dst = f32x4_t{v[0], v[1], v[2], v[3]};
+        *(f32x4_t*)(dst + 4) = f32x4_t{v[4], v[5], v[6], v[7]};
+    }
+}
+
+// Weight pack with 32-bit indices: one thread per 8 consecutive k of one co
+// row, one 16-byte (or two) store.
+template <typename T>
+__global__ void __launch_bounds__(256) conv_pack_weight32(const T* __restrict__ w, T* __restrict__ wp, ConvGeom32 g) {
+    const int nchunk = g.Kp / 8;
+    const int total = g.Cout * nchunk;
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
+        const int co = i / nchunk, k0 = (i - co * nchunk) * 8;
+        T v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = k0 + e < g.Kg ? w[co * g.Kg + k0 + e] : (T)0;
+        store8(wp + co * g.Kp + k0, v);
+    }
+}
+
+// Unfold with 32-bit indices: one thread per 8 consecutive k of one (n, g, l)
+// row of U.  k0 is split into (ci, kh, kw) once; the 8 elements then advance
+// kw, kh, ci by carries, with no division per element.
+template <typename T>
+__global__ void __launch_bounds__(256) conv_unfold32(const T* __restrict__ x, T* __restrict__ u, ConvGeom32 g) {
+    const int nchunk = g.Kp / 8;
+    const int total = g.N * g.groups * g.L * nchunk;
+    const int khw = g.Kh * g.Kw;
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
+        int r = i / nchunk;
+        const int k0 = (i - r * nchunk) * 8;
+        const int l = r % g.L;
+        r /= g.L;
+        const int grp = r % g.groups;
+        const int n = r / g.groups;
+        const int oh = l / g.OW, ow = l - oh * g.OW;
+        int ci = k0 / khw;
+        const int rem = k0 - ci * khw;
+        int kh = rem / g.Kw, kw = rem - kh * g.Kw;
+        const int cbase = n * g.Cin + grp * g.cig;
+        const int ih0 = oh * g.sh - g.ph, iw0 = ow * g.sw - g.pw;
+        T v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            T val = (T)0;
+            if (k0 + e < g.Kg) {
+                const int ih = ih0 + kh * g.dh, iw = iw0 + kw * g.dw;
+                if (ih >= 0 && ih < g.H && iw >= 0 && iw < g.W) val = x[((cbase + ci) * g.H + ih) * g.W + iw];
+            }
+            v[e] = val;
+            if (++kw == g.Kw) {
+                kw = 0;
+                if (++kh == g.Kh) { kh = 0; ++ci; }
+            }
+        }
+        store8(u + ((n * g.groups + grp) * g.L + l) * g.Kp + k0, v);
+    }
+}
+
 // One thread per 8 consecutive k of one (co) row.
 template <typename T>
 __global__ void conv_pack_weight(const T* __restrict__ w, T* __restrict__ wp, ConvGeom g) {
