@@ -160,6 +160,44 @@ def softmax_rows(S, scale):
     return out
 
 
+def _rows_in(x):
+    assert x.dtype in (torch.float32, torch.bfloat16) and x.dim() == 2 and x.stride(1) == 1
+    return BF16 if x.dtype == torch.bfloat16 else F32
+
+
+def rms_norm(x, w, eps):
+    """RMSNorm of each row of x [rows, cols] with weight w [cols] (same dtype)."""
+    lib = _load()
+    dt = _rows_in(x)
+    assert w.dtype == x.dtype and w.dim() == 1 and w.shape[0] == x.shape[1]
+    w = w.contiguous()
+    rows, cols = x.shape
+    out, op = _out((rows, cols))
+    lib.oracle_rms_norm(_i64(rows), _i64(cols), _ptr(x), _i64(x.stride(0)), dt, _ptr(w),
+                        ctypes.c_double(eps), op)
+    return out
+
+
+def log_softmax_rows(x):
+    """log-softmax of each row of x [rows, cols]."""
+    lib = _load()
+    dt = _rows_in(x)
+    rows, cols = x.shape
+    out, op = _out((rows, cols))
+    lib.oracle_log_softmax_rows(_i64(rows), _i64(cols), _ptr(x), _i64(x.stride(0)), dt, op)
+    return out
+
+
+def mean_rows(x):
+    """Mean of each row of x [rows, cols]."""
+    lib = _load()
+    dt = _rows_in(x)
+    rows, cols = x.shape
+    out, op = _out((rows,))
+    lib.oracle_mean_rows(_i64(rows), _i64(cols), _ptr(x), _i64(x.stride(0)), dt, op)
+    return out
+
+
 def attention(Q, K, V, scale, p_bf16=False, slices=None):
     """softmax(scale * Q K^T) V per batch element; Q, K, V [G, T, D]."""
     lib = _load()

@@ -239,6 +239,56 @@ void oracle_softmax_rows(int64_t rows, int64_t cols, const float* S, int64_t ldS
     }
 }
 
+/* ------------------------------------------------------------- row ops ----
+ * The row-per-program reductions beside the matmul: [TM] "Beyond Matrix
+ * Multiplication" gives RMSNorm over the last dimension,
+ *   y_j = x_j * (1 / sqrt(mean_i(x_i^2) + eps)) * w_j,
+ * and log-softmax, y_j = (x_j - m) - log(sum_i exp(x_i - m)), m = max_i x_i;
+ * [TM]'s list of overridden operators and [HB] "与 batch 无关：固定切分" (each
+ * normalisation, softmax and mean reduced by one block per row in a fixed
+ * order) add the row mean, y = sum_i x_i / cols.  Row r of x is
+ * x[r * ldx + i] (dtype 0 binary32 or 1 bfloat16); outputs are dense doubles,
+ * cols per row (one per row for the mean). */
+void oracle_rms_norm(int64_t rows, int64_t cols, const void* x, int64_t ldx, int dtype,
+                     const void* w, double eps, double* y) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        double ss = 0.0;
+        for (int64_t i = 0; i < cols; ++i) {
+            const double v = widen(x, dtype, r * ldx + i);
+            ss += v * v;
+        }
+        const double inv = 1.0 / sqrt(ss / (double)cols + eps);
+        for (int64_t j = 0; j < cols; ++j)
+            y[r * cols + j] = widen(x, dtype, r * ldx + j) * inv * widen(w, dtype, j);
+    }
+}
+
+void oracle_log_softmax_rows(int64_t rows, int64_t cols, const void* x, int64_t ldx, int dtype,
+                             double* y) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        double m = -INFINITY;
+        for (int64_t i = 0; i < cols; ++i) {
+            const double v = widen(x, dtype, r * ldx + i);
+            if (v > m) m = v;
+        }
+        double sum = 0.0;
+        for (int64_t i = 0; i < cols; ++i) sum += exp(widen(x, dtype, r * ldx + i) - m);
+        const double ls = log(sum);
+        for (int64_t j = 0; j < cols; ++j) y[r * cols + j] = (widen(x, dtype, r * ldx + j) - m) - ls;
+    }
+}
+
+void oracle_mean_rows(int64_t rows, int64_t cols, const void* x, int64_t ldx, int dtype, double* y) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        double sum = 0.0;
+        for (int64_t i = 0; i < cols; ++i) sum += widen(x, dtype, r * ldx + i);
+        y[r] = sum / (double)cols;
+    }
+}
+
 /* ------------------------------------------------------------ attention ----
  * [KD] Kernel 2: for each flattened batch element g, S = Q[g] @ K[g]^T,
  * P = softmax(scale * S) over each row, O = P @ V[g].  Q, K, V are [G, T, D]
