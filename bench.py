@@ -210,6 +210,7 @@ def main():
     }
 
     out["invariance_cost"] = invariance_cost(Wd, bd, x0, dq, dk, dv, Y)
+    out["row_ops"] = row_ops(X, Y)
 
     del X, Y, Q, Kt, V, Sb, Pb, Ob, dq, dk, dv
     torch.cuda.empty_cache()
@@ -272,6 +273,34 @@ def invariance_cost(Wd, bd, x0, dq, dk, dv, Y):
     sink = torch.empty(65536, dtype=torch.int32, device=dev)
     tp = _time_ms(lambda: bi_bench.read_probe(dk, sink), iters=5)
     res["hbm_read_probe_GBps"] = round(dk.numel() * 2 / (tp * 1e-3) / 1e9, 1)
+    return res
+
+
+def row_ops(X, Y):
+    """Untimed extra (outside the step): the row operations beside the matmul on
+    the LLM shapes of the addmm workload, against the HBM roofline: RMSNorm and
+    mean over X [8192, 4096] bf16, log-softmax over the addmm output
+    [8192, 14336] bf16 -> fp32 (bytes = input + output + weight)."""
+    import torch
+
+    from invariant_persistent_bf16_amd import bi
+
+    M, K, N = ADDMM["M"], ADDMM["K"], ADDMM["N"]
+    w = torch.ones(K, dtype=torch.bfloat16, device=X.device)
+    yr = torch.empty_like(X)
+    ym = torch.empty(M, dtype=torch.float32, device=X.device)
+    ys = torch.empty(M, N, dtype=torch.float32, device=X.device)
+    cases = {
+        "rms_norm_bf16_8192x4096": (lambda: bi.bi_rms_norm(X, w, 1e-6, out=yr), 2 * M * K * 2 + 2 * K),
+        "mean_bf16_8192x4096": (lambda: bi.bi_mean_rows(X, out=ym), 2 * M * K + 4 * M),
+        "log_softmax_bf16_to_fp32_8192x14336": (lambda: bi.bi_log_softmax_rows(Y, out=ys), M * N * (2 + 4)),
+    }
+    res = {}
+    for name, (fn, nbytes) in cases.items():
+        t = _time_ms(fn, iters=50)
+        gbs = nbytes / (t * 1e-3) / 1e9
+        res[name] = {"us": round(t * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    del yr, ym, ys
     return res
 
 

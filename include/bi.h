@@ -193,6 +193,49 @@ int bi_decode_chunk_tokens(void);
 int bi_softmax_rows(int64_t rows, int64_t cols, const void* S, int64_t ldS, float scale,
                     void* P, int64_t ldP, int out_dtype, void* stream);
 
+/*
+ * Row operations beside the matmul, each row reduced by one wave (one
+ * workgroup for rows longer than 4096) in an order fixed by `cols` alone, never
+ * by the number of rows ("Unmasking the True Culprit ...", section "Beyond
+ * Matrix Multiplication"; the deterministic-inference handbook page, section
+ * "与 batch 无关：固定切分").  Row r of x is x[r * ldx + j] (unit column stride),
+ * in_dtype BI_F32 or BI_BF16 (widened exactly); arithmetic in binary32; the
+ * output is out_dtype, bfloat16 by round-to-nearest-even of the binary32
+ * result.  Rows that are 16-byte (binary32) or 8-byte (bfloat16) aligned with
+ * cols and the leading dimensions multiples of 4 use vector accesses; the
+ * bits are the same either way.  rows == 0 (or cols == 0 where allowed): no
+ * work.  Errors before any launch: BI_ERR_DTYPE, BI_ERR_SHAPE (negative
+ * sizes), BI_ERR_NULL, BI_ERR_LAYOUT (ld < cols with rows > 1, an element
+ * misaligned), BI_ERR_UNSUPPORTED (cols > 2^24), BI_ERR_DEVICE.
+ */
+
+/*
+ * bi_rms_norm — y[r, j] = (x[r, j] * s_r) * w[j],
+ * s_r = 1 / sqrt(sum_i x[r, i]^2 / cols + eps) (section "Batch-Invariant
+ * RMSNorm": the squares summed in a fixed order, divided by cols, then the
+ * reciprocal square root; eps >= 0, finite, else BI_ERR_SHAPE).  w: [cols],
+ * in_dtype, 4-byte (binary32) or 2-byte aligned.  y: [rows, cols] with ldy.
+ */
+int bi_rms_norm(int64_t rows, int64_t cols, const void* x, int64_t ldx, const void* w, float eps,
+                void* y, int64_t ldy, int in_dtype, int out_dtype, void* stream);
+
+/*
+ * bi_log_softmax_rows — y[r, j] = (x[r, j] - m_r) - log(sum_i exp(x[r, i] - m_r)),
+ * m_r = max_i x[r, i] (section "Log-Softmax with Fixed Reduction Strategy").
+ * exp is the hardware base-2 exponential of (x - m) * log2(e); log and the
+ * sums are binary32.  y: [rows, cols] with ldy.
+ */
+int bi_log_softmax_rows(int64_t rows, int64_t cols, const void* x, int64_t ldx, void* y, int64_t ldy,
+                        int in_dtype, int out_dtype, void* stream);
+
+/*
+ * bi_mean_rows — y[r] = sum_j x[r, j] / cols (the overridden mean over the
+ * last dimension in the first page's operator list; the handbook's "求均值").
+ * y: [rows] contiguous.  cols == 0 with rows > 0: BI_ERR_SHAPE.
+ */
+int bi_mean_rows(int64_t rows, int64_t cols, const void* x, int64_t ldx, void* y, int in_dtype,
+                 int out_dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

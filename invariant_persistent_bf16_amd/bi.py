@@ -30,6 +30,9 @@ _SIGS = {
     "bi_decode_attn": (_int, [_i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _f32, _vp, _sz, _int, _int, _vp]),
     "bi_decode_chunk_tokens": (_int, []),
     "bi_softmax_rows": (_int, [_i64, _i64, _vp, _i64, _f32, _vp, _i64, _int, _vp]),
+    "bi_rms_norm": (_int, [_i64, _i64, _vp, _i64, _vp, _f32, _vp, _i64, _int, _int, _vp]),
+    "bi_log_softmax_rows": (_int, [_i64, _i64, _vp, _i64, _vp, _i64, _int, _int, _vp]),
+    "bi_mean_rows": (_int, [_i64, _i64, _vp, _i64, _vp, _int, _int, _vp]),
 }
 
 _lib = None
@@ -198,6 +201,35 @@ def bi_softmax_rows(S, scale, out=None, out_dtype=BI_BF16, stream=None):
     _check("bi_softmax_rows", lib().bi_softmax_rows(rows, cols, _p(S), S.stride(0), float(scale), _p(P),
                                                     P.stride(0), _dt(P), _stream(stream)))
     return P
+
+
+def bi_rms_norm(x, w, eps=1e-6, out=None, out_dtype=None, stream=None):
+    """y = RMSNorm(x) * w over the last dimension of x [rows, cols]."""
+    rows, cols = x.shape
+    od = _dt(x) if out_dtype is None else out_dtype
+    y = _out((rows, cols), od, x.device, out)
+    _check("bi_rms_norm", lib().bi_rms_norm(rows, cols, _p(x), x.stride(0), _p(w), float(eps), _p(y),
+                                            y.stride(0), _dt(x), _dt(y), _stream(stream)))
+    return y
+
+
+def bi_log_softmax_rows(x, out=None, out_dtype=None, stream=None):
+    """log-softmax over the last dimension of x [rows, cols]."""
+    rows, cols = x.shape
+    od = _dt(x) if out_dtype is None else out_dtype
+    y = _out((rows, cols), od, x.device, out)
+    _check("bi_log_softmax_rows", lib().bi_log_softmax_rows(rows, cols, _p(x), x.stride(0), _p(y), y.stride(0),
+                                                            _dt(x), _dt(y), _stream(stream)))
+    return y
+
+
+def bi_mean_rows(x, out=None, out_dtype=BI_F32, stream=None):
+    """Mean over the last dimension of x [rows, cols] -> [rows]."""
+    rows, cols = x.shape
+    y = _out((rows,), out_dtype, x.device, out)
+    _check("bi_mean_rows", lib().bi_mean_rows(rows, cols, _p(x), x.stride(0), _p(y), _dt(x), _dt(y),
+                                              _stream(stream)))
+    return y
 
 
 def attention(Q, K, V, scale, S_buf=None, P_buf=None, out=None, stream=None):

@@ -13,6 +13,7 @@
 #include "gemm_bf16.hpp"
 #include "gemm_f32.hpp"
 #include "softmax.hpp"
+#include "rowops.hpp"
 #include "internal.hpp"
 
 namespace bi {
@@ -190,6 +191,49 @@ int conv_geometry(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout, in
     const int64_t ubytes = N * groups * c.L * c.Kp * esz;
     if (g) *g = c;
     if (ws_bytes) *ws_bytes = (size_t)(wbytes + ubytes);
+    return BI_OK;
+}
+
+// Launch a row operation: the lane count and the number of chunks held in
+// registers are chosen by cols alone (so a row's reduction tree never depends
+// on the number of rows); vector access is chosen by alignment and does not
+// change the bits.
+template <int OP>
+int row_op_launch(int64_t rows, int64_t cols, const void* x, int64_t ldx, const void* w, float eps,
+                  void* y, int64_t ldy, int in_dtype, int out_dtype, hipStream_t st) {
+    const bool ib = in_dtype == BI_BF16, ob = out_dtype == BI_BF16;
+    const uintptr_t vin = ib ? 8 : 16, vout = ob ? 8 : 16;
+    const bool vec = cols % 4 == 0 && aligned(x, vin) && (rows == 1 || ldx % 4 == 0) &&
+                     (OP == RO_MEAN || (aligned(y, vout) && (rows == 1 || ldy % 4 == 0))) &&
+                     (OP != RO_RMS || aligned(w, vin));
+    typedef void (*Kern)(const void*, int64_t, const void*, float, void*, int64_t, int64_t, int64_t, int, int);
+    static const Kern kerns[4][2] = {
+        {row_op_kernel<64, 4, false, OP>, row_op_kernel<64, 4, true, OP>},
+        {row_op_kernel<64, 16, false, OP>, row_op_kernel<64, 16, true, OP>},
+        {row_op_kernel<256, 16, false, OP>, row_op_kernel<256, 16, true, OP>},
+        {row_op_kernel<256, 0, false, OP>, row_op_kernel<256, 0, true, OP>}};
+    const int regime = cols <= 1024 ? 0 : cols <= 4096 ? 1 : cols <= 16384 ? 2 : 3;
+    const int64_t rpb = regime < 2 ? 4 : 1;
+    const dim3 grid((unsigned)std::min<int64_t>((rows + rpb - 1) / rpb, 1ll << 30));
+    hipLaunchKernelGGL(kerns[regime][ib ? 1 : 0], grid, dim3(256), 0, st, x, ldx, w, eps, y, ldy, rows, cols,
+                       vec ? 1 : 0, ob ? 1 : 0);
+    return launch_status();
+}
+
+// Shared argument checks of the row operations (y_rows: the output has one
+// row per input row with ldy, else one value per row).
+int row_op_check(int64_t rows, int64_t cols, const void* x, int64_t ldx, void* y, int64_t ldy,
+                 int in_dtype, int out_dtype, bool y_rows) {
+    if ((in_dtype != BI_F32 && in_dtype != BI_BF16) || (out_dtype != BI_F32 && out_dtype != BI_BF16))
+        return BI_ERR_DTYPE;
+    if (rows < 0 || cols < 0) return BI_ERR_SHAPE;
+    if (cols > (1ll << 24) || rows > (1ll << 40)) return BI_ERR_UNSUPPORTED;
+    if (rows == 0 || cols == 0) return BI_OK;
+    if (!x || !y) return BI_ERR_NULL;
+    if (ldx < 0 || (rows > 1 && ldx < cols)) return BI_ERR_LAYOUT;
+    if (y_rows && (ldy < 0 || (rows > 1 && ldy < cols))) return BI_ERR_LAYOUT;
+    if (!aligned(x, in_dtype == BI_BF16 ? 2 : 4) || !aligned(y, out_dtype == BI_BF16 ? 2 : 4))
+        return BI_ERR_LAYOUT;
     return BI_OK;
 }
 
@@ -405,6 +449,41 @@ int bi_softmax_rows(int64_t rows, int64_t cols, const void* S, int64_t ldS, floa
     const Kern k = kerns[nch == 4 ? 0 : nch == 16 ? 1 : 2][vec ? 1 : 0][ob ? 1 : 0];
     hipLaunchKernelGGL(k, grid, dim3(SM_THREADS), 0, st, s, ldS, scale, P, ldP, rows, cols);
     return launch_status();
+}
+
+int bi_rms_norm(int64_t rows, int64_t cols, const void* x, int64_t ldx, const void* w, float eps,
+                void* y, int64_t ldy, int in_dtype, int out_dtype, void* stream) {
+    int rc = row_op_check(rows, cols, x, ldx, y, ldy, in_dtype, out_dtype, true);
+    if (rc != BI_OK || rows == 0 || cols == 0) return rc;
+    if (!w) return BI_ERR_NULL;
+    if (!aligned(w, in_dtype == BI_BF16 ? 2 : 4)) return BI_ERR_LAYOUT;
+    if (!(eps >= 0.0f) || eps == INFINITY) return BI_ERR_SHAPE;
+    int cus = 0;
+    rc = device_cu_count(&cus);
+    if (rc != BI_OK) return rc;
+    return row_op_launch<RO_RMS>(rows, cols, x, ldx, w, eps, y, ldy, in_dtype, out_dtype, (hipStream_t)stream);
+}
+
+int bi_log_softmax_rows(int64_t rows, int64_t cols, const void* x, int64_t ldx, void* y, int64_t ldy,
+                        int in_dtype, int out_dtype, void* stream) {
+    int rc = row_op_check(rows, cols, x, ldx, y, ldy, in_dtype, out_dtype, true);
+    if (rc != BI_OK || rows == 0 || cols == 0) return rc;
+    int cus = 0;
+    rc = device_cu_count(&cus);
+    if (rc != BI_OK) return rc;
+    return row_op_launch<RO_LOGSOFTMAX>(rows, cols, x, ldx, nullptr, 0.0f, y, ldy, in_dtype, out_dtype,
+                                        (hipStream_t)stream);
+}
+
+int bi_mean_rows(int64_t rows, int64_t cols, const void* x, int64_t ldx, void* y, int in_dtype, int out_dtype,
+                 void* stream) {
+    if (rows > 0 && cols == 0) return BI_ERR_SHAPE;   // the mean of no values is undefined
+    int rc = row_op_check(rows, cols, x, ldx, y, 1, in_dtype, out_dtype, false);
+    if (rc != BI_OK || rows == 0) return rc;
+    int cus = 0;
+    rc = device_cu_count(&cus);
+    if (rc != BI_OK) return rc;
+    return row_op_launch<RO_MEAN>(rows, cols, x, ldx, nullptr, 0.0f, y, 1, in_dtype, out_dtype, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -61,6 +61,9 @@ def bi():
     L.bi_decode_attn.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, ctypes.c_float, vp,
                                  ctypes.c_size_t, ctypes.c_int, ctypes.c_int, vp]
     L.bi_softmax_rows.argtypes = [i64, i64, vp, i64, ctypes.c_float, vp, i64, ctypes.c_int, vp]
+    L.bi_rms_norm.argtypes = [i64, i64, vp, i64, vp, ctypes.c_float, vp, i64, ctypes.c_int, ctypes.c_int, vp]
+    L.bi_log_softmax_rows.argtypes = [i64, i64, vp, i64, vp, i64, ctypes.c_int, ctypes.c_int, vp]
+    L.bi_mean_rows.argtypes = [i64, i64, vp, i64, vp, ctypes.c_int, ctypes.c_int, vp]
     L.bi_status_string.restype = ctypes.c_char_p
     return L
 
@@ -156,3 +159,23 @@ def test_softmax_validation(bi):
     assert bi.bi_softmax_rows(4, 8, None, 8, 1.0, P, 8, BF16, None) == NULL
     assert bi.bi_softmax_rows(4, 8, P, 4, 1.0, P, 8, BF16, None) == LAYOUT
     assert bi.bi_softmax_rows(0, 8, P, 8, 1.0, P, 8, BF16, None) == OK
+
+
+def test_row_ops_validation(bi):
+    rms = lambda rows=4, cols=8, x=P, ldx=8, w=P, eps=1e-6, y=P, ldy=8, i=BF16, o=BF16: \
+        bi.bi_rms_norm(rows, cols, x, ldx, w, eps, y, ldy, i, o, None)
+    assert rms(i=3) == DTYPE and rms(o=9) == DTYPE
+    assert rms(rows=-1) == SHAPE and rms(cols=-2) == SHAPE
+    assert rms(x=None) == NULL and rms(w=None) == NULL and rms(y=None) == NULL
+    assert rms(ldx=4) == LAYOUT and rms(ldy=7) == LAYOUT and rms(x=P + 1) == LAYOUT
+    assert rms(w=P + 1) == LAYOUT
+    assert rms(eps=-1.0) == SHAPE and rms(eps=float("nan")) == SHAPE
+    assert rms(cols=(1 << 24) + 1, ldx=(1 << 24) + 1, ldy=(1 << 24) + 1) == UNSUP
+    assert rms(rows=0) == OK and rms(cols=0) == OK
+    lsm = lambda rows=4, cols=8, x=P, ldx=8, y=P, ldy=8, i=F32, o=F32: \
+        bi.bi_log_softmax_rows(rows, cols, x, ldx, y, ldy, i, o, None)
+    assert lsm(i=2) == DTYPE and lsm(rows=-3) == SHAPE and lsm(y=None) == NULL
+    assert lsm(ldx=7) == LAYOUT and lsm(y=P + 2) == LAYOUT and lsm(rows=0) == OK
+    mean = lambda rows=4, cols=8, x=P, ldx=8, y=P, i=BF16, o=F32: bi.bi_mean_rows(rows, cols, x, ldx, y, i, o, None)
+    assert mean(o=5) == DTYPE and mean(cols=0) == SHAPE and mean(x=None) == NULL
+    assert mean(ldx=3) == LAYOUT and mean(rows=0) == OK and mean(rows=0, cols=0) == OK
