@@ -188,7 +188,8 @@ int bi_decode_chunk_tokens(void);
  * and ldP multiples of 4 are read and written with vector accesses; the
  * result bits are the same either way.  rows == 0 or cols == 0: nothing.
  * Errors: BI_ERR_DTYPE, BI_ERR_SHAPE (negative sizes), BI_ERR_NULL,
- * BI_ERR_LAYOUT (ld < cols with rows > 1, misaligned), BI_ERR_DEVICE.
+ * BI_ERR_LAYOUT (ld < cols with rows > 1, misaligned), BI_ERR_UNSUPPORTED
+ * (cols > 2^24), BI_ERR_DEVICE.
  */
 int bi_softmax_rows(int64_t rows, int64_t cols, const void* S, int64_t ldS, float scale,
                     void* P, int64_t ldP, int out_dtype, void* stream);

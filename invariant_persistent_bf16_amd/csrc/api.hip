@@ -206,17 +206,22 @@ int row_op_launch(int64_t rows, int64_t cols, const void* x, int64_t ldx, const 
     const bool vec = cols % 4 == 0 && aligned(x, vin) && (rows == 1 || ldx % 4 == 0) &&
                      (OP == RO_MEAN || (aligned(y, vout) && (rows == 1 || ldy % 4 == 0))) &&
                      (OP != RO_RMS || aligned(w, vin));
-    typedef void (*Kern)(const void*, int64_t, const void*, float, void*, int64_t, int64_t, int64_t, int, int);
-    static const Kern kerns[4][2] = {
-        {row_op_kernel<64, 4, false, OP>, row_op_kernel<64, 4, true, OP>},
-        {row_op_kernel<64, 16, false, OP>, row_op_kernel<64, 16, true, OP>},
-        {row_op_kernel<256, 16, false, OP>, row_op_kernel<256, 16, true, OP>},
-        {row_op_kernel<256, 0, false, OP>, row_op_kernel<256, 0, true, OP>}};
+    typedef void (*Kern)(const void*, int64_t, const void*, float, void*, int64_t, int64_t, int, int);
+    // [regime][input bfloat16][vector]
+    static const Kern kerns[4][2][2] = {
+        {{row_op_kernel<64, 4, false, OP, false>, row_op_kernel<64, 4, false, OP, true>},
+         {row_op_kernel<64, 4, true, OP, false>, row_op_kernel<64, 4, true, OP, true>}},
+        {{row_op_kernel<64, 16, false, OP, false>, row_op_kernel<64, 16, false, OP, true>},
+         {row_op_kernel<64, 16, true, OP, false>, row_op_kernel<64, 16, true, OP, true>}},
+        {{row_op_kernel<256, 16, false, OP, false>, row_op_kernel<256, 16, false, OP, true>},
+         {row_op_kernel<256, 16, true, OP, false>, row_op_kernel<256, 16, true, OP, true>}},
+        {{row_op_kernel<256, 0, false, OP, false>, row_op_kernel<256, 0, false, OP, true>},
+         {row_op_kernel<256, 0, true, OP, false>, row_op_kernel<256, 0, true, OP, true>}}};
     const int regime = cols <= 1024 ? 0 : cols <= 4096 ? 1 : cols <= 16384 ? 2 : 3;
     const int64_t rpb = regime < 2 ? 4 : 1;
     const dim3 grid((unsigned)std::min<int64_t>((rows + rpb - 1) / rpb, 1ll << 30));
-    hipLaunchKernelGGL(kerns[regime][ib ? 1 : 0], grid, dim3(256), 0, st, x, ldx, w, eps, y, ldy, rows, cols,
-                       vec ? 1 : 0, ob ? 1 : 0);
+    hipLaunchKernelGGL(kerns[regime][ib ? 1 : 0][vec ? 1 : 0], grid, dim3(256), 0, st, x, ldx, w, eps, y, ldy, rows,
+                       (int)cols, ob ? 1 : 0);
     return launch_status();
 }
 
@@ -423,6 +428,7 @@ int bi_softmax_rows(int64_t rows, int64_t cols, const void* S, int64_t ldS, floa
                     int64_t ldP, int out_dtype, void* stream) {
     if (out_dtype != BI_F32 && out_dtype != BI_BF16) return BI_ERR_DTYPE;
     if (rows < 0 || cols < 0) return BI_ERR_SHAPE;
+    if (cols > (1ll << 24)) return BI_ERR_UNSUPPORTED;
     if (rows == 0 || cols == 0) return BI_OK;
     if (!S || !P) return BI_ERR_NULL;
     if ((rows > 1 && (ldS < cols || ldP < cols)) || ldS < 0 || ldP < 0) return BI_ERR_LAYOUT;
@@ -437,7 +443,7 @@ int bi_softmax_rows(int64_t rows, int64_t cols, const void* S, int64_t ldS, floa
     const bool vec = cols % 4 == 0 && aligned(S, 16) && (rows == 1 || ldS % 4 == 0) &&
                      aligned(P, ob ? 8 : 16) && (rows == 1 || ldP % 4 == 0);
     const int nch = cols <= 1024 ? 4 : cols <= 4096 ? 16 : 0;
-    typedef void (*Kern)(const float*, int64_t, float, void*, int64_t, int64_t, int64_t);
+    typedef void (*Kern)(const float*, int64_t, float, void*, int64_t, int64_t, int);
     // [nch 4/16/0][vec][out_bf16]
     static const Kern kerns[3][2][2] = {
         {{softmax_rows_kernel<4, false, 0>, softmax_rows_kernel<4, false, 1>},
@@ -447,7 +453,7 @@ int bi_softmax_rows(int64_t rows, int64_t cols, const void* S, int64_t ldS, floa
         {{softmax_rows_kernel<0, false, 0>, softmax_rows_kernel<0, false, 1>},
          {softmax_rows_kernel<0, true, 0>, softmax_rows_kernel<0, true, 1>}}};
     const Kern k = kerns[nch == 4 ? 0 : nch == 16 ? 1 : 2][vec ? 1 : 0][ob ? 1 : 0];
-    hipLaunchKernelGGL(k, grid, dim3(SM_THREADS), 0, st, s, ldS, scale, P, ldP, rows, cols);
+    hipLaunchKernelGGL(k, grid, dim3(SM_THREADS), 0, st, s, ldS, scale, P, ldP, rows, (int)cols);
     return launch_status();
 }
 

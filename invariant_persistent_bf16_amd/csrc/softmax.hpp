@@ -30,6 +30,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "rowio.hpp"
 
 namespace bi {
 
@@ -57,60 +58,30 @@ __device__ __forceinline__ float wave_max(float x) {
 
 // NCH > 0: the lane keeps its NCH chunks (4 * NCH values) in registers, so
 // cols <= 256 * NCH; NCH == 0: any cols, the row is re-read for each pass.
-// VEC: S rows and P rows allow 16-byte (S, binary32 P) or 8-byte (bfloat16 P)
-// accesses and cols % 4 == 0.
+// VEC: rows allow 16-byte reads of S and 16-byte (binary32 P) or 8-byte
+// (bfloat16 P) writes, and cols % 4 == 0.  Accesses go through rowio.hpp
+// (no access in a branch; positions past cols read as -inf).
 template <int NCH, bool VEC, int OUT_BF16>
 __global__ void __launch_bounds__(SM_THREADS)
 softmax_rows_kernel(const float* __restrict__ S, int64_t ldS, float scale,
-                    void* __restrict__ P, int64_t ldP, int64_t rows, int64_t cols) {
+                    void* __restrict__ P, int64_t ldP, int64_t rows, int cols) {
     const int lane = threadIdx.x & 63;
-    const int64_t nchunk = (cols + 3) / 4;
+    const int nchunk = (cols + 3) / 4;
+    constexpr int OSZ = OUT_BF16 ? 2 : 4;
     for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows; row += (int64_t)gridDim.x * 4) {
-        const float* s = S + row * ldS;
-        // Chunk c of the row, scaled, with -inf past cols.
-        auto load = [&](int64_t c) {
-            f32x4_t x;
-            if constexpr (VEC) {
-                if (c < nchunk) x = *(const f32x4_t*)(s + 4 * c) * scale;
-                else            x = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int64_t j = 4 * c + e;
-                    x[e] = j < cols ? scale * s[j] : -INFINITY;
-                }
-            }
-            return x;
-        };
-        auto store = [&](int64_t c, f32x4_t y) {
-            if constexpr (VEC) {
-                if (c < nchunk) {
-                    if constexpr (OUT_BF16) {
-                        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-                        const u32x2_t w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-                        *(u32x2_t*)((uint16_t*)P + row * ldP + 4 * c) = w;
-                    } else {
-                        *(f32x4_t*)((float*)P + row * ldP + 4 * c) = y;
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int64_t j = 4 * c + e;
-                    if (j < cols) store_out<OUT_BF16>(P, row * ldP + j, y[e]);
-                }
-            }
-        };
+        const __amdgpu_buffer_rsrc_t rs = row_rsrc(S + row * ldS, (int64_t)cols * 4);
+        const __amdgpu_buffer_rsrc_t rp = row_rsrc((const uint8_t*)P + row * ldP * OSZ, (int64_t)cols * OSZ);
+        auto load = [&](int c) { return row_load<false, VEC, true>(rs, c, cols, -INFINITY, scale); };
 
         float m = -INFINITY;
         if constexpr (NCH > 0) {
             f32x4_t x[NCH];
 #pragma unroll
-            for (int v = 0; v < NCH; ++v) {
-                x[v] = load(lane + 64 * v);
+            for (int v = 0; v < NCH; ++v) x[v] = load(lane + 64 * v);
+#pragma unroll
+            for (int v = 0; v < NCH; ++v)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) m = fmaxf(m, x[v][e]);
-            }
             m = wave_max(m);
             float sum = 0.0f;
 #pragma unroll
@@ -127,29 +98,29 @@ softmax_rows_kernel(const float* __restrict__ S, int64_t ldS, float scale,
                 f32x4_t y;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) y[e] = sm_div(x[v][e], sum, rsum);
-                store(lane + 64 * v, y);
+                row_store<VEC>(rp, lane + 64 * v, y, OUT_BF16 != 0);
             }
         } else {
-            for (int64_t c = lane; c < nchunk; c += 64) {
+            for (int c = lane; c < nchunk; c += 64) {
                 const f32x4_t x = load(c);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) m = fmaxf(m, x[e]);
             }
             m = wave_max(m);
             float sum = 0.0f;
-            for (int64_t c = lane; c < nchunk; c += 64) {
+            for (int c = lane; c < nchunk; c += 64) {
                 const f32x4_t x = load(c);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) sum += sm_exp(x[e] - m);
             }
             sum = wave_sum(sum);
             const float rsum = 1.0f / sum;
-            for (int64_t c = lane; c < nchunk; c += 64) {
+            for (int c = lane; c < nchunk; c += 64) {
                 const f32x4_t x = load(c);
                 f32x4_t y;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) y[e] = sm_div(sm_exp(x[e] - m), sum, rsum);
-                store(c, y);
+                row_store<VEC>(rp, c, y, OUT_BF16 != 0);
             }
         }
     }
