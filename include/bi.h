@@ -165,6 +165,8 @@ int bi_conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, const void* x,
  * ws: at least bi_decode_attn_workspace_bytes(B, H, S, D) bytes, 16-byte
  * aligned; receives the per-chunk triples [B, H, nchunk, 2 + D] (binary32:
  * m, l, o[D]) and is owned by the caller.
+ * BI_ERR_UNSUPPORTED when (S + 2048) * D * 2 >= 2^31 (one (b, h) row of K or
+ * V is addressed with 32-bit byte offsets), or D is not 64 or 128.
  */
 size_t bi_decode_attn_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t D);
 int bi_decode_attn(int64_t B, int64_t H, int64_t S, int64_t D,

@@ -402,6 +402,8 @@ int bi_decode_attn(int64_t B, int64_t H, int64_t S, int64_t D, const void* q, co
     if (ws_bytes < bi_decode_attn_workspace_bytes(B, H, S, D) || !aligned(ws, 16))
         return BI_ERR_WORKSPACE;
     if (B * H * nchunk > (1ll << 31) - 1 || B * H * D > (1ll << 40)) return BI_ERR_UNSUPPORTED;
+    // Per-(b, h) K and V byte offsets (up to one chunk past S) are 32-bit.
+    if ((S + DEC_CHUNK) * D * 2 >= (1ll << 31)) return BI_ERR_UNSUPPORTED;
     int cus = 0;
     int rc = device_cu_count(&cus);
     if (rc != BI_OK) return rc;

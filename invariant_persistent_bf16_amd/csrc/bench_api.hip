@@ -178,6 +178,7 @@ int bi_bench_decode_attn_splits(int64_t B, int64_t H, int64_t S, int64_t D, cons
     const int64_t L = S / splits;
     if (L % 8) return BI_ERR_UNSUPPORTED;
     if (L > DEC_CHUNK && L % DEC_CHUNK) return BI_ERR_UNSUPPORTED;
+    if ((S + DEC_CHUNK) * D * 2 >= (1ll << 31)) return BI_ERR_UNSUPPORTED;
     if (B == 0 || H == 0) return BI_OK;
     if (!q || !k || !v || !out) return BI_ERR_NULL;
     if (!ws || ws_bytes < bi_bench_decode_attn_splits_workspace_bytes(B, H, S, D, splits) ||

@@ -25,6 +25,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "rowio.hpp"
 
 namespace bi {
 
@@ -44,7 +45,11 @@ decode_chunk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     constexpr int LPT = D / 8;               // lanes per token
     constexpr int TPI = 64 / LPT;            // tokens per wave-wide load
     constexpr int NI = DEC_TOK_PER_WAVE / TPI;
-    constexpr int BATCH = 8;                 // loads in flight per lane per step
+    // Loads in flight per lane: all of the wave's K (or V) loads for D = 64,
+    // half for D = 128 (register budget); one workgroup per CU then keeps
+    // 256 KiB of K or V in flight, which hides HBM latency without a second
+    // workgroup (whose extra concurrent streams measured slower).
+    constexpr int BATCH = NI < 32 ? NI : 32;
     static_assert(NI % BATCH == 0, "tile shape");
 
     __shared__ float red_m[DEC_WAVES];
@@ -62,8 +67,13 @@ decode_chunk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     const int64_t t0 = w0 + tg;
     const int64_t t_end = min(S, w0 + tw);
 
-    const uint16_t* kb = k + (bh * S) * D + sub * 8;
-    const uint16_t* vb = v + (bh * S) * D + sub * 8;
+    // K and V rows of this (b, h) as buffers ending at token S: loads need no
+    // branch (tokens past S read zero; their scores are masked below) and all
+    // of a batch's loads are in flight together.  The host bounds S*D*2 below
+    // 2^31.  Loads are non-temporal (K and V are read once).
+    const __amdgpu_buffer_rsrc_t rk = row_rsrc(k + (bh * S) * D, S * D * 2);
+    const __amdgpu_buffer_rsrc_t rv = row_rsrc(v + (bh * S) * D, S * D * 2);
+    const int lane_off = sub * 16;
 
     float qf[8];
     {
@@ -83,9 +93,8 @@ decode_chunk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         u32x4_t kr[BATCH];
 #pragma unroll
         for (int b = 0; b < BATCH; ++b) {
-            const int64_t t = t0 + (int64_t)(i0 + b) * TPI;
-            kr[b] = t < t_end ? __builtin_nontemporal_load((const u32x4_t*)(kb + t * D))
-                              : u32x4_t{0u, 0u, 0u, 0u};
+            const int t = (int)(t0 + (int64_t)(i0 + b) * TPI);
+            kr[b] = __builtin_amdgcn_raw_buffer_load_b128(rk, t * (D * 2) + lane_off, 0, 2);
         }
 #pragma unroll
         for (int b = 0; b < BATCH; ++b) {
@@ -101,6 +110,14 @@ decode_chunk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             sc[i0 + b] = t < t_end ? acc * scale : -INFINITY;
             m = fmaxf(m, sc[i0 + b]);
         }
+    }
+    // The first batch of V loads is issued before the chunk maximum (V does
+    // not depend on it), so its latency overlaps the cross-wave reduction.
+    u32x4_t vr0[BATCH];
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+        const int t = (int)(t0 + (int64_t)b * TPI);
+        vr0[b] = __builtin_amdgcn_raw_buffer_load_b128(rv, t * (D * 2) + lane_off, 0, 2);
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
@@ -120,9 +137,8 @@ decode_chunk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         u32x4_t vr[BATCH];
 #pragma unroll
         for (int b = 0; b < BATCH; ++b) {
-            const int64_t t = t0 + (int64_t)(i0 + b) * TPI;
-            vr[b] = t < t_end ? __builtin_nontemporal_load((const u32x4_t*)(vb + t * D))
-                              : u32x4_t{0u, 0u, 0u, 0u};
+            const int t = (int)(t0 + (int64_t)(i0 + b) * TPI);
+            vr[b] = i0 == 0 ? vr0[b] : __builtin_amdgcn_raw_buffer_load_b128(rv, t * (D * 2) + lane_off, 0, 2);
         }
 #pragma unroll
         for (int b = 0; b < BATCH; ++b) {
