@@ -223,6 +223,22 @@ def decode(q, k, v, scale, reqs=None):
     return out
 
 
+def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale):
+    """Decode over a paged cache: q [B,H,D], caches [num_pages,H,P,D],
+    block_table [B, max_pages] int32, seq_lens [B] int32."""
+    lib = _load()
+    q, k_cache, v_cache = q.contiguous(), k_cache.contiguous(), v_cache.contiguous()
+    bt = block_table.contiguous().to(torch.int32)
+    sl = seq_lens.contiguous().to(torch.int32)
+    B, H, D = q.shape
+    P = k_cache.shape[2]
+    out, op = _out((B, H, D))
+    lib.oracle_decode_paged(_i64(B), _i64(H), _i64(D), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(bt),
+                            _i64(bt.shape[1]), _ptr(sl), _i64(P), ctypes.c_double(scale),
+                            ctypes.c_int(_dt(q)), op)
+    return out
+
+
 def decode_chunked(q, k, v, scale, chunk=2048, reqs=None, triples=False):
     """Fixed-length-chunk flash decoding with an ascending-order LSE merge."""
     lib = _load()

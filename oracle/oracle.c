@@ -364,6 +364,45 @@ void oracle_decode(int64_t B, int64_t H, int64_t S, int64_t D, const void* q,
     }
 }
 
+/* Decode over a paged KV cache with per-request lengths: the same unsplit
+ * attention as oracle_decode for request b over its first seq_lens[b] tokens,
+ * token t of request b read from page block_table[b * max_pages + t / P] at
+ * slot t % P of the cache laid out [num_pages, H, P, D] (the storage the
+ * handbook's serving frameworks page their KV cache in; [HB] "框架里的开关" and
+ * "与 batch 无关：固定切分": prefix cache and chunked prefill must not change a
+ * request's bits).  out [B, H, D]; a request with seq_lens[b] == 0 gets NaN. */
+void oracle_decode_paged(int64_t B, int64_t H, int64_t D, const void* q, const void* kc,
+                         const void* vc, const int32_t* block_table, int64_t max_pages,
+                         const int32_t* seq_lens, int64_t P, double scale, int dtype, double* out) {
+    #pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t h = 0; h < H; ++h) {
+            const int64_t S = seq_lens[b];
+            double* o = out + (b * H + h) * D;
+            double* sc = (double*)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+            double m = -INFINITY;
+            for (int64_t t = 0; t < S; ++t) {
+                const int64_t row = ((int64_t)block_table[b * max_pages + t / P] * H + h) * P + t % P;
+                double acc = 0.0;
+                for (int64_t d = 0; d < D; ++d)
+                    acc += widen(q, dtype, (b * H + h) * D + d) * widen(kc, dtype, row * D + d);
+                sc[t] = scale * acc;
+                if (sc[t] > m) m = sc[t];
+            }
+            double den = 0.0;
+            for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+            for (int64_t t = 0; t < S; ++t) {
+                const int64_t row = ((int64_t)block_table[b * max_pages + t / P] * H + h) * P + t % P;
+                const double p = exp(sc[t] - m);
+                den += p;
+                for (int64_t d = 0; d < D; ++d) o[d] += p * widen(vc, dtype, row * D + d);
+            }
+            for (int64_t d = 0; d < D; ++d) o[d] = S > 0 ? o[d] / den : NAN;
+            free(sc);
+        }
+    }
+}
+
 /* [HB] flash-decoding with fixed-length chunks.  The KV sequence is cut into
  * consecutive chunks of `chunk` tokens from position 0 (the last may be
  * shorter).  Each chunk c keeps the triple

@@ -22,6 +22,11 @@ Shapes and distributions follow the pages' workloads:
          bias 0.02*randn [1152]
   attn   Q, K, V randn [B, 8, 1024, 128] flattened to [8B, 1024, 128]
   decode q randn [B, 32, 64], K, V randn [B, 32, 8192, 64]
+  paged decode: the same q, K, V draws per request; each request's tokens are
+         stored in pages of P tokens of a cache [num_pages, H, P, D], pages
+         handed out in a seeded random permutation (so a request's pages are
+         scattered), block_table [B, max_pages] int32 (unused entries -1),
+         seq_lens [B] int32.
 """
 import torch
 
@@ -163,3 +168,32 @@ def uniform(shape, seed, lo=0.0, hi=1.0, dtype=torch.float32):
     g = _gen(seed)
     t = torch.rand(shape, generator=g, dtype=torch.float32)
     return (t * (hi - lo) + lo).to(dtype)
+
+
+def paged_decode_inputs(seq_lens, H=32, D=64, P=16, seed=0, device="cpu", dtype=BF16, spare_pages=7):
+    """q [B, H, D]; k_cache, v_cache [num_pages, H, P, D]; block_table [B, max_pages]
+    int32; seq_lens [B] int32; plus the contiguous K, V of each request (lists of
+    [H, S_b, D]) holding the same values, for comparison.  Page ids are a seeded
+    random permutation of 0 .. num_pages-1 (spare pages stay random)."""
+    B = len(seq_lens)
+    g = _gen(seed)
+    npg = [(int(s) + P - 1) // P for s in seq_lens]
+    max_pages = max(max(npg), 1)
+    num_pages = sum(npg) + spare_pages
+    q = _randn((B, H, D), g).to(dtype)
+    k_cache = _randn((num_pages, H, P, D), g).to(dtype)
+    v_cache = _randn((num_pages, H, P, D), g).to(dtype)
+    perm = torch.randperm(num_pages, generator=g)
+    bt = torch.full((B, max_pages), -1, dtype=torch.int32)
+    k_seq, v_seq = [], []
+    used = 0
+    for b in range(B):
+        pages = perm[used:used + npg[b]]
+        used += npg[b]
+        bt[b, :npg[b]] = pages.to(torch.int32)
+        S = int(seq_lens[b])
+        k_seq.append(k_cache[pages].permute(1, 0, 2, 3).reshape(H, -1, D)[:, :S])
+        v_seq.append(v_cache[pages].permute(1, 0, 2, 3).reshape(H, -1, D)[:, :S])
+    sl = torch.tensor([int(s) for s in seq_lens], dtype=torch.int32)
+    return (q.to(device), k_cache.to(device), v_cache.to(device), bt.to(device), sl.to(device),
+            k_seq, v_seq)
