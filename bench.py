@@ -211,6 +211,7 @@ def main():
 
     out["invariance_cost"] = invariance_cost(Wd, bd, x0, dq, dk, dv, Y)
     out["row_ops"] = row_ops(X, Y)
+    out["paged_decode"] = paged_decode(dq, dk, dv, dout)
 
     del X, Y, Q, Kt, V, Sb, Pb, Ob, dq, dk, dv
     torch.cuda.empty_cache()
@@ -301,6 +302,49 @@ def row_ops(X, Y):
         gbs = nbytes / (t * 1e-3) / 1e9
         res[name] = {"us": round(t * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
     del yr, ym, ys
+    return res
+
+
+def paged_decode(dq, dk, dv, dout):
+    """Untimed extra: decode over a paged cache (16-token pages [num_pages, 32,
+    16, 64], placed by a seeded permutation) holding the decode workload's K and
+    V.  All requests at 8192 tokens (bits checked against the contiguous
+    result), then seeded lengths uniform in [1, 8192]; bytes = the K and V rows
+    of each request's tokens + q + out."""
+    import torch
+
+    from invariant_persistent_bf16_amd import bi
+
+    dev = dq.device
+    B, H, S, D = dk.shape
+    P = 16
+    npb = S // P
+    g = torch.Generator(device=dev)
+    g.manual_seed(21)
+    perm = torch.randperm(B * npb, generator=g, device=dev)
+    kc = torch.empty(B * npb, H, P, D, dtype=dk.dtype, device=dev)
+    vc = torch.empty_like(kc)
+    kc[perm] = dk.view(B, H, npb, P, D).permute(0, 2, 1, 3, 4).reshape(B * npb, H, P, D)
+    vc[perm] = dv.view(B, H, npb, P, D).permute(0, 2, 1, 3, 4).reshape(B * npb, H, P, D)
+    bt = perm.view(B, npb).to(torch.int32)
+    ws = torch.empty(bi.bi_decode_attn_paged_workspace_bytes(B, H, S, D) // 4, dtype=torch.float32, device=dev)
+    o = torch.empty_like(dout)
+    full = torch.full((B,), S, dtype=torch.int32, device=dev)
+    lens = torch.randint(1, S + 1, (B,), generator=torch.Generator().manual_seed(22), dtype=torch.int32)
+    res = {}
+    for name, sl in (("all_8192", full), ("uniform_1_8192", lens.to(dev))):
+        fn = lambda: bi.bi_decode_attn_paged(dq, kc, vc, bt, sl, S, 0.125, out=o, workspace=ws)
+        t = _time_ms(fn)
+        tokens = int(sl.sum().item())
+        nbytes = tokens * H * D * 2 * 2 + B * H * D * (2 + 4)
+        gbs = nbytes / (t * 1e-3) / 1e9
+        res[name] = {"us": round(t * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                     "mean_len": round(tokens / B, 1)}
+        if name == "all_8192":
+            fn()
+            torch.cuda.synchronize()
+            res[name]["bits_equal_contiguous"] = bool(torch.equal(o.view(torch.int32), dout.view(torch.int32)))
+    del kc, vc
     return res
 
 

@@ -178,6 +178,46 @@ int bi_decode_attn(int64_t B, int64_t H, int64_t S, int64_t D,
 int bi_decode_chunk_tokens(void);
 
 /*
+ * bi_decode_attn_paged — bi_decode_attn for a batch of requests of their own
+ * lengths whose K and V live in a paged cache.
+ * Source: the deterministic-inference handbook page, sections "与 batch 无关：
+ * 固定切分" (fixed-length KV split, chunk boundaries at absolute token
+ * positions) and "框架里的开关" (chunked prefill and the prefix cache must
+ * leave a request's results unchanged), applied to the flash-decoding
+ * experiment of section "根源：浮点加法的顺序".
+ *
+ * Request b attends over its first len_b = seq_lens[b] tokens; token t of it
+ * is row t % page_size of page block_table[b * max_pages + t / page_size].
+ * The chunks are [2048c, 2048c + 2048) ∩ [0, len_b) and the arithmetic is that
+ * of bi_decode_attn, so request b's output has the bits bi_decode_attn gives
+ * for B = 1, S = len_b on the same values, whatever the other requests, their
+ * lengths, max_pages, max_seq_len or where its pages are placed.
+ *
+ * q [B, H, D] contiguous; k_cache, v_cache [num_pages, H, page_size, D]
+ * contiguous (one page holds page_size tokens of every head);
+ * block_table [B, max_pages] int32 contiguous (device memory; entries past a
+ * request's ceil(len_b / page_size) pages are not read); seq_lens [B] int32
+ * (device memory); out [B, H, D].  page_size must be a power of two with
+ * max_seq_len <= max_pages * page_size.  max_seq_len (host) bounds every
+ * len_b and sizes the grid and ws: a length outside [0, max_seq_len] is
+ * clamped to it, a page id outside [0, num_pages) reads page 0 (no access
+ * leaves the caches; the result is then meaningless).  len_b = 0 gives NaN.
+ * in_dtype must be BI_BF16; out_dtype BI_F32 or BI_BF16; D 64 or 128.
+ * ws: at least bi_decode_attn_paged_workspace_bytes(B, H, max_seq_len, D)
+ * bytes, 16-byte aligned, owned by the caller.
+ * BI_ERR_UNSUPPORTED when max_seq_len + 2048 >= 2^31 or page_size * D * 2
+ * >= 2^31 (32-bit token and in-page offsets).
+ */
+size_t bi_decode_attn_paged_workspace_bytes(int64_t B, int64_t H, int64_t max_seq_len, int64_t D);
+int bi_decode_attn_paged(int64_t B, int64_t H, int64_t D, const void* q,
+                         const void* k_cache, const void* v_cache,
+                         int64_t num_pages, int64_t page_size,
+                         const int32_t* block_table, int64_t max_pages,
+                         const int32_t* seq_lens, int64_t max_seq_len,
+                         void* out, float scale, void* ws, size_t ws_bytes,
+                         int in_dtype, int out_dtype, void* stream);
+
+/*
  * bi_softmax_rows — P[r, :] = softmax(scale * S[r, :]) for each row, in
  * binary32: max, exponentials, their sum and the division, with one
  * wave per row and a reduction tree fixed by `cols` alone (the

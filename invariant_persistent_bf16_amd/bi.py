@@ -29,6 +29,9 @@ _SIGS = {
     "bi_decode_attn_workspace_bytes": (_sz, [_i64] * 4),
     "bi_decode_attn": (_int, [_i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _f32, _vp, _sz, _int, _int, _vp]),
     "bi_decode_chunk_tokens": (_int, []),
+    "bi_decode_attn_paged_workspace_bytes": (_sz, [_i64] * 4),
+    "bi_decode_attn_paged": (_int, [_i64, _i64, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp,
+                                    _f32, _vp, _sz, _int, _int, _vp]),
     "bi_softmax_rows": (_int, [_i64, _i64, _vp, _i64, _f32, _vp, _i64, _int, _vp]),
     "bi_rms_norm": (_int, [_i64, _i64, _vp, _i64, _vp, _f32, _vp, _i64, _int, _int, _vp]),
     "bi_log_softmax_rows": (_int, [_i64, _i64, _vp, _i64, _vp, _i64, _int, _int, _vp]),
@@ -191,6 +194,29 @@ def bi_decode_attn(q, k, v, scale, out=None, out_dtype=BI_F32, workspace=None, s
                                                   float(scale), _p(workspace),
                                                   workspace.numel() * workspace.element_size(),
                                                   _dt(q), _dt(o), _stream(stream)))
+    return o
+
+
+def bi_decode_attn_paged_workspace_bytes(B, H, max_seq_len, D):
+    return lib().bi_decode_attn_paged_workspace_bytes(B, H, max_seq_len, D)
+
+
+def bi_decode_attn_paged(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, scale, out=None,
+                         out_dtype=BI_F32, workspace=None, stream=None):
+    """Split-KV decode over a paged cache: q [B,H,D], k_cache, v_cache [num_pages,H,P,D],
+    block_table [B, max_pages] int32, seq_lens [B] int32 (both on the device) -> out [B,H,D]."""
+    B, H, D = q.shape
+    num_pages, _, P, _ = k_cache.shape
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_table and seq_lens must be int32")
+    o = _out((B, H, D), out_dtype, q.device, out)
+    need = bi_decode_attn_paged_workspace_bytes(B, H, max_seq_len, D)
+    if workspace is None:
+        workspace = torch.empty(max(need // 4, 1), dtype=torch.float32, device=q.device)
+    _check("bi_decode_attn_paged", lib().bi_decode_attn_paged(
+        B, H, D, _p(q), _p(k_cache), _p(v_cache), num_pages, P, _p(block_table), block_table.shape[1],
+        _p(seq_lens), int(max_seq_len), _p(o), float(scale), _p(workspace),
+        workspace.numel() * workspace.element_size(), _dt(q), _dt(o), _stream(stream)))
     return o
 
 

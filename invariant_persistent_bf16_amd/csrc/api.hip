@@ -242,6 +242,19 @@ int row_op_check(int64_t rows, int64_t cols, const void* x, int64_t ldx, void* y
     return BI_OK;
 }
 
+template <int D>
+static void decode_paged_launch(dim3 g1, dim3 g2, hipStream_t st, bool uni, const void* q, const void* kc,
+                                const void* vc, const int32_t* bt, int64_t max_pages, const int32_t* sl,
+                                int H, int log2p, int num_pages, int max_seq, int maxchunks, float* wsf,
+                                float scale, void* out, int64_t BH, int out_dtype) {
+    auto kern = uni ? decode_chunk_paged_kernel<D, true> : decode_chunk_paged_kernel<D, false>;
+    hipLaunchKernelGGL(kern, g1, dim3(DEC_THREADS), 0, st, (const uint16_t*)q, (const uint16_t*)kc,
+                       (const uint16_t*)vc, bt, max_pages, sl, H, log2p, num_pages, max_seq, maxchunks, (int)BH, wsf,
+                       scale);
+    auto merge = out_dtype == BI_BF16 ? decode_merge_kernel<D, 1> : decode_merge_kernel<D, 0>;
+    hipLaunchKernelGGL(merge, g2, dim3(256), 0, st, (const float*)wsf, out, BH, maxchunks, sl, H, max_seq);
+}
+
 }  // namespace bi
 
 using namespace bi;
@@ -412,17 +425,67 @@ int bi_decode_attn(int64_t B, int64_t H, int64_t S, int64_t D, const void* q, co
     const dim3 g1((unsigned)(BH * nchunk));
     const dim3 g2((unsigned)cdiv(BH * D, 256));
     float* wsf = (float*)ws;
+    const int sn = (int)nchunk;
     if (D == 64) {
         hipLaunchKernelGGL((decode_chunk_kernel<64>), g1, dim3(DEC_THREADS), 0, st,
-                           (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, wsf, S, (int)nchunk, DEC_CHUNK, scale);
-        if (out_dtype == BI_BF16) hipLaunchKernelGGL((decode_merge_kernel<64, 1>), g2, dim3(256), 0, st, wsf, out, BH, (int)nchunk);
-        else                      hipLaunchKernelGGL((decode_merge_kernel<64, 0>), g2, dim3(256), 0, st, wsf, out, BH, (int)nchunk);
+                           (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, wsf, S, sn, DEC_CHUNK, scale);
+        if (out_dtype == BI_BF16) hipLaunchKernelGGL((decode_merge_kernel<64, 1>), g2, dim3(256), 0, st, wsf, out, BH, sn, nullptr, 1, 0);
+        else                      hipLaunchKernelGGL((decode_merge_kernel<64, 0>), g2, dim3(256), 0, st, wsf, out, BH, sn, nullptr, 1, 0);
     } else {
         hipLaunchKernelGGL((decode_chunk_kernel<128>), g1, dim3(DEC_THREADS), 0, st,
-                           (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, wsf, S, (int)nchunk, DEC_CHUNK, scale);
-        if (out_dtype == BI_BF16) hipLaunchKernelGGL((decode_merge_kernel<128, 1>), g2, dim3(256), 0, st, wsf, out, BH, (int)nchunk);
-        else                      hipLaunchKernelGGL((decode_merge_kernel<128, 0>), g2, dim3(256), 0, st, wsf, out, BH, (int)nchunk);
+                           (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, wsf, S, sn, DEC_CHUNK, scale);
+        if (out_dtype == BI_BF16) hipLaunchKernelGGL((decode_merge_kernel<128, 1>), g2, dim3(256), 0, st, wsf, out, BH, sn, nullptr, 1, 0);
+        else                      hipLaunchKernelGGL((decode_merge_kernel<128, 0>), g2, dim3(256), 0, st, wsf, out, BH, sn, nullptr, 1, 0);
     }
+    return launch_status();
+}
+
+size_t bi_decode_attn_paged_workspace_bytes(int64_t B, int64_t H, int64_t max_seq_len, int64_t D) {
+    if (B < 0 || H < 0 || max_seq_len < 1 || D < 1) return 0;
+    return (size_t)(B * H * cdiv(max_seq_len, DEC_CHUNK) * (2 + D) * 4);
+}
+
+int bi_decode_attn_paged(int64_t B, int64_t H, int64_t D, const void* q, const void* k_cache,
+                         const void* v_cache, int64_t num_pages, int64_t page_size,
+                         const int32_t* block_table, int64_t max_pages, const int32_t* seq_lens,
+                         int64_t max_seq_len, void* out, float scale, void* ws, size_t ws_bytes,
+                         int in_dtype, int out_dtype, void* stream) {
+    if (in_dtype != BI_BF16) return BI_ERR_DTYPE;
+    if (out_dtype != BI_F32 && out_dtype != BI_BF16) return BI_ERR_DTYPE;
+    if (B < 0 || H < 0 || num_pages < 1 || max_pages < 1 || max_seq_len < 1) return BI_ERR_SHAPE;
+    if (page_size < 1 || (page_size & (page_size - 1)) != 0) return BI_ERR_SHAPE;
+    if (max_seq_len > max_pages * page_size) return BI_ERR_SHAPE;
+    if (D != 64 && D != 128) return BI_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0) return BI_OK;
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out) return BI_ERR_NULL;
+    if (!ws) return BI_ERR_WORKSPACE;
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_table, 4) ||
+        !aligned(seq_lens, 4) || !aligned(out, out_dtype == BI_BF16 ? 2 : 4))
+        return BI_ERR_LAYOUT;
+    const int64_t maxchunks = cdiv(max_seq_len, DEC_CHUNK);
+    // Token indices and in-page offsets are 32-bit; page ids are int32.
+    if (B * H * maxchunks > (1ll << 31) - 1 || B * H * D > (1ll << 40) || H > (1 << 30) ||
+        max_seq_len + DEC_CHUNK >= (1ll << 31) || page_size * D * 2 >= (1ll << 31) ||
+        num_pages > (1ll << 31) - 1 || B * max_pages > (1ll << 40))
+        return BI_ERR_UNSUPPORTED;
+    if (ws_bytes < bi_decode_attn_paged_workspace_bytes(B, H, max_seq_len, D) || !aligned(ws, 16))
+        return BI_ERR_WORKSPACE;
+    int log2p = 0;
+    while ((1ll << log2p) < page_size) ++log2p;
+    hipStream_t st = (hipStream_t)stream;
+    const int64_t BH = B * H;
+    const dim3 g1((unsigned)(BH * maxchunks));
+    const dim3 g2((unsigned)cdiv(BH * D, 256));
+    // One page holds all of a wave-wide load's tokens (512 / D of them).
+    const bool uni = page_size >= 512 / D;
+    if (D == 64)
+        decode_paged_launch<64>(g1, g2, st, uni, q, k_cache, v_cache, block_table, max_pages, seq_lens, (int)H,
+                                log2p, (int)num_pages, (int)max_seq_len, (int)maxchunks, (float*)ws, scale, out,
+                                BH, out_dtype);
+    else
+        decode_paged_launch<128>(g1, g2, st, uni, q, k_cache, v_cache, block_table, max_pages, seq_lens, (int)H,
+                                 log2p, (int)num_pages, (int)max_seq_len, (int)maxchunks, (float*)ws, scale, out,
+                                 BH, out_dtype);
     return launch_status();
 }
 

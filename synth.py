@@ -170,30 +170,47 @@ def uniform(shape, seed, lo=0.0, hi=1.0, dtype=torch.float32):
     return (t * (hi - lo) + lo).to(dtype)
 
 
-def paged_decode_inputs(seq_lens, H=32, D=64, P=16, seed=0, device="cpu", dtype=BF16, spare_pages=7):
+def paged_decode_inputs(seq_lens, H=32, D=64, P=16, seed=0, device="cpu", dtype=BF16, spare_pages=7,
+                        with_seq=True, block_pages=2048):
     """q [B, H, D]; k_cache, v_cache [num_pages, H, P, D]; block_table [B, max_pages]
-    int32; seq_lens [B] int32; plus the contiguous K, V of each request (lists of
-    [H, S_b, D]) holding the same values, for comparison.  Page ids are a seeded
-    random permutation of 0 .. num_pages-1 (spare pages stay random)."""
+    int32; seq_lens [B] int32; and, if with_seq, the contiguous K, V of each
+    request (lists of [H, S_b, D] views) holding the same values.  Page ids are a
+    seeded random permutation of 0 .. num_pages-1 (spare pages stay random).
+    Drawn on `device`, `block_pages` pages at a time (bounded float32 staging)."""
     B = len(seq_lens)
-    g = _gen(seed)
+    g = _gen(seed, device)
     npg = [(int(s) + P - 1) // P for s in seq_lens]
     max_pages = max(max(npg), 1)
     num_pages = sum(npg) + spare_pages
-    q = _randn((B, H, D), g).to(dtype)
-    k_cache = _randn((num_pages, H, P, D), g).to(dtype)
-    v_cache = _randn((num_pages, H, P, D), g).to(dtype)
-    perm = torch.randperm(num_pages, generator=g)
-    bt = torch.full((B, max_pages), -1, dtype=torch.int32)
+    q = _randn((B, H, D), g, device=device).to(dtype)
+    k_cache = torch.empty((num_pages, H, P, D), dtype=dtype, device=device)
+    v_cache = torch.empty((num_pages, H, P, D), dtype=dtype, device=device)
+    for cache in (k_cache, v_cache):
+        for p0 in range(0, num_pages, block_pages):
+            p1 = min(num_pages, p0 + block_pages)
+            cache[p0:p1] = _randn((p1 - p0, H, P, D), g, device=device).to(dtype)
+    perm = torch.randperm(num_pages, generator=g, device=device)
+    bt = torch.full((B, max_pages), -1, dtype=torch.int32, device=device)
     k_seq, v_seq = [], []
     used = 0
     for b in range(B):
         pages = perm[used:used + npg[b]]
         used += npg[b]
         bt[b, :npg[b]] = pages.to(torch.int32)
-        S = int(seq_lens[b])
-        k_seq.append(k_cache[pages].permute(1, 0, 2, 3).reshape(H, -1, D)[:, :S])
-        v_seq.append(v_cache[pages].permute(1, 0, 2, 3).reshape(H, -1, D)[:, :S])
-    sl = torch.tensor([int(s) for s in seq_lens], dtype=torch.int32)
-    return (q.to(device), k_cache.to(device), v_cache.to(device), bt.to(device), sl.to(device),
-            k_seq, v_seq)
+        if with_seq:
+            S = int(seq_lens[b])
+            k_seq.append(k_cache[pages].permute(1, 0, 2, 3).reshape(H, -1, D)[:, :S])
+            v_seq.append(v_cache[pages].permute(1, 0, 2, 3).reshape(H, -1, D)[:, :S])
+    sl = torch.tensor([int(s) for s in seq_lens], dtype=torch.int32, device=device)
+    return q, k_cache, v_cache, bt, sl, k_seq, v_seq
+
+
+def request_kv(k_cache, v_cache, block_table, seq_lens, b):
+    """The contiguous K, V [1, H, S_b, D] of request b of a paged cache (a gather)."""
+    S = int(seq_lens[b])
+    P = k_cache.shape[2]
+    pages = block_table[b, :(S + P - 1) // P].long()
+    H, D = k_cache.shape[1], k_cache.shape[3]
+    k = k_cache[pages].permute(1, 0, 2, 3).reshape(H, -1, D)[:, :S]
+    v = v_cache[pages].permute(1, 0, 2, 3).reshape(H, -1, D)[:, :S]
+    return k[None].contiguous(), v[None].contiguous()

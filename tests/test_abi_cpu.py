@@ -60,6 +60,10 @@ def bi():
     L.bi_decode_attn_workspace_bytes.argtypes = [i64] * 4
     L.bi_decode_attn.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, ctypes.c_float, vp,
                                  ctypes.c_size_t, ctypes.c_int, ctypes.c_int, vp]
+    L.bi_decode_attn_paged_workspace_bytes.restype = ctypes.c_size_t
+    L.bi_decode_attn_paged_workspace_bytes.argtypes = [i64] * 4
+    L.bi_decode_attn_paged.argtypes = [i64, i64, i64, vp, vp, vp, i64, i64, vp, i64, vp, i64, vp,
+                                       ctypes.c_float, vp, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, vp]
     L.bi_softmax_rows.argtypes = [i64, i64, vp, i64, ctypes.c_float, vp, i64, ctypes.c_int, vp]
     L.bi_rms_norm.argtypes = [i64, i64, vp, i64, vp, ctypes.c_float, vp, i64, ctypes.c_int, ctypes.c_int, vp]
     L.bi_log_softmax_rows.argtypes = [i64, i64, vp, i64, vp, i64, ctypes.c_int, ctypes.c_int, vp]
@@ -151,6 +155,29 @@ def test_decode_workspace_size_and_validation(bi):
     assert dec(ws_bytes=8) == WS
     assert dec(q=P + 8) == LAYOUT
     assert dec(B=0) == OK
+
+
+def test_paged_decode_workspace_size_and_validation(bi):
+    assert bi.bi_decode_attn_paged_workspace_bytes(256, 32, 8192, 64) == 256 * 32 * 4 * 66 * 4
+    assert bi.bi_decode_attn_paged_workspace_bytes(3, 2, 2049, 128) == 3 * 2 * 2 * 130 * 4
+    assert bi.bi_decode_attn_paged_workspace_bytes(3, 2, 0, 128) == 0
+
+    def dec(**kw):
+        a = dict(B=2, H=2, D=64, q=P, kc=P, vc=P, num_pages=64, page=16, bt=P, max_pages=32, sl=P,
+                 max_seq=512, out=P, scale=0.125, ws=P, ws_bytes=1 << 20, ind=BF16, outd=F32)
+        a.update(kw)
+        return bi.bi_decode_attn_paged(*a.values(), None)
+
+    assert dec(ind=F32) == DTYPE and dec(outd=7) == DTYPE
+    assert dec(page=12) == SHAPE and dec(page=0) == SHAPE        # page size a power of two
+    assert dec(max_seq=513) == SHAPE                             # beyond max_pages * page
+    assert dec(max_seq=0) == SHAPE and dec(num_pages=0) == SHAPE and dec(B=-1) == SHAPE
+    assert dec(D=96) == UNSUP
+    assert dec(max_seq=(1 << 31) - 100, max_pages=1 << 27) == UNSUP
+    assert dec(bt=None) == NULL and dec(sl=None) == NULL and dec(vc=None) == NULL
+    assert dec(ws=None) == WS and dec(ws_bytes=100) == WS
+    assert dec(kc=P + 8) == LAYOUT and dec(bt=P + 2) == LAYOUT
+    assert dec(B=0) == OK and dec(H=0) == OK
 
 
 def test_softmax_validation(bi):
