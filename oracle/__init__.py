@@ -239,6 +239,26 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale):
     return out
 
 
+def prefill_paged(q, cu_q, q_pos0, k_cache, v_cache, block_table, scale):
+    """Causal prefill over a paged cache: q [total_q, H, D] (request b's rows
+    cu_q[b] .. cu_q[b+1]-1, the first at absolute position q_pos0[b]), caches
+    [num_pages, H, P, D], block_table [B, max_pages] int32."""
+    lib = _load()
+    q, k_cache, v_cache = q.contiguous(), k_cache.contiguous(), v_cache.contiguous()
+    cu = torch.as_tensor(cu_q).contiguous().to(torch.int32)
+    p0 = torch.as_tensor(q_pos0).contiguous().to(torch.int32)
+    bt = block_table.contiguous().to(torch.int32)
+    T, H, D = q.shape
+    B = p0.shape[0]
+    assert cu.shape[0] == B + 1 and int(cu[-1]) == T
+    P = k_cache.shape[2]
+    out, op = _out((T, H, D))
+    lib.oracle_prefill_paged(_i64(B), _i64(H), _i64(D), _ptr(q), _ptr(cu), _ptr(p0), _ptr(k_cache),
+                             _ptr(v_cache), _ptr(bt), _i64(bt.shape[1]), _i64(P), ctypes.c_double(scale),
+                             ctypes.c_int(_dt(q)), op)
+    return out
+
+
 def decode_chunked(q, k, v, scale, chunk=2048, reqs=None, triples=False):
     """Fixed-length-chunk flash decoding with an ascending-order LSE merge."""
     lib = _load()

@@ -403,6 +403,52 @@ void oracle_decode_paged(int64_t B, int64_t H, int64_t D, const void* q, const v
     }
 }
 
+/* Causal prefill attention over a paged KV cache, for chunked prefill with a
+ * prefix cache ([HB] "与 batch 无关：固定切分", the items on attention and on
+ * chunked prefill with the prefix cache: a request's attention must not depend
+ * on how its prompt was cut into prefill chunks or where its KV came from).
+ * Request b owns query rows cu_q[b] .. cu_q[b+1]-1 of q [total_q, H, D]; row
+ * cu_q[b] + j sits at absolute position pos = q_pos0[b] + j and attends to the
+ * request's keys 0 .. pos (inclusive), key t read from page
+ * block_table[b * max_pages + t / P], slot t % P of the caches
+ * [num_pages, H, P, D].  Unsplit fp64 attention; out [total_q, H, D]. */
+void oracle_prefill_paged(int64_t B, int64_t H, int64_t D, const void* q, const int32_t* cu_q,
+                          const int32_t* q_pos0, const void* kc, const void* vc,
+                          const int32_t* block_table, int64_t max_pages, int64_t P, double scale,
+                          int dtype, double* out) {
+    const int64_t total = cu_q[B];
+    #pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int64_t r = 0; r < total; ++r) {
+        for (int64_t h = 0; h < H; ++h) {
+            int64_t b = 0;
+            while (cu_q[b + 1] <= r) ++b;
+            const int64_t S = (int64_t)q_pos0[b] + (r - cu_q[b]) + 1;   /* keys 0 .. pos */
+            const int32_t* bt = block_table + b * max_pages;
+            double* o = out + (r * H + h) * D;
+            double* sc = (double*)malloc(sizeof(double) * (size_t)S);
+            double m = -INFINITY;
+            for (int64_t t = 0; t < S; ++t) {
+                const int64_t row = ((int64_t)bt[t / P] * H + h) * P + t % P;
+                double acc = 0.0;
+                for (int64_t d = 0; d < D; ++d)
+                    acc += widen(q, dtype, (r * H + h) * D + d) * widen(kc, dtype, row * D + d);
+                sc[t] = scale * acc;
+                if (sc[t] > m) m = sc[t];
+            }
+            double den = 0.0;
+            for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+            for (int64_t t = 0; t < S; ++t) {
+                const int64_t row = ((int64_t)bt[t / P] * H + h) * P + t % P;
+                const double p = exp(sc[t] - m);
+                den += p;
+                for (int64_t d = 0; d < D; ++d) o[d] += p * widen(vc, dtype, row * D + d);
+            }
+            for (int64_t d = 0; d < D; ++d) o[d] /= den;
+            free(sc);
+        }
+    }
+}
+
 /* [HB] flash-decoding with fixed-length chunks.  The KV sequence is cut into
  * consecutive chunks of `chunk` tokens from position 0 (the last may be
  * shorter).  Each chunk c keeps the triple

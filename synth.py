@@ -22,6 +22,9 @@ Shapes and distributions follow the pages' workloads:
          bias 0.02*randn [1152]
   attn   Q, K, V randn [B, 8, 1024, 128] flattened to [8B, 1024, 128]
   decode q randn [B, 32, 64], K, V randn [B, 32, 8192, 64]
+  paged prefill: q randn [total_q, H, D] (request b's rows cu_q[b] .. cu_q[b+1]-1,
+         the first at position prefix_b), then the K and V caches as for paged
+         decode holding each request's prefix_b + q_len_b tokens.
   paged decode: the same q, K, V draws per request; each request's tokens are
          stored in pages of P tokens of a cache [num_pages, H, P, D], pages
          handed out in a seeded random permutation (so a request's pages are
@@ -214,3 +217,36 @@ def request_kv(k_cache, v_cache, block_table, seq_lens, b):
     k = k_cache[pages].permute(1, 0, 2, 3).reshape(H, -1, D)[:, :S]
     v = v_cache[pages].permute(1, 0, 2, 3).reshape(H, -1, D)[:, :S]
     return k[None].contiguous(), v[None].contiguous()
+
+
+def paged_prefill_inputs(prefix_lens, q_lens, H=8, D=128, P=16, seed=0, device="cpu", dtype=BF16,
+                         spare_pages=5, block_pages=2048):
+    """Chunked-prefill inputs: q [total_q, H, D]; cu_q [B+1] int32; q_pos0 [B] int32
+    (= prefix_lens); k_cache, v_cache [num_pages, H, P, D] holding each request's
+    prefix_b + q_len_b tokens; block_table [B, max_pages] int32 (pages a seeded
+    permutation, unused entries -1)."""
+    B = len(q_lens)
+    g = _gen(seed, device)
+    kv = [int(a) + int(n) for a, n in zip(prefix_lens, q_lens)]
+    cu = [0]
+    for n in q_lens:
+        cu.append(cu[-1] + int(n))
+    q = _randn((cu[-1], H, D), g, device=device).to(dtype)
+    npg = [(n + P - 1) // P for n in kv]
+    max_pages = max(max(npg), 1)
+    num_pages = sum(npg) + spare_pages
+    k_cache = torch.empty((num_pages, H, P, D), dtype=dtype, device=device)
+    v_cache = torch.empty((num_pages, H, P, D), dtype=dtype, device=device)
+    for cache in (k_cache, v_cache):
+        for p0 in range(0, num_pages, block_pages):
+            p1 = min(num_pages, p0 + block_pages)
+            cache[p0:p1] = _randn((p1 - p0, H, P, D), g, device=device).to(dtype)
+    perm = torch.randperm(num_pages, generator=g, device=device)
+    bt = torch.full((B, max_pages), -1, dtype=torch.int32, device=device)
+    used = 0
+    for b in range(B):
+        bt[b, :npg[b]] = perm[used:used + npg[b]].to(torch.int32)
+        used += npg[b]
+    cu_q = torch.tensor(cu, dtype=torch.int32, device=device)
+    q_pos0 = torch.tensor([int(a) for a in prefix_lens], dtype=torch.int32, device=device)
+    return q, cu_q, q_pos0, k_cache, v_cache, bt
