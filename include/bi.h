@@ -218,6 +218,48 @@ int bi_decode_attn_paged(int64_t B, int64_t H, int64_t D, const void* q,
                          int in_dtype, int out_dtype, void* stream);
 
 /*
+ * bi_prefill_attn_paged — causal attention of a batch of prefill chunks over
+ * a paged KV cache, the KV split at a fixed length of 4096 tokens.
+ * Source: the deterministic-inference handbook page, section "与 batch 无关：
+ * 固定切分" (attention splits KV by a fixed length, 4096 tokens for prefill;
+ * a request's KV and attention must not depend on how its prompt was cut into
+ * prefill chunks or whether its prefix came from the cache), with the
+ * per-chunk triple and log-sum-exp merge of section "根源：浮点加法的顺序".
+ *
+ * Request b owns query rows cu_q[b] .. cu_q[b+1]-1 of q [total_q, H, D]
+ * (contiguous); row cu_q[b] + j is at position pos = q_pos0[b] + j and
+ * attends to the request's keys 0 .. pos, key t stored at row t % page_size
+ * of page block_table[b * max_pages + t / page_size] of k_cache and v_cache
+ * [num_pages, H, page_size, D] (the caller has written the chunk's own keys
+ * and values there).  With x_t = (q . k_t) * fl(scale * log2 e) in binary32,
+ * each 4096-token chunk c of keys gives m_c = max x_t, l_c = sum 2^(x_t - m_c),
+ * o_c = sum 2^(x_t - m_c) v_t, merged in ascending c:
+ *   out = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c,  M = max_c m_c.
+ * A query's bits depend only on its position and the keys: the same prompt
+ * prefilled in one call or in chunks (each with its q_pos0), alone or in a
+ * batch, gives the same bits per query.
+ *
+ * cu_q [B+1], q_pos0 [B], block_table [B, max_pages]: int32 device memory.
+ * max_q and max_kv_len (host) size the grid: every request has at most max_q
+ * queries and q_pos0[b] + (its query count) <= max_kv_len <= max_pages *
+ * page_size; device values outside these bounds are clamped (no access
+ * leaves the buffers; the result is then meaningless), a page id outside
+ * [0, num_pages) reads page 0.  out [total_q, H, D], 16-byte aligned.
+ * in_dtype BI_BF16; out_dtype BI_F32 or BI_BF16; D must be 128; page_size a
+ * power of two.  ws: bi_prefill_attn_paged_workspace_bytes(total_q, H,
+ * max_kv_len, D) bytes, 16-byte aligned, owned by the caller (0 bytes, and ws
+ * may be null, when max_kv_len <= 4096).
+ */
+size_t bi_prefill_attn_paged_workspace_bytes(int64_t total_q, int64_t H, int64_t max_kv_len, int64_t D);
+int bi_prefill_attn_paged(int64_t B, int64_t H, int64_t D, const void* q, int64_t total_q,
+                          const int32_t* cu_q, const int32_t* q_pos0, int64_t max_q,
+                          const void* k_cache, const void* v_cache,
+                          int64_t num_pages, int64_t page_size,
+                          const int32_t* block_table, int64_t max_pages, int64_t max_kv_len,
+                          void* out, float scale, void* ws, size_t ws_bytes,
+                          int in_dtype, int out_dtype, void* stream);
+
+/*
  * bi_softmax_rows — P[r, :] = softmax(scale * S[r, :]) for each row, in
  * binary32: max, exponentials, their sum and the division, with one
  * wave per row and a reduction tree fixed by `cols` alone (the

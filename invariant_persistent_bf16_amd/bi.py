@@ -32,6 +32,9 @@ _SIGS = {
     "bi_decode_attn_paged_workspace_bytes": (_sz, [_i64] * 4),
     "bi_decode_attn_paged": (_int, [_i64, _i64, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp,
                                     _f32, _vp, _sz, _int, _int, _vp]),
+    "bi_prefill_attn_paged_workspace_bytes": (_sz, [_i64] * 4),
+    "bi_prefill_attn_paged": (_int, [_i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _vp, _i64,
+                                     _i64, _vp, _f32, _vp, _sz, _int, _int, _vp]),
     "bi_softmax_rows": (_int, [_i64, _i64, _vp, _i64, _f32, _vp, _i64, _int, _vp]),
     "bi_rms_norm": (_int, [_i64, _i64, _vp, _i64, _vp, _f32, _vp, _i64, _int, _int, _vp]),
     "bi_log_softmax_rows": (_int, [_i64, _i64, _vp, _i64, _vp, _i64, _int, _int, _vp]),
@@ -217,6 +220,33 @@ def bi_decode_attn_paged(q, k_cache, v_cache, block_table, seq_lens, max_seq_len
         B, H, D, _p(q), _p(k_cache), _p(v_cache), num_pages, P, _p(block_table), block_table.shape[1],
         _p(seq_lens), int(max_seq_len), _p(o), float(scale), _p(workspace),
         workspace.numel() * workspace.element_size(), _dt(q), _dt(o), _stream(stream)))
+    return o
+
+
+def bi_prefill_attn_paged_workspace_bytes(total_q, H, max_kv_len, D):
+    return lib().bi_prefill_attn_paged_workspace_bytes(total_q, H, max_kv_len, D)
+
+
+def bi_prefill_attn_paged(q, cu_q, q_pos0, max_q, k_cache, v_cache, block_table, max_kv_len, scale,
+                          out=None, out_dtype=BI_F32, workspace=None, stream=None):
+    """Causal prefill attention over a paged cache, KV split at 4096 tokens:
+    q [total_q, H, D]; cu_q [B+1], q_pos0 [B], block_table [B, max_pages] int32 on
+    the device; caches [num_pages, H, P, D] -> out [total_q, H, D]."""
+    T, H, D = q.shape
+    B = q_pos0.shape[0]
+    num_pages, _, P, _ = k_cache.shape
+    for t in (cu_q, q_pos0, block_table):
+        if t.dtype != torch.int32:
+            raise TypeError("cu_q, q_pos0 and block_table must be int32")
+    o = _out((T, H, D), out_dtype, q.device, out)
+    need = bi_prefill_attn_paged_workspace_bytes(T, H, max_kv_len, D)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("bi_prefill_attn_paged", lib().bi_prefill_attn_paged(
+        B, H, D, _p(q), T, _p(cu_q), _p(q_pos0), int(max_q), _p(k_cache), _p(v_cache), num_pages, P,
+        _p(block_table), block_table.shape[1], int(max_kv_len), _p(o), float(scale), _p(workspace), wsz,
+        _dt(q), _dt(o), _stream(stream)))
     return o
 
 

@@ -10,6 +10,7 @@
 #include "../../include/bi.h"
 #include "conv_pack.hpp"
 #include "decode.hpp"
+#include "prefill.hpp"
 #include "gemm_bf16.hpp"
 #include "gemm_f32.hpp"
 #include "softmax.hpp"
@@ -486,6 +487,72 @@ int bi_decode_attn_paged(int64_t B, int64_t H, int64_t D, const void* q, const v
         decode_paged_launch<128>(g1, g2, st, uni, q, k_cache, v_cache, block_table, max_pages, seq_lens, (int)H,
                                  log2p, (int)num_pages, (int)max_seq_len, (int)maxchunks, (float*)ws, scale, out,
                                  BH, out_dtype);
+    return launch_status();
+}
+
+size_t bi_prefill_attn_paged_workspace_bytes(int64_t total_q, int64_t H, int64_t max_kv_len, int64_t D) {
+    if (total_q < 0 || H < 0 || max_kv_len < 1 || D < 1) return 0;
+    const int64_t nch = cdiv(max_kv_len, PF_CHUNK);
+    return nch > 1 ? (size_t)(nch * H * (2 + D) * total_q * 4) : 0;
+}
+
+int bi_prefill_attn_paged(int64_t B, int64_t H, int64_t D, const void* q, int64_t total_q,
+                          const int32_t* cu_q, const int32_t* q_pos0, int64_t max_q,
+                          const void* k_cache, const void* v_cache, int64_t num_pages, int64_t page_size,
+                          const int32_t* block_table, int64_t max_pages, int64_t max_kv_len,
+                          void* out, float scale, void* ws, size_t ws_bytes,
+                          int in_dtype, int out_dtype, void* stream) {
+    if (in_dtype != BI_BF16) return BI_ERR_DTYPE;
+    if (out_dtype != BI_F32 && out_dtype != BI_BF16) return BI_ERR_DTYPE;
+    if (B < 0 || H < 0 || total_q < 0 || max_q < 1 || num_pages < 1 || max_pages < 1 || max_kv_len < 1)
+        return BI_ERR_SHAPE;
+    if (page_size < 1 || (page_size & (page_size - 1)) != 0) return BI_ERR_SHAPE;
+    if (max_kv_len > max_pages * page_size) return BI_ERR_SHAPE;
+    if (D != 128) return BI_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0 || total_q == 0) return BI_OK;
+    if (!q || !cu_q || !q_pos0 || !k_cache || !v_cache || !block_table || !out) return BI_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(cu_q, 4) ||
+        !aligned(q_pos0, 4) || !aligned(block_table, 4) || !aligned(out, 16))
+        return BI_ERR_LAYOUT;
+    const int64_t maxchunks = cdiv(max_kv_len, PF_CHUNK);
+    const int64_t ntiles = cdiv(max_q, PF_QT);
+    // Positions, in-page offsets and page ids are 32-bit; row offsets 64-bit.
+    if (maxchunks * B * ntiles * H > (1ll << 31) - 1 || max_q > (1ll << 30) || H > (1 << 20) ||
+        max_kv_len + PF_CHUNK >= (1ll << 31) || page_size * D * 2 >= (1ll << 31) ||
+        num_pages > (1ll << 31) - 1 || B > (1 << 30) || total_q * H * D > (1ll << 46))
+        return BI_ERR_UNSUPPORTED;
+    const size_t need = bi_prefill_attn_paged_workspace_bytes(total_q, H, max_kv_len, D);
+    if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 16))) return BI_ERR_WORKSPACE;
+    int log2p = 0;
+    while ((1ll << log2p) < page_size) ++log2p;
+    PfArgs a;
+    a.q = (const uint16_t*)q;
+    a.kc = (const uint8_t*)k_cache;
+    a.vc = (const uint8_t*)v_cache;
+    a.table = block_table;
+    a.cu_q = cu_q;
+    a.q_pos0 = q_pos0;
+    a.ws = (float*)ws;
+    a.out = out;
+    a.total_q = total_q;
+    a.max_pages = max_pages;
+    a.B = (int)B;
+    a.H = (int)H;
+    a.log2p = log2p;
+    a.num_pages = (int)num_pages;
+    a.max_q = (int)max_q;
+    a.max_kv = (int)max_kv_len;
+    a.ntiles = (int)ntiles;
+    a.cscale = (float)((double)scale * 1.4426950408889634);
+    hipStream_t st = (hipStream_t)stream;
+    const dim3 g1((unsigned)(maxchunks * B * ntiles * H));
+    if (out_dtype == BI_BF16) hipLaunchKernelGGL((prefill_chunk_kernel<128, 1>), g1, dim3(PF_THREADS), 0, st, a);
+    else                      hipLaunchKernelGGL((prefill_chunk_kernel<128, 0>), g1, dim3(PF_THREADS), 0, st, a);
+    if (maxchunks > 1) {
+        const dim3 g2((unsigned)(B * ntiles * H));
+        if (out_dtype == BI_BF16) hipLaunchKernelGGL((prefill_merge_kernel<128, 1>), g2, dim3(256), 0, st, a);
+        else                      hipLaunchKernelGGL((prefill_merge_kernel<128, 0>), g2, dim3(256), 0, st, a);
+    }
     return launch_status();
 }
 

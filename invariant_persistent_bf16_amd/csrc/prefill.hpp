@@ -1,0 +1,436 @@
+// Causal prefill attention over a paged KV cache with the KV split at a fixed
+// length of 4096 tokens (the deterministic-inference handbook page, section
+// "与 batch 无关：固定切分": attention splits KV by a fixed token count, 4096 for
+// prefill, never by a count of parts chosen from the load; chunked prefill and
+// the prefix cache must leave a request's attention unchanged).
+//
+// Request b owns query rows cu_q[b] .. cu_q[b+1]-1 of q [total_q, H, D]; row
+// cu_q[b] + j sits at position pos = q_pos0[b] + j and attends to the
+// request's keys 0 .. pos, key t in page table[b][t >> log2p], slot
+// t & (P - 1) of the caches [num_pages, H, P, D].  The keys are cut into
+// chunks [4096c, 4096c + 4096); chunk c of a query yields the triple
+//     m_c = max_t x_t,  l_c = sum_t 2^(x_t - m_c),  o_c = sum_t 2^(x_t - m_c) v_t
+// with x_t = (q . k_t) * (scale * log2 e) (the base-2 form of the softmax), and
+// the triples are merged in ascending chunk order:
+//     M = max_c m_c,  out = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c.
+// Every step of a query's arithmetic is a function of its position and the
+// keys alone, never of the other queries in its tile or batch: so a prompt
+// prefilled in one call, in several chunks, or after a prefix-cache hit gives
+// the same bits for each query.
+//
+// Kernel 1, one workgroup of 8 waves per (chunk, request, 256-query tile,
+// head); wave w owns 32 queries.  The chunk's keys advance in blocks of 64
+// through a 3-stage LDS ring (K and V, 32 KiB per stage), copied HBM -> LDS by
+// global_load_lds_dwordx4 two blocks ahead of use.  Per block and wave:
+//   * S^T = K Q^T on the MFMA (v_mfma_f32_32x32x16_bf16, D/16 slices in
+//     ascending d): lane l then holds query l % 32 and 32 of the 64 keys, so a
+//     query's maximum and sum are a lane's own values plus one exchange with
+//     lane l ^ 32;
+//   * online softmax within the chunk: m' = max(m, block max),
+//     l' = l * 2^(m - m') + sum 2^(x - m'), o' = o * 2^(m - m') + P V, keys of
+//     the block in a fixed order; masked keys (t > pos) give exactly 0;
+//   * O^T += V^T P^T on the MFMA, P^T straight from the score registers as
+//     two bfloat16 terms (hi = bf16(p), lo = bf16(p - hi); two MFMAs, so p
+//     enters the binary32 sums to about 2^-17), V^T read with
+//     ds_read_b64_tr_b16 (gfx950's transposing LDS read).  The MFMA's 16-key slices take the keys of a lane
+//     half in the order the score registers hold them, so V's rows sit in LDS
+//     with bits 2 and 3 of the key index swapped.
+// A query with one chunk (pos < 4096) writes out = o / l itself (the merge of
+// one triple gives these bits); others write their triples to ws
+// [chunk][H][2 + D][total_q], and kernel 2 merges them.
+#pragma once
+
+#include <type_traits>
+
+#include "common.hpp"
+
+namespace bi {
+
+constexpr int PF_CHUNK = 4096;
+constexpr int PF_KB = 64;                  // keys per block
+constexpr int PF_WAVES = 8;
+constexpr int PF_QT = PF_WAVES * 32;       // queries per tile
+constexpr int PF_THREADS = PF_WAVES * 64;
+constexpr int PF_NSTAGE = 3;
+
+typedef __attribute__((address_space(3))) void pf_lds_t;
+typedef short pf_v4i16_t __attribute__((ext_vector_type(4)));
+
+struct PfArgs {
+    const uint16_t* q;
+    const uint8_t* kc;
+    const uint8_t* vc;
+    const int32_t* table;
+    const int32_t* cu_q;
+    const int32_t* q_pos0;
+    float* ws;
+    void* out;
+    int64_t total_q, max_pages;
+    int B, H, log2p, num_pages, max_q, max_kv, ntiles;
+    float cscale;   // scale * log2(e)
+};
+
+// Geometry of request b, device values clamped into range: rows
+// [r0, r0 + n) of q; query j at position min(p0 + j, max_kv - 1).
+struct PfReq {
+    int64_t r0;
+    int n, p0;
+};
+__device__ __forceinline__ PfReq pf_request(const PfArgs& a, int b) {
+    PfReq r;
+    const int64_t lo = min(max((int64_t)a.cu_q[b], (int64_t)0), a.total_q);
+    const int64_t hi = min(max((int64_t)a.cu_q[b + 1], lo), a.total_q);
+    r.r0 = lo;
+    r.n = (int)min(hi - lo, (int64_t)a.max_q);
+    r.p0 = min(max(a.q_pos0[b], 0), a.max_kv - 1);
+    return r;
+}
+
+// s_waitcnt vmcnt(V) with expcnt and lgkmcnt left free (gfx9 encoding).
+template <int V>
+__device__ __forceinline__ void pf_wait_vm() {
+    __builtin_amdgcn_s_waitcnt((V & 15) | (7 << 4) | (15 << 8) | ((V >> 4) << 14));
+}
+
+// s_waitcnt lgkmcnt(min(N, 15)) (the counter has 4 bits; waiting for fewer
+// outstanding reads than asked is still safe), tied to the register `v` that
+// the caller is about to use, so no use of v can be scheduled before it.
+template <int N, class T>
+__device__ __forceinline__ void pf_wait_lgkm(T& v) {
+    constexpr int n = N < 15 ? N : 15;
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "n"(n));
+}
+// LDS fragment reads as inline assembly: the compiler would otherwise wait for
+// every copy still in flight into the ring (it cannot tell the stages apart)
+// before each read.  Their results are waited for explicitly (pf_wait_lgkm);
+// volatile asm statements keep their order, and LDS reads complete in order.
+template <int OFF>
+__device__ __forceinline__ u32x4_t pf_read128(uint32_t addr) {
+    u32x4_t r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+typedef uint32_t pf_u32x2_t __attribute__((ext_vector_type(2)));
+template <int OFF>
+__device__ __forceinline__ pf_u32x2_t pf_read_tr(uint32_t addr) {
+    pf_u32x2_t r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+template <int I, int N, class F>
+__device__ __forceinline__ void pf_static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        pf_static_for<I + 1, N>(f);
+    }
+}
+
+__device__ __forceinline__ int pf_swap23(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+
+template <int D, int OUT_BF16>
+__global__ void __launch_bounds__(PF_THREADS)
+prefill_chunk_kernel(PfArgs a) {
+    constexpr int ROWB = D * 2;                // bytes of one K or V row
+    constexpr int BLK = PF_KB * ROWB;          // one K (or V) block
+    constexpr int STAGE = 2 * BLK;
+    constexpr int NS = D / 16;                 // 16-wide d slices of S^T
+    constexpr int NDB = D / 32;                // 32-wide d blocks of O^T
+    static_assert(D == 128, "LDS swizzles below assume 256-byte rows");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[PF_NSTAGE * STAGE];
+    __shared__ int pids[PF_CHUNK];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hl = lane >> 5;
+
+    // Workgroup -> (chunk c, request b, tile t, head h); heads fastest, so
+    // that the round-robin dealing of workgroups to the 8 XCDs keeps every
+    // tile of a head on one XCD (its K and V shared in that L2); the causal
+    // tiles with the most keys first.
+    int wi = blockIdx.x;
+    const int h = wi % a.H;
+    wi /= a.H;
+    const int t = a.ntiles - 1 - wi % a.ntiles;
+    wi /= a.ntiles;
+    const int b = wi % a.B;
+    const int c = wi / a.B;
+
+    const PfReq rq = pf_request(a, b);
+    const int q_lo = t * PF_QT;
+    if (q_lo >= rq.n) return;
+    const int q_hi = min(q_lo + PF_QT, rq.n) - 1;
+    const int pos_hi = min(rq.p0 + q_hi, a.max_kv - 1);
+    const int kc0 = c * PF_CHUNK;
+    if (kc0 > pos_hi) return;
+    const int kend = min(kc0 + PF_CHUNK, pos_hi + 1);     // keys [kc0, kend)
+    const int nblk = (kend - kc0 + PF_KB - 1) / PF_KB;
+
+    // Page ids of the chunk's keys (ids outside the cache read page 0).
+    const int pfirst = kc0 >> a.log2p;
+    const int np = ((kend - 1) >> a.log2p) - pfirst + 1;
+    const int32_t* trow = a.table + (int64_t)b * a.max_pages + pfirst;
+    for (int i = tid; i < np; i += PF_THREADS) {
+        const int pg = trow[i];
+        pids[i] = (unsigned)pg < (unsigned)a.num_pages ? pg : 0;
+    }
+    __syncthreads();
+
+    // This lane's query (rows past the request read its last row and are
+    // not written) and the wave's position range.
+    const int wq0 = q_lo + 32 * wave;
+    const bool wave_on = wq0 < rq.n;
+    const int qi = wq0 + (lane & 31);
+    const bool q_ok = qi < rq.n;
+    const int64_t row = rq.r0 + min(qi, rq.n - 1);
+    const int pos = min(rq.p0 + min(qi, rq.n - 1), a.max_kv - 1);
+    const int wpos_lo = min(rq.p0 + min(wq0, rq.n - 1), a.max_kv - 1);
+    const int wpos_hi = min(rq.p0 + min(wq0 + 31, rq.n - 1), a.max_kv - 1);
+
+    // Q as the B operand of S^T: lane l holds q[l % 32][16s + 8 hl .. + 7].
+    u32x4_t qf[NS];
+    {
+        const uint16_t* qrow = a.q + (row * a.H + h) * D + 8 * hl;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) qf[s] = *(const u32x4_t*)(qrow + 16 * s);
+    }
+
+    // K block in LDS: row = key (256 bytes), 16-byte chunk c at c ^ (row & 15).
+    // V block: row rho holds key swap23(rho), chunk c at c ^ 4 (rho & 3).
+    const int pmask = (1 << a.log2p) - 1;
+    auto copy_block = [&](int j, int st) {
+        const int kbase = kc0 + j * PF_KB;
+        uint8_t* kdst = smem + st * STAGE;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int rho = 8 * wave + 4 * i + (lane >> 4);
+            const int p = lane & 15;
+            {
+                const int key = min(kbase + rho, kend - 1);
+                const int pg = pids[(key >> a.log2p) - pfirst];
+                const uint8_t* src = a.kc + ((((int64_t)pg * a.H + h) << a.log2p) + (key & pmask)) * ROWB +
+                                     ((p ^ (rho & 15)) << 4);
+                __builtin_amdgcn_global_load_lds((const void*)src, (pf_lds_t*)(kdst + (8 * wave + 4 * i) * ROWB),
+                                                 16, 0, 0);
+            }
+            {
+                const int key = min(kbase + pf_swap23(rho), kend - 1);
+                const int pg = pids[(key >> a.log2p) - pfirst];
+                const uint8_t* src = a.vc + ((((int64_t)pg * a.H + h) << a.log2p) + (key & pmask)) * ROWB +
+                                     ((p ^ (4 * (rho & 3))) << 4);
+                __builtin_amdgcn_global_load_lds((const void*)src,
+                                                 (pf_lds_t*)(kdst + BLK + (8 * wave + 4 * i) * ROWB), 16, 0, 0);
+            }
+        }
+    };
+
+    // Per-lane LDS offsets of the fragments.
+    //  K (srcA of S^T): row 32 kb + l % 32, chunk (2s + hl) ^ (l & 15).
+    //  V^T (srcA of O^T, transposing reads): within a 16-lane group g, lane li
+    //  addresses row 8 hl + (li >> 2) (+ 4 for the second half of the 8 keys,
+    //  + 16 per 16-key slice) and the 8 bytes of d block db at chunk
+    //  4 (db ^ (li >> 2)) + 2 (g & 1) + ((li & 3) >> 1), half li & 1.
+    uint32_t koff[NS], voff[NDB];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) koff[s] = (lane & 31) * ROWB + ((((2 * s) | hl) ^ (lane & 15)) << 4);
+    {
+        const int g = lane >> 4, li = lane & 15, z = li >> 2;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+            voff[db] = BLK + (8 * hl + z) * ROWB + ((4 * (db ^ z) + 2 * (g & 1) + ((li & 3) >> 1)) << 4) +
+                       (li & 1) * 8;
+    }
+
+    const uint32_t lds0 = (uint32_t)(size_t)((const __attribute__((address_space(3))) uint8_t*)smem);
+    float m_run = -INFINITY, l_run = 0.0f;
+    f32x16_t o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
+
+    copy_block(0, 0);
+    if (nblk > 1) copy_block(1, 1);
+    for (int j = 0; j < nblk; ++j) {
+        const int st = j % PF_NSTAGE;
+        // Copies of block j done (block j + 1's four may still fly), then
+        // every wave's: stage (j + 2) % 3 was last read in step j - 1.
+        if (j + 1 < nblk) pf_wait_vm<4>();
+        else              pf_wait_vm<0>();
+        __builtin_amdgcn_s_barrier();
+        if (j + 2 < nblk) copy_block(j + 2, (j + 2) % PF_NSTAGE);
+        const int kbase = kc0 + j * PF_KB;
+        if (!wave_on || kbase > wpos_hi) continue;        // every key masked for this wave
+        const uint32_t sb = lds0 + st * STAGE;
+
+        // S^T for the block's two 32-key halves: 2 x NS fragment reads, then
+        // the MFMAs as their reads land (LDS reads complete in order).
+        u32x4_t kf[2][NS];
+        uint32_t ka[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) ka[s] = sb + koff[s];
+        pf_static_for<0, 2 * NS>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            kf[i / NS][i % NS] = pf_read128<(i / NS) * 32 * ROWB>(ka[i % NS]);
+        });
+        f32x16_t sacc[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
+        pf_static_for<0, 2 * NS>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            pf_wait_lgkm<2 * NS - 1 - i>(kf[i / NS][i % NS]);
+            sacc[i / NS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[i / NS][i % NS]),
+                                                                   as_bf16x8(qf[i % NS]), sacc[i / NS], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        // The V^T fragments do not depend on the scores: issue their reads now.
+        pf_u32x2_t vf[NDB][4][2];
+        uint32_t va[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) va[db] = sb + voff[db];
+        pf_static_for<0, NDB * 8>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            constexpr int db = i / 8, u = (i / 2) % 4, hr = i % 2;
+            vf[db][u][hr] = pf_read_tr<u * 16 * ROWB + hr * 4 * ROWB>(va[db]);
+        });
+        // Scores in the base-2 domain; key of (kb, r): kbase + 32 kb + 8 (r >> 2) + 4 hl + (r & 3).
+        const bool need_mask = kbase + PF_KB - 1 > wpos_lo;
+        float mb = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float x = sacc[kb][r] * a.cscale;
+                if (need_mask) {
+                    const int key = kbase + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
+                    x = key <= pos ? x : -INFINITY;
+                }
+                sacc[kb][r] = x;
+                mb = fmaxf(mb, x);
+            }
+        mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+        const float m_new = fmaxf(m_run, mb);
+        const bool dead = m_new == -INFINITY;                // no key of the chunk so far
+        const float alpha = dead ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        // P as two bfloat16 terms, hi = bf16(p) and lo = bf16(p - hi): their
+        // products with the bfloat16 V are exact in the binary32 MFMA sums, so
+        // P V carries p to about 2^-17 instead of bfloat16's 2^-9.
+        float ps = 0.0f;
+        u32x4_t pb[4], pl[4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float p0 = dead ? 0.0f : __builtin_amdgcn_exp2f(sacc[kb][r] - m_new);
+                const float p1 = dead ? 0.0f : __builtin_amdgcn_exp2f(sacc[kb][r + 1] - m_new);
+                ps += p0;
+                ps += p1;
+                const uint32_t hi = pack_bf16x2(p0, p1);
+                pb[2 * kb + (r >> 3)][(r & 7) >> 1] = hi;
+                pl[2 * kb + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0 - bf16lo_to_f32(hi), p1 - bf16hi_to_f32(hi));
+            }
+        l_run = l_run * alpha + ps;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        // O^T += V^T P^T over the 4 slices of 16 keys.
+        pf_static_for<0, NDB * 4>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            constexpr int db = i / 4, u = i % 4;
+            pf_wait_lgkm<(NDB * 4 - 1 - i) * 2>(vf[db][u][1]);
+            pf_wait_lgkm<(NDB * 4 - 1 - i) * 2>(vf[db][u][0]);
+            const u32x4_t v = {vf[db][u][0][0], vf[db][u][0][1], vf[db][u][1][0], vf[db][u][1][1]};
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(v), as_bf16x8(pb[u]), o[db], 0, 0, 0);
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(v), as_bf16x8(pl[u]), o[db], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    }
+
+    // ---- results of this chunk for the queries that have keys in it
+    if (!wave_on) return;
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    if (!q_ok || pos < kc0) return;
+    const int nch = pos / PF_CHUNK + 1;
+    if (nch == 1) {
+        // out[row][h][d], d = 32 db + 8 (r >> 2) + 4 hl + (r & 3).
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int64_t e = (row * a.H + h) * D + 32 * db + 8 * g + 4 * hl;
+                f32x4_t v;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) v[k] = o[db][4 * g + k] / l_tot;
+                if constexpr (OUT_BF16) {
+                    typedef uint32_t u32x2_t_ __attribute__((ext_vector_type(2)));
+                    *(u32x2_t_*)((uint16_t*)a.out + e) = u32x2_t_{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                } else {
+                    *(f32x4_t*)((float*)a.out + e) = v;
+                }
+            }
+    } else {
+        const int64_t tq = a.total_q;
+        float* w = a.ws + ((int64_t)c * a.H + h) * (2 + D) * tq + row;
+        if (hl == 0) {
+            w[0] = m_run;
+            w[tq] = l_tot;
+        }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) w[(2 + 32 * db + 8 * (r >> 2) + 4 * hl + (r & 3)) * tq] = o[db][r];
+    }
+}
+
+// Merge of the chunk triples of the queries with more than one chunk (one
+// thread per query of a 256-query tile of one head), in ascending chunk order:
+// M = max m_c, den = sum 2^(m_c - M) l_c, num_d = sum 2^(m_c - M) o_c[d].
+template <int D, int OUT_BF16>
+__global__ void __launch_bounds__(256)
+prefill_merge_kernel(PfArgs a) {
+    int wi = blockIdx.x;
+    const int h = wi % a.H;
+    wi /= a.H;
+    const int t = wi % a.ntiles;
+    const int b = wi / a.ntiles;
+    const PfReq rq = pf_request(a, b);
+    const int qi = t * PF_QT + threadIdx.x;
+    if (qi >= rq.n) return;
+    const int pos = min(rq.p0 + qi, a.max_kv - 1);
+    const int nch = pos / PF_CHUNK + 1;
+    if (nch == 1) return;
+    const int64_t row = rq.r0 + qi, tq = a.total_q;
+    const int64_t cstride = (int64_t)a.H * (2 + D) * tq;
+    const float* w = a.ws + (int64_t)h * (2 + D) * tq + row;
+    float M = -INFINITY;
+    for (int c = 0; c < nch; ++c) M = fmaxf(M, w[c * cstride]);
+    float num[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) num[d] = 0.0f;
+    float den = 0.0f;
+    for (int c = 0; c < nch; ++c) {
+        const float* wc = w + c * cstride;
+        const float f = __builtin_amdgcn_exp2f(wc[0] - M);
+        den = fmaf(f, wc[tq], den);
+#pragma unroll
+        for (int d = 0; d < D; ++d) num[d] = fmaf(f, wc[(2 + d) * tq], num[d]);
+    }
+    const int64_t e = (row * a.H + h) * D;
+#pragma unroll
+    for (int d = 0; d < D; d += 4) {
+        f32x4_t v;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = num[d + k] / den;
+        if constexpr (OUT_BF16) {
+            typedef uint32_t u32x2_t_ __attribute__((ext_vector_type(2)));
+            *(u32x2_t_*)((uint16_t*)a.out + e + d) = u32x2_t_{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        } else {
+            *(f32x4_t*)((float*)a.out + e + d) = v;
+        }
+    }
+}
+
+}  // namespace bi

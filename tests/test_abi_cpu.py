@@ -64,6 +64,10 @@ def bi():
     L.bi_decode_attn_paged_workspace_bytes.argtypes = [i64] * 4
     L.bi_decode_attn_paged.argtypes = [i64, i64, i64, vp, vp, vp, i64, i64, vp, i64, vp, i64, vp,
                                        ctypes.c_float, vp, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, vp]
+    L.bi_prefill_attn_paged_workspace_bytes.restype = ctypes.c_size_t
+    L.bi_prefill_attn_paged_workspace_bytes.argtypes = [i64] * 4
+    L.bi_prefill_attn_paged.argtypes = [i64, i64, i64, vp, i64, vp, vp, i64, vp, vp, i64, i64, vp, i64, i64, vp,
+                                        ctypes.c_float, vp, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, vp]
     L.bi_softmax_rows.argtypes = [i64, i64, vp, i64, ctypes.c_float, vp, i64, ctypes.c_int, vp]
     L.bi_rms_norm.argtypes = [i64, i64, vp, i64, vp, ctypes.c_float, vp, i64, ctypes.c_int, ctypes.c_int, vp]
     L.bi_log_softmax_rows.argtypes = [i64, i64, vp, i64, vp, i64, ctypes.c_int, ctypes.c_int, vp]
@@ -178,6 +182,28 @@ def test_paged_decode_workspace_size_and_validation(bi):
     assert dec(ws=None) == WS and dec(ws_bytes=100) == WS
     assert dec(kc=P + 8) == LAYOUT and dec(bt=P + 2) == LAYOUT
     assert dec(B=0) == OK and dec(H=0) == OK
+
+
+def test_prefill_workspace_size_and_validation(bi):
+    assert bi.bi_prefill_attn_paged_workspace_bytes(1000, 8, 4096, 128) == 0       # one chunk: none
+    assert bi.bi_prefill_attn_paged_workspace_bytes(1000, 8, 4097, 128) == 2 * 8 * 130 * 1000 * 4
+
+    def pf(**kw):
+        a = dict(B=2, H=2, D=128, q=P, total_q=64, cu=P, p0=P, max_q=32, kc=P, vc=P, num_pages=64,
+                 page=16, bt=P, max_pages=32, max_kv=512, out=P, scale=0.1, ws=P, ws_bytes=0,
+                 ind=BF16, outd=F32)
+        a.update(kw)
+        return bi.bi_prefill_attn_paged(*a.values(), None)
+
+    assert pf(ind=F32) == DTYPE and pf(outd=3) == DTYPE
+    assert pf(page=24) == SHAPE and pf(max_kv=513) == SHAPE and pf(max_q=0) == SHAPE
+    assert pf(total_q=-1) == SHAPE and pf(num_pages=0) == SHAPE
+    assert pf(D=64) == UNSUP
+    assert pf(cu=None) == NULL and pf(bt=None) == NULL and pf(out=None) == NULL
+    assert pf(out=P + 8) == LAYOUT and pf(q=P + 4) == LAYOUT and pf(p0=P + 2) == LAYOUT
+    assert pf(max_kv=5000, max_pages=400) == WS                       # two chunks need ws
+    assert pf(max_kv=5000, max_pages=400, ws=P + 8, ws_bytes=1 << 20) == WS    # 16-byte aligned ws
+    assert pf(B=0) == OK and pf(total_q=0) == OK
 
 
 def test_softmax_validation(bi):
