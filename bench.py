@@ -212,6 +212,7 @@ def main():
     out["invariance_cost"] = invariance_cost(Wd, bd, x0, dq, dk, dv, Y)
     out["row_ops"] = row_ops(X, Y)
     out["paged_decode"] = paged_decode(dq, dk, dv, dout)
+    out["prefill"] = prefill()
 
     del X, Y, Q, Kt, V, Sb, Pb, Ob, dq, dk, dv
     torch.cuda.empty_cache()
@@ -346,6 +347,30 @@ def paged_decode(dq, dk, dv, dout):
             res[name]["bits_equal_contiguous"] = bool(torch.equal(o.view(torch.int32), dout.view(torch.int32)))
     del kc, vc
     return res
+
+
+def prefill():
+    """Untimed extra: causal prefill attention over a paged cache (KV split at
+    4096 tokens), one 8192-token prompt, 32 heads, D = 128, 16-token pages;
+    flops = 4 * D * H * T(T+1)/2 (the two products over the causal pairs; the
+    second product's two bfloat16 terms of P are not counted)."""
+    import torch
+
+    import synth
+    from invariant_persistent_bf16_amd import bi
+
+    T, H, D = 8192, 32, 128
+    dev = torch.device("cuda:0")
+    q, cu, p0, kc, vc, bt = synth.paged_prefill_inputs([0], [T], H=H, D=D, P=16, seed=31, device=dev)
+    o = torch.empty(T, H, D, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(bi.bi_prefill_attn_paged_workspace_bytes(T, H, T, D) // 4, dtype=torch.float32, device=dev)
+    t = _time_ms(lambda: bi.bi_prefill_attn_paged(q, cu, p0, T, kc, vc, bt, T, 1 / math.sqrt(D), out=o,
+                                                  out_dtype=bi.BI_BF16, workspace=ws), iters=10)
+    flops = 4 * D * H * T * (T + 1) / 2
+    tf = flops / (t * 1e-3) / 1e12
+    del q, kc, vc, o, ws
+    return {"config": "B=1 T=8192 H=32 D=128 P=16 causal, bf16 out", "us": round(t * 1e3, 1),
+            "TFLOP/s": round(tf, 1), "frac_bf16_peak": round(tf / (PEAK_BF16_TFLOPS), 4)}
 
 
 def gemm_traffic(path):

@@ -493,7 +493,7 @@ int bi_decode_attn_paged(int64_t B, int64_t H, int64_t D, const void* q, const v
 size_t bi_prefill_attn_paged_workspace_bytes(int64_t total_q, int64_t H, int64_t max_kv_len, int64_t D) {
     if (total_q < 0 || H < 0 || max_kv_len < 1 || D < 1) return 0;
     const int64_t nch = cdiv(max_kv_len, PF_CHUNK);
-    return nch > 1 ? (size_t)(nch * H * (2 + D) * total_q * 4) : 0;
+    return nch > 1 ? (size_t)(nch * H * (4 + D) * total_q * 4) : 0;
 }
 
 int bi_prefill_attn_paged(int64_t B, int64_t H, int64_t D, const void* q, int64_t total_q,
@@ -519,7 +519,7 @@ int bi_prefill_attn_paged(int64_t B, int64_t H, int64_t D, const void* q, int64_
     // Positions, in-page offsets and page ids are 32-bit; row offsets 64-bit.
     if (maxchunks * B * ntiles * H > (1ll << 31) - 1 || max_q > (1ll << 30) || H > (1 << 20) ||
         max_kv_len + PF_CHUNK >= (1ll << 31) || page_size * D * 2 >= (1ll << 31) ||
-        num_pages > (1ll << 31) - 1 || B > (1 << 30) || total_q * H * D > (1ll << 46))
+        num_pages > (1ll << 31) - 1 || B > (1 << 30) || cdiv(total_q * H * (D / 4), 256) > (1ll << 31) - 1)
         return BI_ERR_UNSUPPORTED;
     const size_t need = bi_prefill_attn_paged_workspace_bytes(total_q, H, max_kv_len, D);
     if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 16))) return BI_ERR_WORKSPACE;
@@ -549,7 +549,7 @@ int bi_prefill_attn_paged(int64_t B, int64_t H, int64_t D, const void* q, int64_
     if (out_dtype == BI_BF16) hipLaunchKernelGGL((prefill_chunk_kernel<128, 1>), g1, dim3(PF_THREADS), 0, st, a);
     else                      hipLaunchKernelGGL((prefill_chunk_kernel<128, 0>), g1, dim3(PF_THREADS), 0, st, a);
     if (maxchunks > 1) {
-        const dim3 g2((unsigned)(B * ntiles * H));
+        const dim3 g2((unsigned)cdiv(total_q * H * (D / 4), 256));
         if (out_dtype == BI_BF16) hipLaunchKernelGGL((prefill_merge_kernel<128, 1>), g2, dim3(256), 0, st, a);
         else                      hipLaunchKernelGGL((prefill_merge_kernel<128, 0>), g2, dim3(256), 0, st, a);
     }

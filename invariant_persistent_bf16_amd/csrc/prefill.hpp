@@ -37,7 +37,7 @@
 //     with bits 2 and 3 of the key index swapped.
 // A query with one chunk (pos < 4096) writes out = o / l itself (the merge of
 // one triple gives these bits); others write their triples to ws
-// [chunk][H][2 + D][total_q], and kernel 2 merges them.
+// [chunk][H][total_q][4 + D], and kernel 2 merges them.
 #pragma once
 
 #include <type_traits>
@@ -332,10 +332,13 @@ prefill_chunk_kernel(PfArgs a) {
                 pl[2 * kb + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0 - bf16lo_to_f32(hi), p1 - bf16hi_to_f32(hi));
             }
         l_run = l_run * alpha + ps;
+        // o * 1 = o: skip the rescale when no query of the wave raised its maximum.
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        }
         // O^T += V^T P^T over the 4 slices of 16 keys.
         pf_static_for<0, NDB * 4>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
@@ -372,64 +375,69 @@ prefill_chunk_kernel(PfArgs a) {
                 }
             }
     } else {
-        const int64_t tq = a.total_q;
-        float* w = a.ws + ((int64_t)c * a.H + h) * (2 + D) * tq + row;
-        if (hl == 0) {
-            w[0] = m_run;
-            w[tq] = l_tot;
-        }
+        // Triple row [m, l, -, -, o[0 .. D)] of this (chunk, head, query).
+        float* w = a.ws + (((int64_t)c * a.H + h) * a.total_q + row) * (4 + D);
+        if (hl == 0) *(f32x4_t*)w = f32x4_t{m_run, l_tot, 0.0f, 0.0f};
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) w[(2 + 32 * db + 8 * (r >> 2) + 4 * hl + (r & 3)) * tq] = o[db][r];
+            for (int g = 0; g < 4; ++g)
+                *(f32x4_t*)(w + 4 + 32 * db + 8 * g + 4 * hl) =
+                    f32x4_t{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
     }
 }
 
-// Merge of the chunk triples of the queries with more than one chunk (one
-// thread per query of a 256-query tile of one head), in ascending chunk order:
-// M = max m_c, den = sum 2^(m_c - M) l_c, num_d = sum 2^(m_c - M) o_c[d].
+// Merge of the chunk triples of the queries with more than one chunk, in
+// ascending chunk order: M = max m_c, den = sum 2^(m_c - M) l_c,
+// num_d = sum 2^(m_c - M) o_c[d], out_d = num_d / den.  One thread per (query
+// row, head, 4 consecutive d); the request of a row is found by bisection of
+// cu_q.  Triple rows are [m, l, -, -, o[0 .. D)] (ws [chunk][H][total_q][4 + D]).
 template <int D, int OUT_BF16>
 __global__ void __launch_bounds__(256)
 prefill_merge_kernel(PfArgs a) {
-    int wi = blockIdx.x;
-    const int h = wi % a.H;
-    wi /= a.H;
-    const int t = wi % a.ntiles;
-    const int b = wi / a.ntiles;
-    const PfReq rq = pf_request(a, b);
-    const int qi = t * PF_QT + threadIdx.x;
-    if (qi >= rq.n) return;
-    const int pos = min(rq.p0 + qi, a.max_kv - 1);
+    constexpr int Q4 = D / 4;
+    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (i >= a.total_q * a.H * Q4) return;
+    const int d4 = (int)(i % Q4);
+    const int64_t rh = i / Q4;
+    const int h = (int)(rh % a.H);
+    const int64_t row = rh / a.H;
+    // request of this row: the last b with cu_q[b] <= row (clamped as in kernel 1)
+    int lo = 0, hi = a.B - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (min(max((int64_t)a.cu_q[mid], (int64_t)0), a.total_q) <= row) lo = mid;
+        else hi = mid - 1;
+    }
+    const PfReq rq = pf_request(a, lo);
+    const int64_t qi = row - rq.r0;
+    if (qi < 0 || qi >= rq.n) return;
+    const int pos = min(rq.p0 + (int)qi, a.max_kv - 1);
     const int nch = pos / PF_CHUNK + 1;
     if (nch == 1) return;
-    const int64_t row = rq.r0 + qi, tq = a.total_q;
-    const int64_t cstride = (int64_t)a.H * (2 + D) * tq;
-    const float* w = a.ws + (int64_t)h * (2 + D) * tq + row;
+    const int64_t cstride = (int64_t)a.H * a.total_q * (4 + D);
+    const float* w = a.ws + ((int64_t)h * a.total_q + row) * (4 + D);
     float M = -INFINITY;
     for (int c = 0; c < nch; ++c) M = fmaxf(M, w[c * cstride]);
-    float num[D];
-#pragma unroll
-    for (int d = 0; d < D; ++d) num[d] = 0.0f;
+    f32x4_t num = {0.0f, 0.0f, 0.0f, 0.0f};
     float den = 0.0f;
     for (int c = 0; c < nch; ++c) {
         const float* wc = w + c * cstride;
         const float f = __builtin_amdgcn_exp2f(wc[0] - M);
-        den = fmaf(f, wc[tq], den);
+        den = fmaf(f, wc[1], den);
+        const f32x4_t ov = *(const f32x4_t*)(wc + 4 + 4 * d4);
 #pragma unroll
-        for (int d = 0; d < D; ++d) num[d] = fmaf(f, wc[(2 + d) * tq], num[d]);
+        for (int k = 0; k < 4; ++k) num[k] = fmaf(f, ov[k], num[k]);
     }
-    const int64_t e = (row * a.H + h) * D;
+    f32x4_t v;
 #pragma unroll
-    for (int d = 0; d < D; d += 4) {
-        f32x4_t v;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = num[d + k] / den;
-        if constexpr (OUT_BF16) {
-            typedef uint32_t u32x2_t_ __attribute__((ext_vector_type(2)));
-            *(u32x2_t_*)((uint16_t*)a.out + e + d) = u32x2_t_{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        } else {
-            *(f32x4_t*)((float*)a.out + e + d) = v;
-        }
+    for (int k = 0; k < 4; ++k) v[k] = num[k] / den;
+    const int64_t e = (row * a.H + h) * D + 4 * d4;
+    if constexpr (OUT_BF16) {
+        typedef uint32_t u32x2_t_ __attribute__((ext_vector_type(2)));
+        *(u32x2_t_*)((uint16_t*)a.out + e) = u32x2_t_{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    } else {
+        *(f32x4_t*)((float*)a.out + e) = v;
     }
 }
 

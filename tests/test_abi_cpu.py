@@ -186,7 +186,7 @@ def test_paged_decode_workspace_size_and_validation(bi):
 
 def test_prefill_workspace_size_and_validation(bi):
     assert bi.bi_prefill_attn_paged_workspace_bytes(1000, 8, 4096, 128) == 0       # one chunk: none
-    assert bi.bi_prefill_attn_paged_workspace_bytes(1000, 8, 4097, 128) == 2 * 8 * 130 * 1000 * 4
+    assert bi.bi_prefill_attn_paged_workspace_bytes(1000, 8, 4097, 128) == 2 * 8 * 132 * 1000 * 4
 
     def pf(**kw):
         a = dict(B=2, H=2, D=128, q=P, total_q=64, cu=P, p0=P, max_q=32, kc=P, vc=P, num_pages=64,
