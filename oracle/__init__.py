@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 _i64 = ctypes.c_int64
 _vp = ctypes.c_void_p
 _dp = ctypes.POINTER(ctypes.c_double)
@@ -43,7 +43,9 @@ def _dt(t):
         return F32
     if t.dtype == torch.bfloat16:
         return BF16
-    raise TypeError(f"oracle takes float32 or bfloat16 tensors, got {t.dtype}")
+    if t.dtype == torch.float16:
+        return F16
+    raise TypeError(f"oracle takes float32, bfloat16 or float16 tensors, got {t.dtype}")
 
 
 def _cpu(t):
@@ -82,7 +84,7 @@ def bf16_rne_array(a):
 
 
 def widen(t, i):
-    """Exact value of element i of a float32 / bfloat16 tensor."""
+    """Exact value of element i of a float32 / bfloat16 / float16 tensor."""
     return _load().oracle_widen(_ptr(t), _dt(t), i)
 
 

@@ -50,9 +50,23 @@
 
 #define OR_F32 0
 #define OR_BF16 1
+#define OR_F16 2
 
 /* bfloat16 is the top half of a binary32: widen by placing the 16 bits high. */
+/* IEEE binary16 bits -> its exact value: sign, 5-bit exponent (bias 15),
+ * 10-bit fraction; exponent 0 is subnormal (fraction * 2^-24), exponent 31 is
+ * infinity (fraction 0) or NaN. */
+static double f16_value(uint16_t h) {
+    const int s = h >> 15, e = (h >> 10) & 31, f = h & 1023;
+    double v;
+    if (e == 0) v = ldexp((double)f, -24);
+    else if (e == 31) v = f ? NAN : INFINITY;
+    else v = ldexp((double)(1024 + f), e - 25);
+    return s ? -v : v;
+}
+
 static double widen(const void* p, int dtype, int64_t i) {
+    if (dtype == OR_F16) return f16_value(((const uint16_t*)p)[i]);
     if (dtype == OR_BF16) {
         uint32_t u = ((uint32_t)((const uint16_t*)p)[i]) << 16;
         float f;
@@ -117,8 +131,8 @@ void oracle_bmm(int64_t G, int64_t M, int64_t N, int64_t K,
     int64_t ns = slices ? nslices : G;
     for (int64_t s = 0; s < ns; ++s) {
         int64_t g = slices ? slices[s] : s;
-        const char* a = (const char*)A + (size_t)(g * sAg) * (dtype == OR_BF16 ? 2 : 4);
-        const char* b = (const char*)B + (size_t)(g * sBg) * (dtype == OR_BF16 ? 2 : 4);
+        const char* a = (const char*)A + (size_t)(g * sAg) * (dtype == OR_F32 ? 4 : 2);
+        const char* b = (const char*)B + (size_t)(g * sBg) * (dtype == OR_F32 ? 4 : 2);
         oracle_mm(M, N, K, a, sAm, sAk, b, sBk, sBn, NULL, dtype, NULL, 0, C + s * M * N);
     }
 }
