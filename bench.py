@@ -213,6 +213,7 @@ def main():
     out["row_ops"] = row_ops(X, Y)
     out["paged_decode"] = paged_decode(dq, dk, dv, dout)
     out["prefill"] = prefill()
+    out["f16_addmm"] = f16_addmm(W, bias, X, Y)
 
     del X, Y, Q, Kt, V, Sb, Pb, Ob, dq, dk, dv
     torch.cuda.empty_cache()
@@ -347,6 +348,23 @@ def paged_decode(dq, dk, dv, dout):
             res[name]["bits_equal_contiguous"] = bool(torch.equal(o.view(torch.int32), dout.view(torch.int32)))
     del kc, vc
     return res
+
+
+def f16_addmm(W, bias, X, Y):
+    """Untimed extra: the fp16 configuration of the same addmm (M=8192, K=4096,
+    N=14336, fp16 operands and output; the workload's values converted to fp16)."""
+    import torch
+
+    from invariant_persistent_bf16_amd import bi
+
+    dev = X.device
+    Wh, bh, Xh = W.to(dev, torch.float16), bias.to(dev, torch.float16), X.to(torch.float16)
+    Yh = torch.empty(Y.shape, dtype=torch.float16, device=dev)
+    t = _time_ms(lambda: bi.bi_addmm(bh, Xh, Wh, out=Yh, out_dtype=bi.BI_F16), iters=20)
+    M, K, N = ADDMM["M"], ADDMM["K"], ADDMM["N"]
+    tf = 2 * M * N * K / (t * 1e-3) / 1e12
+    del Wh, Xh, Yh
+    return {"ms": round(t, 4), "TFLOP/s": round(tf, 1), "frac_f16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
 
 
 def prefill():

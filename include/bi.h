@@ -24,8 +24,9 @@
  *   - Ownership: the caller owns every buffer, outputs and workspaces
  *     included.  The library allocates no device memory and keeps no mutable
  *     global state (it caches the read-only compute-unit count per device).
- *   - Dtypes: BI_F32 = IEEE binary32, BI_BF16 = bfloat16.  Accumulation is
- *     always binary32.  bfloat16 outputs are the binary32 result rounded to
+ *   - Dtypes: BI_F32 = IEEE binary32, BI_BF16 = bfloat16, BI_F16 = IEEE
+ *     binary16 (the matmul family and the convolution only).  Accumulation is
+ *     always binary32.  16-bit outputs are the binary32 result rounded to
  *     nearest-even, bit for bit the same as rounding the BI_F32 output.
  *   - Errors: arguments are checked on the host before anything is enqueued;
  *     a negative bi_status is returned and nothing runs.  A failed launch
@@ -43,7 +44,7 @@
 extern "C" {
 #endif
 
-typedef enum { BI_F32 = 0, BI_BF16 = 1 } bi_dtype;
+typedef enum { BI_F32 = 0, BI_BF16 = 1, BI_F16 = 2 } bi_dtype;
 
 typedef enum {
     BI_OK = 0,
@@ -67,12 +68,16 @@ const char* bi_status_string(int status);
  *
  * A: element (i,k) at A[i*sAm + k*sAk]; B: (k,j) at B[k*sBk + j*sBn];
  * C: (i,j) at C[i*sCm + j*sCn].  in_dtype is the dtype of A and B,
- * out_dtype the dtype of C.
+ * out_dtype the dtype of C: BI_F32, or the 16-bit in_dtype (BI_BF16 is also
+ * accepted for BI_F32 operands).  BI_F16 operands run the bfloat16 kernel's
+ * tile, K order and schedule on the binary16 matrix-core instruction: one
+ * fixed configuration per dtype, as the source's per-dtype table (whose fp16
+ * entry is a wider tile for its hardware).
  * Reduction: k ascending in fixed steps of the dtype's K tile; each output
  * tile is owned by one workgroup from the first k to the last (no split-K,
  * no atomics).  Row i of C depends only on row i of A, B, K and the dtypes.
  * Layout accepted:
- *   BI_BF16: sAk == 1, sAm % 8 == 0, A 16-byte aligned, K % 8 == 0;
+ *   BI_BF16, BI_F16: sAk == 1, sAm % 8 == 0, A 16-byte aligned, K % 8 == 0;
  *            B either K-contiguous (sBk == 1, sBn % 8 == 0) or N-contiguous
  *            (sBn == 1, sBk % 8 == 0, N % 8 == 0), 16-byte aligned;
  *            C with sCn == 1.
@@ -92,7 +97,7 @@ int bi_mm(int64_t M, int64_t N, int64_t K,
  * rounded once to out_dtype.  bias == NULL gives bi_mm.
  * Source: as bi_mm; the wrapper's bias argument and the addmm override in
  * "Integration with PyTorch: The torch.Library Approach".
- * Layout rules: as bi_mm; bias is contiguous and, for BI_BF16, 16-byte aligned.
+ * Layout rules: as bi_mm; bias is contiguous and aligned to its element.
  */
 int bi_addmm(int64_t M, int64_t N, int64_t K,
              const void* A, int64_t sAm, int64_t sAk,
@@ -108,7 +113,7 @@ int bi_addmm(int64_t M, int64_t N, int64_t K,
  * and the same ordered K reduction, so adding elements adds independent work.
  * Slice g of the result is bit-identical to bi_mm on A[g], B[g] alone.
  * Element strides sAg, sBg, sCg step between slices (0 broadcasts an operand).
- * Layout rules per slice: as bi_mm, and for BI_BF16 sAg % 8 == sBg % 8 == 0.
+ * Layout rules per slice: as bi_mm, and for 16-bit dtypes sAg % 8 == sBg % 8 == 0.
  */
 int bi_bmm(int64_t G, int64_t M, int64_t N, int64_t K,
            const void* A, int64_t sAg, int64_t sAm, int64_t sAk,
@@ -129,7 +134,8 @@ int bi_bmm(int64_t G, int64_t M, int64_t N, int64_t K,
  * x [N, Cin, H, W] contiguous; w [Cout, Cin/groups, Kh, Kw] contiguous;
  * bias [Cout] or NULL; y [N, Cout, OH, OW] contiguous with
  * OH = (H + 2*ph - dh*(Kh-1) - 1)/sh + 1 (and OW likewise).
- * x, w, bias are in_dtype (BI_BF16 or BI_F32); y is out_dtype.
+ * x, w, bias are in_dtype (BI_BF16, BI_F16 or BI_F32); y is out_dtype (as
+ * bi_mm).
  * ws: device workspace of at least bi_conv2d_workspace_bytes(...) bytes,
  * 256-byte aligned, owned by the caller, contents undefined on return.
  * Errors: BI_ERR_SHAPE if Cin or Cout is not divisible by groups or the

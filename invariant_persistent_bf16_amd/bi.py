@@ -13,7 +13,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbi.so")
 
-BI_F32, BI_BF16 = 0, 1
+BI_F32, BI_BF16, BI_F16 = 0, 1, 2
 _i64, _vp, _int, _f32, _sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 
 _SIGS = {
@@ -79,11 +79,13 @@ def _dt(t):
         return BI_F32
     if t.dtype == torch.bfloat16:
         return BI_BF16
+    if t.dtype == torch.float16:
+        return BI_F16
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
 def _tdt(code):
-    return torch.float32 if code == BI_F32 else torch.bfloat16
+    return {BI_F32: torch.float32, BI_BF16: torch.bfloat16, BI_F16: torch.float16}[code]
 
 
 def _p(t):

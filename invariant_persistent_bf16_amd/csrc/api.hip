@@ -46,9 +46,18 @@ static inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % 
 static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // ------------------------------------------------------------------- GEMM
+// Output dtypes: binary32 always; bfloat16 for bfloat16 or binary32 operands;
+// binary16 for binary16 operands.
+static bool gemm_out_ok(int in, int out) {
+    if (out == BI_F32) return true;
+    if (out == BI_BF16) return in == BI_BF16 || in == BI_F32;
+    if (out == BI_F16) return in == BI_F16;
+    return false;
+}
+
 int gemm_check(const GemmDesc& d) {
-    if (d.in_dtype != BI_F32 && d.in_dtype != BI_BF16) return BI_ERR_DTYPE;
-    if (d.out_dtype != BI_F32 && d.out_dtype != BI_BF16) return BI_ERR_DTYPE;
+    if (d.in_dtype != BI_F32 && d.in_dtype != BI_BF16 && d.in_dtype != BI_F16) return BI_ERR_DTYPE;
+    if (!gemm_out_ok(d.in_dtype, d.out_dtype)) return BI_ERR_DTYPE;
     if (d.G1 < 0 || d.G2 < 1 || d.M < 0 || d.N < 0 || d.K < 0) return BI_ERR_SHAPE;
     if (d.G1 == 0 || d.M == 0 || d.N == 0) return BI_OK;   // nothing to compute
     if (!d.C) return BI_ERR_NULL;
@@ -58,9 +67,9 @@ int gemm_check(const GemmDesc& d) {
     for (int64_t s : strides)
         if (s < 0) return BI_ERR_LAYOUT;
     if (d.sCn != 1) return BI_ERR_LAYOUT;
-    const int osz = d.out_dtype == BI_BF16 ? 2 : 4;
+    const int osz = d.out_dtype == BI_F32 ? 4 : 2;
     if (!aligned(d.C, osz)) return BI_ERR_LAYOUT;
-    if (d.in_dtype == BI_BF16) {
+    if (d.in_dtype != BI_F32) {
         if (d.K > 0) {
             if (d.K % 8 != 0) return BI_ERR_LAYOUT;
             if (d.sAk != 1 || (d.M > 1 && d.sAm % 8 != 0) || !aligned(d.A, 16)) return BI_ERR_LAYOUT;
@@ -82,8 +91,8 @@ int gemm_check(const GemmDesc& d) {
         if (d.K > 0 && (!aligned(d.A, 4) || !aligned(d.B, 4))) return BI_ERR_LAYOUT;
         if (d.bias && !aligned(d.bias, 4)) return BI_ERR_LAYOUT;
     }
-    const int64_t bm = d.in_dtype == BI_BF16 ? G16_BM : G32_BM;
-    const int64_t bn = d.in_dtype == BI_BF16 ? G16_BN : G32_BN;
+    const int64_t bm = d.in_dtype != BI_F32 ? G16_BM : G32_BM;
+    const int64_t bn = d.in_dtype != BI_F32 ? G16_BN : G32_BN;
     if (d.G1 > (1ll << 30) || d.G2 > (1ll << 30) || d.K > (1ll << 30)) return BI_ERR_UNSUPPORTED;
     const int64_t tiles = cdiv(d.M, bm) * cdiv(d.N, bn);
     const int64_t slices = d.G1 * d.G2;
@@ -100,7 +109,8 @@ int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override) {
     int rc = device_cu_count(&cus);
     if (rc != BI_OK) return rc;
     const bool out_bf16 = d.out_dtype == BI_BF16;
-    if (d.in_dtype == BI_BF16) {
+    if (d.in_dtype != BI_F32) {
+        const bool out16 = d.out_dtype != BI_F32;
         GemmParams p;
         p.A = (const uint16_t*)d.A; p.B = (const uint16_t*)d.B;
         p.bias = (const uint16_t*)d.bias; p.C = d.C;
@@ -115,18 +125,22 @@ int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override) {
         p.total_tiles = (int)(p.tiles_per_slice * d.G1 * d.G2);
         const int grid = grid_override > 0 ? grid_override : (p.total_tiles < cus ? p.total_tiles : cus);
         const bool kc = d.K == 0 || (d.sBk == 1 && (d.N == 1 || d.sBn % 8 == 0));
-        const int osz = out_bf16 ? 2 : 4;
+        const int osz = out16 ? 2 : 4;
         const int vel = 16 / osz;   // elements per 16-byte chunk
         const bool cvec = aligned(d.C, 16) && d.N % vel == 0 && d.sCm % vel == 0 && d.sC1 % vel == 0 &&
                           d.sC2 % vel == 0;
-        void (*kern)(GemmParams);
-        if (kc) {
-            if (out_bf16) kern = cvec ? gemm_bf16_persistent<true, 1, true> : gemm_bf16_persistent<true, 1, false>;
-            else          kern = cvec ? gemm_bf16_persistent<true, 0, true> : gemm_bf16_persistent<true, 0, false>;
-        } else {
-            if (out_bf16) kern = cvec ? gemm_bf16_persistent<false, 1, true> : gemm_bf16_persistent<false, 1, false>;
-            else          kern = cvec ? gemm_bf16_persistent<false, 0, true> : gemm_bf16_persistent<false, 0, false>;
-        }
+        typedef void (*Kern)(GemmParams);
+        // [f16][B K-contiguous][16-bit out][vector epilogue]
+        static const Kern kerns[2][2][2][2] = {
+            {{{gemm_bf16_persistent<false, 0, false>, gemm_bf16_persistent<false, 0, true>},
+              {gemm_bf16_persistent<false, 1, false>, gemm_bf16_persistent<false, 1, true>}},
+             {{gemm_bf16_persistent<true, 0, false>, gemm_bf16_persistent<true, 0, true>},
+              {gemm_bf16_persistent<true, 1, false>, gemm_bf16_persistent<true, 1, true>}}},
+            {{{gemm_bf16_persistent<false, 0, false, true>, gemm_bf16_persistent<false, 0, true, true>},
+              {gemm_bf16_persistent<false, 1, false, true>, gemm_bf16_persistent<false, 1, true, true>}},
+             {{gemm_bf16_persistent<true, 0, false, true>, gemm_bf16_persistent<true, 0, true, true>},
+              {gemm_bf16_persistent<true, 1, false, true>, gemm_bf16_persistent<true, 1, true, true>}}}};
+        const Kern kern = kerns[d.in_dtype == BI_F16][kc][out16][cvec];
         hipLaunchKernelGGL(kern, dim3(grid), dim3(G16_THREADS), 0, st, p);
     } else {
         GemmF32Params p;
@@ -174,7 +188,7 @@ GemmDesc bmm_desc(int64_t G, int64_t M, int64_t N, int64_t K,
 int conv_geometry(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout, int64_t Kh,
                   int64_t Kw, int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh,
                   int64_t dw, int64_t groups, int in_dtype, ConvGeom* g, size_t* ws_bytes) {
-    if (in_dtype != BI_F32 && in_dtype != BI_BF16) return BI_ERR_DTYPE;
+    if (in_dtype != BI_F32 && in_dtype != BI_BF16 && in_dtype != BI_F16) return BI_ERR_DTYPE;
     if (N < 0 || Cin < 1 || H < 1 || W < 1 || Cout < 1 || Kh < 1 || Kw < 1) return BI_ERR_SHAPE;
     if (sh < 1 || sw < 1 || dh < 1 || dw < 1 || ph < 0 || pw < 0 || groups < 1) return BI_ERR_SHAPE;
     if (Cin % groups != 0 || Cout % groups != 0) return BI_ERR_SHAPE;
@@ -187,7 +201,7 @@ int conv_geometry(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout, in
     c.cig = Cin / groups; c.cog = Cout / groups;
     c.Kg = c.cig * Kh * Kw;
     c.Kp = cdiv(c.Kg, 8) * 8;
-    const int64_t esz = in_dtype == BI_BF16 ? 2 : 4;
+    const int64_t esz = in_dtype == BI_F32 ? 4 : 2;
     const int64_t wbytes = cdiv(Cout * c.Kp * esz, 256) * 256;
     const int64_t ubytes = N * groups * c.L * c.Kp * esz;
     if (g) *g = c;
@@ -325,14 +339,14 @@ int bi_conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, const void* x, int64
     int rc = conv_geometry(N, Cin, H, W, Cout, Kh, Kw, sh, sw, ph, pw, dh, dw, groups, in_dtype,
                            &g, &need);
     if (rc != BI_OK) return rc;
-    if (out_dtype != BI_F32 && out_dtype != BI_BF16) return BI_ERR_DTYPE;
+    if (!gemm_out_ok(in_dtype, out_dtype)) return BI_ERR_DTYPE;
     if (N == 0) return BI_OK;
     if (!x || !w || !y) return BI_ERR_NULL;
     if (!ws) return BI_ERR_WORKSPACE;
     if (ws_bytes < need || !aligned(ws, 256)) return BI_ERR_WORKSPACE;
-    const int64_t esz = in_dtype == BI_BF16 ? 2 : 4;
+    const int64_t esz = in_dtype == BI_F32 ? 4 : 2;
     if (!aligned(x, esz) || !aligned(w, esz) || (bias && !aligned(bias, esz)) ||
-        !aligned(y, out_dtype == BI_BF16 ? 2 : 4))
+        !aligned(y, out_dtype == BI_F32 ? 4 : 2))
         return BI_ERR_LAYOUT;
     // The GEMM over (sample, group) slices: A = packed weight, B = unfold (K-contiguous).
     uint8_t* wp = (uint8_t*)ws;
@@ -365,7 +379,7 @@ int bi_conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, const void* x, int64
         g32.Kh = (int)Kh; g32.Kw = (int)Kw; g32.sh = (int)sh; g32.sw = (int)sw; g32.ph = (int)ph; g32.pw = (int)pw;
         g32.dh = (int)dh; g32.dw = (int)dw; g32.groups = (int)groups; g32.OW = (int)g.OW; g32.L = (int)g.L;
         g32.cig = (int)g.cig; g32.Kg = (int)g.Kg; g32.Kp = (int)g.Kp;
-        if (in_dtype == BI_BF16) {
+        if (in_dtype != BI_F32) {
             hipLaunchKernelGGL((conv_pack_weight32<uint16_t>), dim3(wgrid), dim3(256), 0, st,
                                (const uint16_t*)w, (uint16_t*)wp, g32);
             hipLaunchKernelGGL((conv_unfold32<uint16_t>), dim3(ugrid), dim3(256), 0, st,
@@ -376,7 +390,7 @@ int bi_conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, const void* x, int64
             hipLaunchKernelGGL((conv_unfold32<float>), dim3(ugrid), dim3(256), 0, st,
                                (const float*)x, (float*)u, g32);
         }
-    } else if (in_dtype == BI_BF16) {
+    } else if (in_dtype != BI_F32) {
         hipLaunchKernelGGL((conv_pack_weight<uint16_t>), dim3(wgrid), dim3(256), 0, st,
                            (const uint16_t*)w, (uint16_t*)wp, g);
         hipLaunchKernelGGL((conv_unfold<uint16_t>), dim3(ugrid), dim3(256), 0, st,

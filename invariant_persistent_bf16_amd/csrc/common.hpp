@@ -7,6 +7,7 @@
 namespace bi {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -27,6 +28,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ f16x8_t as_f16x8(u32x4_t v) { return __builtin_bit_cast(f16x8_t, v); }
 
 // Two binary32 values -> two bfloat16 (a in the low half), round to nearest
 // even.  gfx950's v_cvt_pk_bf16_f32; it agrees bit for bit with
@@ -36,6 +38,28 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     typedef float f32x2_t __attribute__((ext_vector_type(2)));
     const f32x2_t v = {a, b};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// Two binary32 values -> two IEEE binary16 (a in the low half), round to
+// nearest even (the language's conversion; overflow gives infinity).
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+    typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+__device__ __forceinline__ float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+// 16-bit element type of the matrix-core path: bfloat16 or binary16.
+template <bool F16>
+__device__ __forceinline__ uint32_t pack16x2(float a, float b) {
+    if constexpr (F16) return pack_f16x2(a, b);
+    else               return pack_bf16x2(a, b);
+}
+template <bool F16>
+__device__ __forceinline__ float h16_to_f32(uint16_t h) {
+    if constexpr (F16) return f16_to_f32(h);
+    else               return bf16_to_f32(h);
 }
 
 // Output element store in the requested dtype (0 = binary32, 1 = bfloat16).

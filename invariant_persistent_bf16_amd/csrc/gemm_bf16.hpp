@@ -153,7 +153,11 @@ struct G16Frags {
 
 // CVEC: C allows 16-byte row stores (C aligned to 16 bytes; N, sCm, sC1, sC2
 // multiples of 16 bytes' worth of elements); otherwise element stores.
-template <bool B_KCONTIG, int OUT_BF16, bool CVEC>
+// F16: binary16 operands (v_mfma_f32_32x32x16_f16, binary16 bias and 16-bit
+// output) instead of bfloat16; the same tile, K order and schedule, the
+// pages' fixed configuration per dtype.  OUT_BF16: 16-bit output in the
+// operands' type (else binary32).
+template <bool B_KCONTIG, int OUT_BF16, bool CVEC, bool F16 = false>
 __global__ void __launch_bounds__(G16_THREADS, 1)
 gemm_bf16_persistent(GemmParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[G16_LDS_BYTES];
@@ -310,7 +314,7 @@ gemm_bf16_persistent(GemmParams p) {
         if (bb) {
             const int64_t b0 = p.bias_rows ? m0 : n0;
             const int64_t nb = (p.bias_rows ? p.M : p.N) - b0;
-            const float b = bf16_to_f32(bb[b0 + min<int64_t>(tid, nb - 1)]);
+            const float b = h16_to_f32<F16>(bb[b0 + min<int64_t>(tid, nb - 1)]);
             if (p.bias_rows) brow_t = b;
             else             bcol_t = b;
         }
@@ -344,8 +348,12 @@ gemm_bf16_persistent(GemmParams p) {
             g16_static_for<0, 32>([&](auto ic) {
                 constexpr int i = decltype(ic)::value;
                 constexpr int kk = i / 16, im = (i / 4) % 4, in = i % 4;
-                acc[im][in] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    as_bf16x8(cur.b[kk][in]), as_bf16x8(cur.a[kk][im]), acc[im][in], 0, 0, 0);
+                if constexpr (F16)
+                    acc[im][in] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        as_f16x8(cur.b[kk][in]), as_f16x8(cur.a[kk][im]), acc[im][in], 0, 0, 0);
+                else
+                    acc[im][in] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        as_bf16x8(cur.b[kk][in]), as_bf16x8(cur.a[kk][im]), acc[im][in], 0, 0, 0);
                 constexpr int slot = g16_slot<B_KCONTIG>(i);
                 if constexpr (slot >= 0 && slot < 32) {
                     lds_read(nxt, std::integral_constant<int, (ST + 1) % 4>{}, std::integral_constant<int, slot>{});
@@ -452,7 +460,7 @@ gemm_bf16_persistent(GemmParams p) {
                                 const f32x4_t v = value(std::integral_constant<int, im>{}, qc);
                                 if constexpr (OUT_BF16) {
                                     const int c = in * 4 + g;
-                                    const v2u32_t w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                                    const v2u32_t w = {pack16x2<F16>(v[0], v[1]), pack16x2<F16>(v[2], v[3])};
                                     *(v2u32_t*)(stg + r * ROWB + ((c ^ (r & (NCH - 1))) << 4) + 8 * lh) = w;
                                 } else {
                                     const int c = in * 8 + 2 * g + lh;
@@ -480,7 +488,7 @@ gemm_bf16_persistent(GemmParams p) {
                             for (int j = 0; j < 4; ++j) {
                                 const uint32_t off = col + j < cols_valid ? (uint32_t)(vrow + (col + j) * ESZ) : G16_OOB;
                                 if constexpr (OUT_BF16)
-                                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pack_bf16x2(v[j], 0.0f), rsC,
+                                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pack16x2<F16>(v[j], 0.0f), rsC,
                                                                           (int)off, 0, 0);
                                 else
                                     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[j]), rsC, (int)off, 0, 0);

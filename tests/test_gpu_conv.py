@@ -78,7 +78,7 @@ CASES = [
 
 
 @pytest.mark.parametrize("case", CASES)
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
 def test_general_conv_parity(case, dtype):
     N, Cin, H, W, Cout, Kh, Kw, st, pd, dl, gr = case
     x = synth.randn((N, Cin, H, W), seed=30, dtype=dtype)
