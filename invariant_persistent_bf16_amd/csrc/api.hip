@@ -89,6 +89,8 @@ int gemm_check(const GemmDesc& d) {
         if (d.bias && !aligned(d.bias, 2)) return BI_ERR_LAYOUT;
     } else {
         if (d.K > 0 && (!aligned(d.A, 4) || !aligned(d.B, 4))) return BI_ERR_LAYOUT;
+        // k times the K stride is a 32-bit element offset.
+        if (d.K > 0 && (d.K * d.sAk >= (1ll << 31) || d.K * d.sBk >= (1ll << 31))) return BI_ERR_UNSUPPORTED;
         if (d.bias && !aligned(d.bias, 4)) return BI_ERR_LAYOUT;
     }
     const int64_t bm = d.in_dtype != BI_F32 ? G16_BM : G32_BM;
@@ -156,8 +158,13 @@ int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override) {
         p.total_tiles = (int)(p.tiles_per_slice * d.G1 * d.G2);
         const int cap = 4 * cus;
         const int grid = grid_override > 0 ? grid_override : (p.total_tiles < cap ? p.total_tiles : cap);
-        if (out_bf16) hipLaunchKernelGGL((gemm_f32_persistent<1>), dim3(grid), dim3(G32_THREADS), 0, st, p);
-        else          hipLaunchKernelGGL((gemm_f32_persistent<0>), dim3(grid), dim3(G32_THREADS), 0, st, p);
+        // The K tail variant only where K is not a multiple of the K step (the
+        // arithmetic of both is the same MFMA chain over the same zero-padded K).
+        const bool ktail = d.K % G32_BK != 0;
+        typedef void (*Kern32)(GemmF32Params);
+        static const Kern32 kerns32[2][2] = {{gemm_f32_persistent<0, false>, gemm_f32_persistent<0, true>},
+                                              {gemm_f32_persistent<1, false>, gemm_f32_persistent<1, true>}};
+        hipLaunchKernelGGL(kerns32[out_bf16][ktail], dim3(grid), dim3(G32_THREADS), 0, st, p);
     }
     return launch_status();
 }

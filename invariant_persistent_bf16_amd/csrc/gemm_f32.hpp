@@ -9,8 +9,16 @@
 // binary32 precision: nothing is rounded to a narrower type.
 //
 // Operands may have any element strides (the loads are scalar and coalesced
-// along whichever stride is 1), so transposed views need no copy.
+// along whichever stride is 1), so transposed views need no copy.  Loads run
+// three K steps ahead of their LDS store in four register sets, issued
+// unconditionally (past the last step they re-read it), so the compiler's
+// waits cover exactly the set being stored; the address of each element is
+// fixed per tile and a step adds a uniform offset.  Per step that leaves one
+// address add per load beside the 16 MFMAs (the K-tail variant, used only when
+// K is not a multiple of the step, clamps k per element and zeroes the tail).
 #pragma once
+
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -35,7 +43,7 @@ struct GemmF32Params {
     int bias_rows;      // 1: bias indexed by row (conv output channel), 0: by column
 };
 
-template <int OUT_BF16>
+template <int OUT_BF16, bool KTAIL>
 __global__ void __launch_bounds__(G32_THREADS)
 gemm_f32_persistent(GemmF32Params p) {
     // LDS holds A as [k][m] and B as [k][n] so that the 32 lanes feeding one
@@ -71,44 +79,69 @@ gemm_f32_persistent(GemmF32Params p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 
-        float ra[8], rb[8];
-        auto load_tile = [&](int kt) {
-            const int64_t k0 = (int64_t)kt * G32_BK;
+        // Loads run three K steps ahead of their LDS store: step j's operands
+        // go to register set j % 4, issued at the start of step j - 3.  Every
+        // step issues its loads (past the last step it re-reads the last one,
+        // unused), so the code is straight-line and each store waits only for
+        // its own set.  The K tail (k >= K, read from a clamped address)
+        // becomes zero at the store.
+        float ra[4][8], rb[4][8];
+        // Per element of the thread's share of a step: its address at k = 0 of
+        // the tile, fixed for the tile; a step adds the uniform k0 times the K
+        // stride.  KTAIL (K not a multiple of the step): the element's k is
+        // clamped to K - 1 (32-bit: the host bounds K times the strides below
+        // 2^31) and the tail becomes zero at the store.
+        const float* pa[8];
+        const float* pb[8];
+        int ka[8], kb_[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int idx = tid + G32_THREADS * i;
-                const int mm = a_kfast ? idx / G32_BK : idx % G32_BM;
-                const int kk = a_kfast ? idx % G32_BK : idx / G32_BM;
-                int64_t r = m0 + mm;
-                r = r < p.M ? r : p.M - 1;
-                const int64_t k = k0 + kk;
-                ra[i] = k < p.K ? Ab[r * p.sAm + k * p.sAk] : 0.0f;
+        for (int i = 0; i < 8; ++i) {
+            const int idx = tid + G32_THREADS * i;
+            const int mm = a_kfast ? idx / G32_BK : idx % G32_BM;
+            ka[i] = a_kfast ? idx % G32_BK : idx / G32_BM;
+            const int64_t r = min(m0 + mm, p.M - 1);
+            const int nn = b_kfast ? idx / G32_BK : idx % G32_BN;
+            kb_[i] = b_kfast ? idx % G32_BK : idx / G32_BN;
+            const int64_t c = min(n0 + nn, p.N - 1);
+            if constexpr (KTAIL) {
+                pa[i] = Ab + r * p.sAm;
+                pb[i] = Bb + c * p.sBn;
+            } else {
+                pa[i] = Ab + r * p.sAm + ka[i] * p.sAk;
+                pb[i] = Bb + c * p.sBn + kb_[i] * p.sBk;
             }
+        }
+        const int K1 = (int)p.K - 1, sAk = (int)p.sAk, sBk = (int)p.sBk;
+        auto load_tile = [&](int kt, auto uc) {
+            constexpr int u = decltype(uc)::value;
+            const int k0 = min(kt, nk - 1) * G32_BK;
+            if constexpr (KTAIL) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int idx = tid + G32_THREADS * i;
-                const int nn = b_kfast ? idx / G32_BK : idx % G32_BN;
-                const int kk = b_kfast ? idx % G32_BK : idx / G32_BN;
-                int64_t c = n0 + nn;
-                c = c < p.N ? c : p.N - 1;
-                const int64_t k = k0 + kk;
-                rb[i] = k < p.K ? Bb[k * p.sBk + c * p.sBn] : 0.0f;
+                for (int i = 0; i < 8; ++i) ra[u][i] = pa[i][min(k0 + ka[i], K1) * sAk];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) rb[u][i] = pb[i][min(k0 + kb_[i], K1) * sBk];
+            } else {
+                const int64_t oa = (int64_t)k0 * p.sAk, ob = (int64_t)k0 * p.sBk;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ra[u][i] = pa[i][oa];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) rb[u][i] = pb[i][ob];
             }
         };
-        auto store_tile = [&](int st) {
+        auto store_tile = [&](int kt, auto uc) {
+            constexpr int u = decltype(uc)::value, st = u & 1;
+            const int kl = (int)p.K - kt * G32_BK;   // valid k within this step
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int idx = tid + G32_THREADS * i;
                 const int mm = a_kfast ? idx / G32_BK : idx % G32_BM;
-                const int kk = a_kfast ? idx % G32_BK : idx / G32_BM;
-                sA[st][kk][mm] = ra[i];
+                sA[st][ka[i]][mm] = !KTAIL || ka[i] < kl ? ra[u][i] : 0.0f;
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int idx = tid + G32_THREADS * i;
                 const int nn = b_kfast ? idx / G32_BK : idx % G32_BN;
-                const int kk = b_kfast ? idx % G32_BK : idx / G32_BN;
-                sB[st][kk][nn] = rb[i];
+                sB[st][kb_[i]][nn] = !KTAIL || kb_[i] < kl ? rb[u][i] : 0.0f;
             }
         };
         auto compute_tile = [&](int st) {
@@ -120,18 +153,35 @@ gemm_f32_persistent(GemmF32Params p) {
                 acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
             }
         };
+        // Step t (set u = t % 4, LDS stage t % 2): loads of step t + 3 into set
+        // (u + 3) % 4, the MFMAs of step t, the store of step t + 1, barrier.
+        auto step = [&](int t, auto uc) {
+            constexpr int u = decltype(uc)::value;
+            load_tile(t + 3, std::integral_constant<int, (u + 3) % 4>{});
+            compute_tile(u & 1);
+            store_tile(t + 1, std::integral_constant<int, (u + 1) % 4>{});
+            __syncthreads();
+        };
 
         if (nk > 0) {
-            load_tile(0);
-            store_tile(0);
+            load_tile(0, std::integral_constant<int, 0>{});
+            load_tile(1, std::integral_constant<int, 1>{});
+            load_tile(2, std::integral_constant<int, 2>{});
+            store_tile(0, std::integral_constant<int, 0>{});
             __syncthreads();
-            for (int kt = 0; kt < nk; ++kt) {
-                const bool more = kt + 1 < nk;
-                if (more) load_tile(kt + 1);
-                compute_tile(kt & 1);
-                if (more) store_tile((kt + 1) & 1);
-                __syncthreads();
+            // Four steps per trip (register sets are named statically), then the
+            // remaining zero to three steps.  The last step's store (of step nk)
+            // writes zeros into a stage that is not read again.
+            int t = 0;
+            for (; t + 4 <= nk; t += 4) {
+                step(t, std::integral_constant<int, 0>{});
+                step(t + 1, std::integral_constant<int, 1>{});
+                step(t + 2, std::integral_constant<int, 2>{});
+                step(t + 3, std::integral_constant<int, 3>{});
             }
+            if (t < nk) step(t, std::integral_constant<int, 0>{});
+            if (t + 1 < nk) step(t + 1, std::integral_constant<int, 1>{});
+            if (t + 2 < nk) step(t + 2, std::integral_constant<int, 2>{});
         }
 
         void* Cb = (OUT_BF16 ? (void*)((uint16_t*)p.C + s1 * p.sC1 + s2 * p.sC2)
