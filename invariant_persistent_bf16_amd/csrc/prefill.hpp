@@ -28,7 +28,8 @@
 //     lane l ^ 32;
 //   * online softmax within the chunk: m' = max(m, block max),
 //     l' = l * 2^(m - m') + sum 2^(x - m'), o' = o * 2^(m - m') + P V, keys of
-//     the block in a fixed order; masked keys (t > pos) give exactly 0;
+//     the block in a fixed order, 2^(x - m') evaluated as 2^fma(q.k, c, -m');
+//     masked keys (t > pos) give exactly 0;
 //   * O^T += V^T P^T on the MFMA, P^T straight from the score registers as
 //     two bfloat16 terms (hi = bf16(p), lo = bf16(p - hi); two MFMAs, so p
 //     enters the binary32 sums to about 2^-17), V^T read with
@@ -294,14 +295,16 @@ prefill_chunk_kernel(PfArgs a) {
             constexpr int db = i / 8, u = (i / 2) % 4, hr = i % 2;
             vf[db][u][hr] = pf_read_tr<u * 16 * ROWB + hr * 4 * ROWB>(va[db]);
         });
-        // Scores in the base-2 domain; key of (kb, r): kbase + 32 kb + 8 (r >> 2) + 4 hl + (r & 3).
+        // Key of (kb, r): kbase + 32 kb + 8 (r >> 2) + 4 hl + (r & 3).  The
+        // block maximum is taken on the raw dot products and scaled once:
+        // c * max(s) = max(c * s) in binary32 (c > 0, rounding is monotonic).
         const bool need_mask = kbase + PF_KB - 1 > wpos_lo;
         float mb = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float x = sacc[kb][r] * a.cscale;
+                float x = sacc[kb][r];
                 if (need_mask) {
                     const int key = kbase + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
                     x = key <= pos ? x : -INFINITY;
@@ -310,21 +313,24 @@ prefill_chunk_kernel(PfArgs a) {
                 mb = fmaxf(mb, x);
             }
         mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-        const float m_new = fmaxf(m_run, mb);
-        const bool dead = m_new == -INFINITY;                // no key of the chunk so far
-        const float alpha = dead ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        const float m_new = fmaxf(m_run, mb * a.cscale);
+        // No key of the chunk yet (m_new = -inf): subtract 0 instead, so that
+        // every 2^(x - m) is 2^-inf = 0 and alpha = 0 (o and l are still 0).
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
         m_run = m_new;
         // P as two bfloat16 terms, hi = bf16(p) and lo = bf16(p - hi): their
         // products with the bfloat16 V are exact in the binary32 MFMA sums, so
         // P V carries p to about 2^-17 instead of bfloat16's 2^-9.
+        // p = 2^(s * c - m) with one rounding (fused multiply-add).
         float ps = 0.0f;
         u32x4_t pb[4], pl[4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
-                const float p0 = dead ? 0.0f : __builtin_amdgcn_exp2f(sacc[kb][r] - m_new);
-                const float p1 = dead ? 0.0f : __builtin_amdgcn_exp2f(sacc[kb][r + 1] - m_new);
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], a.cscale, -m_use));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + 1], a.cscale, -m_use));
                 ps += p0;
                 ps += p1;
                 const uint32_t hi = pack_bf16x2(p0, p1);
