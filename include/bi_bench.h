@@ -37,6 +37,30 @@ int bi_bench_gemm_grid(int64_t G, int64_t M, int64_t N, int64_t K,
                        int in_dtype, int out_dtype, int grid, void* stream);
 
 /*
+ * bi_bench_gemm_tile — the invariant 16-bit GEMM of bi_bmm with the kernel
+ * forced: tile_rows 0 = the persistent 256x256 kernel, 32 / 64 / 128 = the
+ * small-tile kernel with (tile_rows x 32) blocks, one wave each.  bias (or
+ * NULL) is indexed by column (bias_rows 0, as bi_addmm) or by row (1, as the
+ * convolution's output channels).  Every tile_rows gives the same bits as
+ * bi_bmm / bi_addmm, which choose the kernel from the shape (the choice is
+ * reported by bi_bench_gemm_tile_rows).  Binary32 operands: BI_ERR_DTYPE.
+ */
+int bi_bench_gemm_tile(int64_t G, int64_t M, int64_t N, int64_t K,
+                       const void* A, int64_t sAg, int64_t sAm, int64_t sAk,
+                       const void* B, int64_t sBg, int64_t sBk, int64_t sBn,
+                       const void* bias, int bias_rows,
+                       void* C, int64_t sCg, int64_t sCm, int64_t sCn,
+                       int in_dtype, int out_dtype, int tile_rows, void* stream);
+
+/*
+ * bi_bench_gemm_tile_rows — the tile_rows that bi_bmm (G slices) or
+ * bi_addmm / bi_mm (G = 1) pick for a 16-bit M x N x K product on the current
+ * device: 0 (persistent kernel) or 32 / 64 / 128.  0 for binary32 operands.
+ * Negative bi_status on a bad shape or without a gfx950 device.
+ */
+int bi_bench_gemm_tile_rows(int64_t G, int64_t M, int64_t N, int64_t K, int in_dtype);
+
+/*
  * bi_bench_splitk_policy — the number of K splits a batch-size-tuned GEMM
  * would pick for an M x N x K product.
  *   rule 0: fill the compute units: splits = clamp(CUs / tiles, 1, 16),

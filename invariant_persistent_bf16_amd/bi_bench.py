@@ -18,6 +18,9 @@ _i64, _vp, _int, _f32, _sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctyp
 _SIGS = {
     "bi_bench_gemm_grid": (_int, [_i64] * 4 + [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _vp,
                                              _i64, _i64, _i64, _int, _int, _int, _vp]),
+    "bi_bench_gemm_tile": (_int, [_i64] * 4 + [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _int, _vp,
+                                             _i64, _i64, _i64, _int, _int, _int, _vp]),
+    "bi_bench_gemm_tile_rows": (_int, [_i64, _i64, _i64, _i64, _int]),
     "bi_bench_splitk_policy": (_int, [_i64, _i64, _i64, _int]),
     "bi_bench_addmm_splitk_workspace_bytes": (_sz, [_i64, _i64, _int]),
     "bi_bench_addmm_splitk": (_int, [_i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i64,
@@ -64,6 +67,33 @@ def gemm_grid(A, B, grid, bias=None, out=None, out_dtype=None, stream=None):
         B.stride(2), _p(bias), _p(C), C.stride(0), C.stride(1), C.stride(2), _dt(A), _dt(C), grid,
         _stream(stream)))
     return C[0] if squeeze else C
+
+
+def gemm_tile(A, B, tile_rows, bias=None, bias_rows=False, out=None, out_dtype=None, stream=None):
+    """The invariant 16-bit batched GEMM (A [G,M,K] or [M,K]) with the kernel
+    forced: tile_rows 0 = persistent 256x256, 32 / 64 / 128 = small tile."""
+    squeeze = A.dim() == 2
+    if squeeze:
+        A, B = A.unsqueeze(0), B.unsqueeze(0)
+    G, M, K = A.shape
+    N = B.shape[2]
+    od = _dt(A) if out_dtype is None else out_dtype
+    C = out if out is not None else torch.empty((G, M, N), dtype=_bi._tdt(od), device=A.device)
+    if C.dim() == 2:
+        C = C.unsqueeze(0)
+    _check("bi_bench_gemm_tile", lib().bi_bench_gemm_tile(
+        G, M, N, K, _p(A), A.stride(0), A.stride(1), A.stride(2), _p(B), B.stride(0), B.stride(1),
+        B.stride(2), _p(bias), int(bias_rows), _p(C), C.stride(0), C.stride(1), C.stride(2), _dt(A), _dt(C),
+        tile_rows, _stream(stream)))
+    return C[0] if squeeze else C
+
+
+def gemm_tile_rows(G, M, N, K, in_dtype=_bi.BI_BF16):
+    """The kernel bi_bmm / bi_addmm pick for the shape: 0 (persistent) or 32 / 64 / 128."""
+    r = lib().bi_bench_gemm_tile_rows(G, M, N, K, in_dtype)
+    if r < 0:
+        raise RuntimeError(f"bi_bench_gemm_tile_rows: {_bi.lib().bi_status_string(r).decode()}")
+    return r
 
 
 def splitk_policy(M, N, K, rule=0):

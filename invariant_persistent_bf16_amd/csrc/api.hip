@@ -4,6 +4,7 @@
 // calls enqueue kernels on the caller's stream and return without waiting.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstring>
 
@@ -12,6 +13,7 @@
 #include "decode.hpp"
 #include "prefill.hpp"
 #include "gemm_bf16.hpp"
+#include "gemm_small.hpp"
 #include "gemm_f32.hpp"
 #include "softmax.hpp"
 #include "rowops.hpp"
@@ -103,9 +105,48 @@ int gemm_check(const GemmDesc& d) {
     return BI_OK;
 }
 
+// Rows per block of the small-tile kernel for a 16-bit product, or 0 for the
+// persistent kernel: a function of the shape alone (both kernels give the same
+// bits).  The small tile is considered only where the 256x256 tiles do not
+// fill the compute units; then the estimated times decide.  Measured on
+// MI355X: a 256x256 tile costs about 0.52 us per 32-wide K step plus about
+// 6 us of launch, prologue and epilogue; the small-tile waves sustain about
+// 8 TB/s of operand reads from L2 (each block reads its rows of A and its 32
+// columns of B over the whole of K), and a wave needs about 0.15 us per K
+// step plus 2 us when it is latency bound.  Rows past M are not read.
+int gemm_tile_rows(const GemmDesc& d, int cus) {
+    const int64_t slices = d.G1 * d.G2;
+    const int64_t tiles = slices * cdiv(d.M, G16_BM) * cdiv(d.N, G16_BN);
+    if (tiles >= cus) return 0;
+    const int64_t nk = cdiv(d.K, G16_BK);
+    const double t_persistent = 6.0 + 0.52 * (double)nk;
+    const int64_t nblk = cdiv(d.N, 32);
+    double best = t_persistent;
+    int best_rows = 0;
+    for (int rows : {32, 64, 128}) {
+        if (rows > 32 && d.M <= rows / 2) break;   // a taller block only adds empty rows
+        const int64_t blocks = slices * cdiv(d.M, rows) * nblk;
+        const double bytes = (double)(slices * d.M * nblk + blocks * 32) * (double)(nk * G16_BK) * 2.0;
+        const double t = std::max(bytes / 8.0e6, 2.0 + 0.15 * (double)nk);
+        if (t < best) { best = t; best_rows = rows; }
+    }
+    return best_rows;
+}
+
+template <bool KC, int O16, bool F16>
+static void gemm_small_launch(const GemmParams& p, int rows, int cvec4, hipStream_t st) {
+    typedef void (*KernS)(GemmParams, int);
+    const KernS k = rows == 128 ? gemm_bf16_small<KC, O16, F16, 4>
+                  : rows == 64  ? gemm_bf16_small<KC, O16, F16, 2>
+                                : gemm_bf16_small<KC, O16, F16, 1>;
+    const int grid = (int)(cdiv(p.total_tiles, 8) * 8);
+    hipLaunchKernelGGL(k, dim3(grid), dim3(GS_THREADS), 0, st, p, cvec4);
+}
+
 // Launch an already checked GEMM.  grid_override > 0 forces the persistent
-// grid size (used only to show that the result does not depend on it).
-int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override) {
+// grid size and tile_rows >= 0 the kernel (both used only to show that the
+// result does not depend on them).
+int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override, int tile_rows) {
     if (d.G1 == 0 || d.M == 0 || d.N == 0) return BI_OK;
     int cus = 0;
     int rc = device_cu_count(&cus);
@@ -113,6 +154,41 @@ int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override) {
     const bool out_bf16 = d.out_dtype == BI_BF16;
     if (d.in_dtype != BI_F32) {
         const bool out16 = d.out_dtype != BI_F32;
+        const bool kc = d.K == 0 || (d.sBk == 1 && (d.N == 1 || d.sBn % 8 == 0));
+        const int rows = tile_rows >= 0 ? tile_rows : grid_override > 0 ? 0 : gemm_tile_rows(d, cus);
+        if (rows != 0 && rows != 32 && rows != 64 && rows != 128) return BI_ERR_UNSUPPORTED;
+        if (rows > 0) {
+            GemmParams p;
+            p.A = (const uint16_t*)d.A; p.B = (const uint16_t*)d.B;
+            p.bias = (const uint16_t*)d.bias; p.C = d.C;
+            p.M = d.M; p.N = d.N; p.K = d.K;
+            p.sAm = d.sAm; p.sBk = d.sBk; p.sBn = d.sBn; p.sCm = d.sCm;
+            p.G2 = d.G2;
+            p.sA1 = d.sA1; p.sA2 = d.sA2; p.sB1 = d.sB1; p.sB2 = d.sB2;
+            p.sC1 = d.sC1; p.sC2 = d.sC2; p.sBias2 = d.sBias2; p.bias_rows = d.bias_rows;
+            p.tiles_m = (int)cdiv(d.M, rows);
+            p.tiles_n = (int)cdiv(d.N, 32);
+            p.tiles_per_slice = p.tiles_m * p.tiles_n;
+            const int64_t total = (int64_t)p.tiles_per_slice * d.G1 * d.G2;
+            if (total > (1ll << 30)) return BI_ERR_UNSUPPORTED;
+            p.total_tiles = (int)total;
+            const int osz = out16 ? 2 : 4;
+            const int cvec4 = aligned(d.C, 4 * osz) && d.N % 4 == 0 && d.sCm % 4 == 0 && d.sC1 % 4 == 0 &&
+                              d.sC2 % 4 == 0;
+            const bool f16 = d.in_dtype == BI_F16;
+            if (f16) {
+                if (kc) { if (out16) gemm_small_launch<true, 1, true>(p, rows, cvec4, st);
+                          else       gemm_small_launch<true, 0, true>(p, rows, cvec4, st); }
+                else    { if (out16) gemm_small_launch<false, 1, true>(p, rows, cvec4, st);
+                          else       gemm_small_launch<false, 0, true>(p, rows, cvec4, st); }
+            } else {
+                if (kc) { if (out16) gemm_small_launch<true, 1, false>(p, rows, cvec4, st);
+                          else       gemm_small_launch<true, 0, false>(p, rows, cvec4, st); }
+                else    { if (out16) gemm_small_launch<false, 1, false>(p, rows, cvec4, st);
+                          else       gemm_small_launch<false, 0, false>(p, rows, cvec4, st); }
+            }
+            return launch_status();
+        }
         GemmParams p;
         p.A = (const uint16_t*)d.A; p.B = (const uint16_t*)d.B;
         p.bias = (const uint16_t*)d.bias; p.C = d.C;
@@ -126,7 +202,6 @@ int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override) {
         p.tiles_per_slice = p.tiles_m * p.tiles_n;
         p.total_tiles = (int)(p.tiles_per_slice * d.G1 * d.G2);
         const int grid = grid_override > 0 ? grid_override : (p.total_tiles < cus ? p.total_tiles : cus);
-        const bool kc = d.K == 0 || (d.sBk == 1 && (d.N == 1 || d.sBn % 8 == 0));
         const int osz = out16 ? 2 : 4;
         const int vel = 16 / osz;   // elements per 16-byte chunk
         const bool cvec = aligned(d.C, 16) && d.N % vel == 0 && d.sCm % vel == 0 && d.sC1 % vel == 0 &&
@@ -377,7 +452,7 @@ int bi_conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, const void* x, int64
     const int wgrid = (int)std::min<int64_t>(cdiv(wchunks, 256), 8 * cus);
     const int ugrid = (int)std::min<int64_t>(cdiv(uchunks, 256), 64 * cus);
     const int64_t lim32 = (1ll << 31) - 1;
-    const bool idx32 = N * Cin * H * W <= lim32 && N * groups * g.L * g.Kp <= lim32 && Cout * g.Kp <= lim32 &&
+    const bool idx32 = N * Cin * H * W <= lim32 && N * groups * g.L * g.Kp + Cout * g.Kp <= lim32 &&
                        g.OH * sh + (Kh - 1) * dh <= lim32 && g.OW * sw + (Kw - 1) * dw <= lim32 &&
                        N * Cin <= lim32 / std::max<int64_t>(H * W, 1);
     if (idx32) {
@@ -386,17 +461,13 @@ int bi_conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, const void* x, int64
         g32.Kh = (int)Kh; g32.Kw = (int)Kw; g32.sh = (int)sh; g32.sw = (int)sw; g32.ph = (int)ph; g32.pw = (int)pw;
         g32.dh = (int)dh; g32.dw = (int)dw; g32.groups = (int)groups; g32.OW = (int)g.OW; g32.L = (int)g.L;
         g32.cig = (int)g.cig; g32.Kg = (int)g.Kg; g32.Kp = (int)g.Kp;
-        if (in_dtype != BI_F32) {
-            hipLaunchKernelGGL((conv_pack_weight32<uint16_t>), dim3(wgrid), dim3(256), 0, st,
-                               (const uint16_t*)w, (uint16_t*)wp, g32);
-            hipLaunchKernelGGL((conv_unfold32<uint16_t>), dim3(ugrid), dim3(256), 0, st,
-                               (const uint16_t*)x, (uint16_t*)u, g32);
-        } else {
-            hipLaunchKernelGGL((conv_pack_weight32<float>), dim3(wgrid), dim3(256), 0, st,
-                               (const float*)w, (float*)wp, g32);
-            hipLaunchKernelGGL((conv_unfold32<float>), dim3(ugrid), dim3(256), 0, st,
-                               (const float*)x, (float*)u, g32);
-        }
+        const int pgrid = (int)std::min<int64_t>(cdiv(wchunks + uchunks, 256), 64 * cus);
+        if (in_dtype != BI_F32)
+            hipLaunchKernelGGL((conv_prepare32<uint16_t>), dim3(pgrid), dim3(256), 0, st,
+                               (const uint16_t*)w, (uint16_t*)wp, (const uint16_t*)x, (uint16_t*)u, g32);
+        else
+            hipLaunchKernelGGL((conv_prepare32<float>), dim3(pgrid), dim3(256), 0, st,
+                               (const float*)w, (float*)wp, (const float*)x, (float*)u, g32);
     } else if (in_dtype != BI_F32) {
         hipLaunchKernelGGL((conv_pack_weight<uint16_t>), dim3(wgrid), dim3(256), 0, st,
                            (const uint16_t*)w, (uint16_t*)wp, g);

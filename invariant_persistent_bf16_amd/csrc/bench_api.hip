@@ -96,7 +96,39 @@ int bi_bench_gemm_grid(int64_t G, int64_t M, int64_t N, int64_t K, const void* A
     d.in_dtype = in_dtype; d.out_dtype = out_dtype;
     int rc = gemm_check(d);
     if (rc != BI_OK) return rc;
-    return gemm_launch(d, (hipStream_t)stream, grid);
+    return gemm_launch(d, (hipStream_t)stream, grid, 0);
+}
+
+int bi_bench_gemm_tile(int64_t G, int64_t M, int64_t N, int64_t K, const void* A, int64_t sAg,
+                       int64_t sAm, int64_t sAk, const void* B, int64_t sBg, int64_t sBk,
+                       int64_t sBn, const void* bias, int bias_rows, void* C, int64_t sCg, int64_t sCm,
+                       int64_t sCn, int in_dtype, int out_dtype, int tile_rows, void* stream) {
+    if (tile_rows != 0 && tile_rows != 32 && tile_rows != 64 && tile_rows != 128) return BI_ERR_UNSUPPORTED;
+    if (in_dtype == BI_F32) return BI_ERR_DTYPE;
+    if (bias_rows != 0 && bias_rows != 1) return BI_ERR_UNSUPPORTED;
+    GemmDesc d;
+    std::memset(&d, 0, sizeof(d));
+    d.G1 = G; d.G2 = 1; d.M = M; d.N = N; d.K = K;
+    d.A = A; d.sA1 = sAg; d.sAm = sAm; d.sAk = sAk;
+    d.B = B; d.sB1 = sBg; d.sBk = sBk; d.sBn = sBn;
+    d.bias = bias; d.bias_rows = bias_rows;
+    d.C = C; d.sC1 = sCg; d.sCm = sCm; d.sCn = sCn;
+    d.in_dtype = in_dtype; d.out_dtype = out_dtype;
+    int rc = gemm_check(d);
+    if (rc != BI_OK) return rc;
+    return gemm_launch(d, (hipStream_t)stream, 0, tile_rows);
+}
+
+int bi_bench_gemm_tile_rows(int64_t G, int64_t M, int64_t N, int64_t K, int in_dtype) {
+    if (G < 1 || M < 1 || N < 1 || K < 0) return BI_ERR_SHAPE;
+    if (in_dtype == BI_F32) return 0;
+    GemmDesc d;
+    std::memset(&d, 0, sizeof(d));
+    d.G1 = G; d.G2 = 1; d.M = M; d.N = N; d.K = K; d.in_dtype = in_dtype;
+    int cus = 0;
+    int rc = device_cu_count(&cus);
+    if (rc != BI_OK) return rc;
+    return gemm_tile_rows(d, cus);
 }
 
 int bi_bench_splitk_policy(int64_t M, int64_t N, int64_t K, int rule) {

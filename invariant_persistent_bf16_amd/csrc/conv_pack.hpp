@@ -42,32 +42,30 @@ __device__ __forceinline__ void store8(T* dst, const T (&v)[8]) {
     }
 }
 
-// Weight pack with 32-bit indices: one thread per 8 consecutive k of one co
-// row, one 16-byte (or two) store.
+// Weight pack and unfold with 32-bit indices, in one launch (at one image
+// each is only a few microseconds of work, less than a launch's fixed cost):
+// work item i < Cout * Kp/8 packs 8 consecutive k of one co row; the others
+// unfold 8 consecutive k of one (n, g, l) row of U.  For the unfold, k0 is
+// split into (ci, kh, kw) once; the 8 elements then advance kw, kh, ci by
+// carries, with no division per element.  One 16-byte (or two) store per item.
 template <typename T>
-__global__ void __launch_bounds__(256) conv_pack_weight32(const T* __restrict__ w, T* __restrict__ wp, ConvGeom32 g) {
+__global__ void __launch_bounds__(256) conv_prepare32(const T* __restrict__ w, T* __restrict__ wp,
+                                                     const T* __restrict__ x, T* __restrict__ u, ConvGeom32 g) {
     const int nchunk = g.Kp / 8;
-    const int total = g.Cout * nchunk;
-    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
-        const int co = i / nchunk, k0 = (i - co * nchunk) * 8;
-        T v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = k0 + e < g.Kg ? w[co * g.Kg + k0 + e] : (T)0;
-        store8(wp + co * g.Kp + k0, v);
-    }
-}
-
-// Unfold with 32-bit indices: one thread per 8 consecutive k of one (n, g, l)
-// row of U.  k0 is split into (ci, kh, kw) once; the 8 elements then advance
-// kw, kh, ci by carries, with no division per element.
-template <typename T>
-__global__ void __launch_bounds__(256) conv_unfold32(const T* __restrict__ x, T* __restrict__ u, ConvGeom32 g) {
-    const int nchunk = g.Kp / 8;
-    const int total = g.N * g.groups * g.L * nchunk;
+    const int wtotal = g.Cout * nchunk;
+    const int total = wtotal + g.N * g.groups * g.L * nchunk;
     const int khw = g.Kh * g.Kw;
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
-        int r = i / nchunk;
-        const int k0 = (i - r * nchunk) * 8;
+        T v[8];
+        if (i < wtotal) {
+            const int co = i / nchunk, k0 = (i - co * nchunk) * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = k0 + e < g.Kg ? w[co * g.Kg + k0 + e] : (T)0;
+            store8(wp + co * g.Kp + k0, v);
+            continue;
+        }
+        int r = (i - wtotal) / nchunk;
+        const int k0 = (i - wtotal - r * nchunk) * 8;
         const int l = r % g.L;
         r /= g.L;
         const int grp = r % g.groups;
@@ -78,7 +76,6 @@ __global__ void __launch_bounds__(256) conv_unfold32(const T* __restrict__ x, T*
         int kh = rem / g.Kw, kw = rem - kh * g.Kw;
         const int cbase = n * g.Cin + grp * g.cig;
         const int ih0 = oh * g.sh - g.ph, iw0 = ow * g.sw - g.pw;
-        T v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             T val = (T)0;

@@ -21,6 +21,13 @@ struct GemmDesc {
 
 int device_cu_count(int* cus);
 int gemm_check(const GemmDesc& d);
-int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override);
+// Rows per block of the small-tile kernel that gemm_launch picks for a 16-bit
+// product (0: the persistent 256x256 kernel).
+int gemm_tile_rows(const GemmDesc& d, int cus);
+// tile_rows: -1 lets the shape choose the kernel; 0 forces the persistent
+// 256x256 kernel (on grid_override workgroups if > 0); 32, 64 or 128 force
+// the small-tile kernel with blocks of that many rows.  Every choice gives the
+// same bits.
+int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override, int tile_rows = -1);
 
 }  // namespace bi
