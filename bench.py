@@ -210,6 +210,7 @@ def main():
     }
 
     out["invariance_cost"] = invariance_cost(Wd, bd, x0, dq, dk, dv, Y)
+    out["small_batch"] = small_batch(Wd, bd, x0, cwd, cbd, cx0)
     out["row_ops"] = row_ops(X, Y)
     out["paged_decode"] = paged_decode(dq, dk, dv, dout)
     out["prefill"] = prefill()
@@ -236,10 +237,80 @@ def _time_ms(fn, iters=20):
     return e0.elapsed_time(e1) / iters
 
 
+def _graph_us(fn, n=20):
+    """GPU time of one call in microseconds, without the host's launch cost:
+    n calls captured in a HIP graph (the library's kernels only, no memset
+    nodes), replayed; best of 3 replays."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = float("inf")
+    for _ in range(3):
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) * 1e3 / n)
+    del g
+    return best
+
+
+def small_batch(Wd, bd, x0, cwd, cbd, cx0):
+    """Untimed extra: batch 1 of the addmm and conv workloads, where 256x256
+    tiles leave most compute units idle.  The library then picks the small-tile
+    kernel (same bits); forced persistent-kernel times beside it (GPU time from
+    graph replay)."""
+    import torch
+
+    import synth
+    from invariant_persistent_bf16_amd import bi, bi_bench
+
+    dev = Wd.device
+    K, N = ADDMM["K"], ADDMM["N"]
+    res = {}
+    for M in (1, 64):
+        X = synth.addmm_batch(x0, M, device=dev)
+        y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        ta = _graph_us(lambda: bi.bi_addmm(bd, X, Wd, out=y))
+        tp = _graph_us(lambda: bi_bench.gemm_tile(X, Wd, 0, bias=bd, out=y))
+        res[f"addmm_M{M}"] = {"us": round(ta, 2), "tile_rows": bi_bench.gemm_tile_rows(1, M, N, K),
+                              "persistent_us": round(tp, 2),
+                              "W_GBps": round(K * N * 2 / (ta * 1e-6) / 1e9, 1)}
+    cx = synth.conv_batch(cx0, 1, device=dev)
+    cy = torch.empty(1, 1152, 16, 16, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(bi.bi_conv2d_workspace_bytes(cx.shape, cwd.shape, (14, 14)), dtype=torch.uint8, device=dev)
+    tc = _graph_us(lambda: bi.bi_conv2d(cx, cwd, cbd, stride=(14, 14), out=cy, workspace=ws))
+    # The conv's GEMM alone: packed weight [1152, 592] x unfold [256, 592]^T, row bias.
+    Ap = torch.zeros(1152, 592, dtype=torch.bfloat16, device=dev)
+    Ap[:, :588] = cwd.reshape(1152, 588)
+    U = torch.zeros(256, 592, dtype=torch.bfloat16, device=dev)
+    U[:, :588] = cx.reshape(3, 16, 14, 16, 14).permute(1, 3, 0, 2, 4).reshape(256, 588)
+    yg = torch.empty(1152, 256, dtype=torch.bfloat16, device=dev)
+    tg = {r: _graph_us(lambda: bi_bench.gemm_tile(Ap, U.t(), r, bias=cbd, bias_rows=True, out=yg))
+          for r in (0, bi_bench.gemm_tile_rows(1, 1152, 256, 592))}
+    res["conv2d_B1"] = {"us": round(tc, 2), "gemm_tile_rows": bi_bench.gemm_tile_rows(1, 1152, 256, 592),
+                        "gemm_us": round(min(v for r, v in tg.items() if r != 0), 2),
+                        "gemm_persistent_us": round(tg[0], 2)}
+    return res
+
+
 def invariance_cost(Wd, bd, x0, dq, dk, dv, Y):
     """Untimed extra: the invariant kernels against batch-size-tuned variants
     (split-K for the GEMM filling the CUs, split-KV by load for decode) at the
-    batch sizes where they differ, plus an HBM read-rate probe."""
+    batch sizes where they differ (GPU time from graph replay), plus an HBM
+    read-rate probe."""
     import torch
 
     import synth
@@ -254,8 +325,8 @@ def invariance_cost(Wd, bd, x0, dq, dk, dv, Y):
         s = bi_bench.splitk_policy(M, N, K, 0)
         ws = torch.empty(max(1, s * M * N), dtype=torch.float32, device=dev)
         yv = Y[:M]
-        ti = _time_ms(lambda: bi.bi_addmm(bd, X, Wd, out=yv))
-        ts = _time_ms(lambda: bi_bench.addmm_splitk(bd, X, Wd, s, out=yv, workspace=ws))
+        ti = _graph_us(lambda: bi.bi_addmm(bd, X, Wd, out=yv)) * 1e-3
+        ts = _graph_us(lambda: bi_bench.addmm_splitk(bd, X, Wd, s, out=yv, workspace=ws)) * 1e-3
         res["addmm"][str(M)] = {"invariant_us": round(ti * 1e3, 2), "splitk_us": round(ts * 1e3, 2),
                                 "splits": s, "invariant_over_splitk": round(ti / ts, 3)}
     H, S, D = DEC["H"], DEC["S"], DEC["D"]
@@ -267,8 +338,8 @@ def invariance_cost(Wd, bd, x0, dq, dk, dv, Y):
                          dtype=torch.float32, device=dev)
         wsf = torch.empty(bi.bi_decode_attn_workspace_bytes(B, H, S, D) // 4 + 1, dtype=torch.float32,
                           device=dev)
-        tf = _time_ms(lambda: bi.bi_decode_attn(q, k, v, 0.125, out=o, workspace=wsf))
-        tl = _time_ms(lambda: bi_bench.decode_attn_splits(q, k, v, 0.125, s, out=o, workspace=ws))
+        tf = _graph_us(lambda: bi.bi_decode_attn(q, k, v, 0.125, out=o, workspace=wsf)) * 1e-3
+        tl = _graph_us(lambda: bi_bench.decode_attn_splits(q, k, v, 0.125, s, out=o, workspace=ws)) * 1e-3
         gbs = B * H * 2 * S * D * 2 / 1e9
         res["decode"][str(B)] = {"fixed_chunk_us": round(tf * 1e3, 2), "by_load_us": round(tl * 1e3, 2),
                                  "splits_by_load": s, "fixed_GBps": round(gbs / (tf * 1e-3), 1),
