@@ -393,9 +393,11 @@ gemm_bf16_persistent(GemmParams p) {
         // CVEC: each wave stages its 128x128 block through its own 32 KiB of
         // the (now idle) LDS ring, 16-byte chunks of row r at chunk ^ (r mod
         // chunks per row) so that neither side conflicts, then writes whole
-        // rows with 16-byte stores (one instruction = 8 full 128-byte lines
-        // for bfloat16); binary32 goes in two halves of 64 rows.  Otherwise:
-        // one buffer store per element.
+        // rows with 16-byte non-temporal stores (one instruction = 8 full
+        // 128-byte lines for bfloat16; the output is not re-read by this
+        // kernel, and keeping it out of the caches leaves them to the operand
+        // panels); binary32 goes in two halves of 64 rows.  Otherwise: one
+        // buffer store per element.
         // Bounds without branches: the buffer's record count ends at the last
         // valid element of this wave's block, so rows past M fall outside it,
         // and a lane whose columns are past N stores at the out-of-range
@@ -473,7 +475,7 @@ gemm_bf16_persistent(GemmParams p) {
                             const int r = i * RPI + rsub;
                             const u32x4_t d = *(const u32x4_t*)(stg + r * ROWB + ((t ^ (r & (NCH - 1))) << 4));
                             const uint32_t off = col_ok ? (uint32_t)((ps * RPP + r) * sCm * ESZ + t * 16) : G16_OOB;
-                            __builtin_amdgcn_raw_buffer_store_b128(d, rsC, (int)off, 0, 0);
+                            __builtin_amdgcn_raw_buffer_store_b128(d, rsC, (int)off, 0, 2);
                         });
                     });
                 } else {
