@@ -52,7 +52,7 @@ constexpr int PF_KB = 64;                  // keys per block
 constexpr int PF_WAVES = 8;
 constexpr int PF_QT = PF_WAVES * 32;       // queries per tile
 constexpr int PF_THREADS = PF_WAVES * 64;
-constexpr int PF_NSTAGE = 3;
+constexpr int PF_NSTAGE = 4;
 
 typedef __attribute__((address_space(3))) void pf_lds_t;
 typedef short pf_v4i16_t __attribute__((ext_vector_type(4)));
@@ -198,13 +198,18 @@ prefill_chunk_kernel(PfArgs a) {
     // K block in LDS: row = key (256 bytes), 16-byte chunk c at c ^ (row & 15).
     // V block: row rho holds key swap23(rho), chunk c at c ^ 4 (rho & 3).
     const int pmask = (1 << a.log2p) - 1;
+    // The lane's row and chunk are recomputed from an opaque copy of the lane
+    // id at each call, so that none of the address arithmetic is kept live
+    // across the block loop (registers are the limit there).
     auto copy_block = [&](int j, int st) {
         const int kbase = kc0 + j * PF_KB;
         uint8_t* kdst = smem + st * STAGE;
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int rho = 8 * wave + 4 * i + (lane >> 4);
-            const int p = lane & 15;
+            const int rho = 8 * wave + 4 * i + (ln >> 4);
+            const int p = ln & 15;
             {
                 const int key = min(kbase + rho, kend - 1);
                 const int pg = pids[(key >> a.log2p) - pfirst];
@@ -230,15 +235,16 @@ prefill_chunk_kernel(PfArgs a) {
     //  addresses row 8 hl + (li >> 2) (+ 4 for the second half of the 8 keys,
     //  + 16 per 16-key slice) and the 8 bytes of d block db at chunk
     //  4 (db ^ (li >> 2)) + 2 (g & 1) + ((li & 3) >> 1), half li & 1.
-    uint32_t koff[NS], voff[NDB];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) koff[s] = (lane & 31) * ROWB + ((((2 * s) | hl) ^ (lane & 15)) << 4);
+    // K fragment s: row l % 32, chunk (2s | hl) ^ (l & 15) = (2s ^ (l & 14)) | (hl ^ (l & 1)),
+    // i.e. byte offset k0 + ((32 s) ^ ke).  V^T fragment db: v0 + ((64 db) ^ vz).
+    // (Two registers per operand instead of one per fragment.)
+    const uint32_t k0 = (lane & 31) * ROWB + ((hl ^ (lane & 1)) << 4);
+    const uint32_t ke = (lane & 14) << 4;
+    uint32_t v0, vz;
     {
         const int g = lane >> 4, li = lane & 15, z = li >> 2;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-            voff[db] = BLK + (8 * hl + z) * ROWB + ((4 * (db ^ z) + 2 * (g & 1) + ((li & 3) >> 1)) << 4) +
-                       (li & 1) * 8;
+        v0 = BLK + (8 * hl + z) * ROWB + ((2 * (g & 1) + ((li & 3) >> 1)) << 4) + (li & 1) * 8;
+        vz = z << 6;
     }
 
     const uint32_t lds0 = (uint32_t)(size_t)((const __attribute__((address_space(3))) uint8_t*)smem);
@@ -249,55 +255,94 @@ prefill_chunk_kernel(PfArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
 
-    copy_block(0, 0);
-    if (nblk > 1) copy_block(1, 1);
-    for (int j = 0; j < nblk; ++j) {
-        const int st = j % PF_NSTAGE;
-        // Copies of block j done (block j + 1's four may still fly), then
-        // every wave's: stage (j + 2) % 3 was last read in step j - 1.
-        if (j + 1 < nblk) pf_wait_vm<4>();
-        else              pf_wait_vm<0>();
-        __builtin_amdgcn_s_barrier();
-        if (j + 2 < nblk) copy_block(j + 2, (j + 2) % PF_NSTAGE);
-        const int kbase = kc0 + j * PF_KB;
-        if (!wave_on || kbase > wpos_hi) continue;        // every key masked for this wave
-        const uint32_t sb = lds0 + st * STAGE;
+    // Blocks 0 .. nlive - 1 of the chunk hold keys that precede the wave's
+    // last query; the wave skips the others.
+    const int nlive = !wave_on || wpos_hi < kc0 ? 0 : min(nblk, (wpos_hi - kc0) / PF_KB + 1);
+    f32x16_t sacc[2];        // S^T of a block, from its S^T products to its softmax step
+    u32x4_t pb[4], pl[4];    // P^T of a block (hi and lo terms), from its softmax step to its P.V products
 
-        // S^T for the block's two 32-key halves: 2 x NS fragment reads, then
-        // the MFMAs as their reads land (LDS reads complete in order).
+    // S^T = K Q^T of block i.
+    auto qk = [&](int i) {
+        const uint32_t sk = lds0 + (i % PF_NSTAGE) * STAGE + k0;
         u32x4_t kf[2][NS];
-        uint32_t ka[NS];
-#pragma unroll
-        for (int s = 0; s < NS; ++s) ka[s] = sb + koff[s];
         pf_static_for<0, 2 * NS>([&](auto ic) {
-            constexpr int i = decltype(ic)::value;
-            kf[i / NS][i % NS] = pf_read128<(i / NS) * 32 * ROWB>(ka[i % NS]);
+            constexpr int k = decltype(ic)::value;
+            kf[k / NS][k % NS] = pf_read128<(k / NS) * 32 * ROWB>(sk + (((k % NS) << 5) ^ ke));
         });
-        f32x16_t sacc[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
         pf_static_for<0, 2 * NS>([&](auto ic) {
-            constexpr int i = decltype(ic)::value;
-            pf_wait_lgkm<2 * NS - 1 - i>(kf[i / NS][i % NS]);
-            sacc[i / NS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[i / NS][i % NS]),
-                                                                   as_bf16x8(qf[i % NS]), sacc[i / NS], 0, 0, 0);
+            constexpr int k = decltype(ic)::value;
+            pf_wait_lgkm<2 * NS - 1 - k>(kf[k / NS][k % NS]);
+            sacc[k / NS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[k / NS][k % NS]),
+                                                                   as_bf16x8(qf[k % NS]), sacc[k / NS], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         });
-        // The V^T fragments do not depend on the scores: issue their reads now.
+    };
+    // O^T += V^T P^T of block i over its 4 slices of 16 keys.
+    auto pv = [&](int i) {
+        const uint32_t sv = lds0 + (i % PF_NSTAGE) * STAGE + v0;
         pf_u32x2_t vf[NDB][4][2];
-        uint32_t va[NDB];
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) va[db] = sb + voff[db];
         pf_static_for<0, NDB * 8>([&](auto ic) {
-            constexpr int i = decltype(ic)::value;
-            constexpr int db = i / 8, u = (i / 2) % 4, hr = i % 2;
-            vf[db][u][hr] = pf_read_tr<u * 16 * ROWB + hr * 4 * ROWB>(va[db]);
+            constexpr int k = decltype(ic)::value;
+            constexpr int db = k / 8, u = (k / 2) % 4, hr = k % 2;
+            vf[db][u][hr] = pf_read_tr<u * 16 * ROWB + hr * 4 * ROWB>(sv + ((db << 6) ^ vz));
         });
-        // Key of (kb, r): kbase + 32 kb + 8 (r >> 2) + 4 hl + (r & 3).  The
-        // block maximum is taken on the raw dot products and scaled once:
-        // c * max(s) = max(c * s) in binary32 (c > 0, rounding is monotonic).
+        pf_static_for<0, NDB * 4>([&](auto ic) {
+            constexpr int k = decltype(ic)::value, db = k / 4, u = k % 4;
+            pf_wait_lgkm<(NDB * 4 - 1 - k) * 2>(vf[db][u][1]);
+            pf_wait_lgkm<(NDB * 4 - 1 - k) * 2>(vf[db][u][0]);
+            const u32x4_t v = {vf[db][u][0][0], vf[db][u][0][1], vf[db][u][1][0], vf[db][u][1][1]};
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(v), as_bf16x8(pb[u]), o[db], 0, 0, 0);
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(v), as_bf16x8(pl[u]), o[db], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    // P.V of block i - 1 with S^T of block i: each K read is issued once a
+    // P.V pair has consumed its V^T fragment (reads complete in order; the
+    // wait counts include the K reads issued after each pair's V^T reads).
+    auto pvqk = [&](int i) {
+        const uint32_t sv = lds0 + ((i - 1) % PF_NSTAGE) * STAGE + v0;
+        const uint32_t sk = lds0 + (i % PF_NSTAGE) * STAGE + k0;
+        pf_u32x2_t vf[NDB][4][2];
+        u32x4_t kf[2][NS];
+        pf_static_for<0, NDB * 8>([&](auto ic) {
+            constexpr int k = decltype(ic)::value;
+            constexpr int db = k / 8, u = (k / 2) % 4, hr = k % 2;
+            vf[db][u][hr] = pf_read_tr<u * 16 * ROWB + hr * 4 * ROWB>(sv + ((db << 6) ^ vz));
+        });
+        static_assert(NDB * 4 == 2 * NS, "one K read per P.V pair");
+        pf_static_for<0, NDB * 4>([&](auto ic) {
+            constexpr int k = decltype(ic)::value, db = k / 4, u = k % 4;
+            pf_wait_lgkm<(NDB * 4 - 1 - k) * 2 + k>(vf[db][u][1]);
+            pf_wait_lgkm<(NDB * 4 - 1 - k) * 2 + k>(vf[db][u][0]);
+            const u32x4_t v = {vf[db][u][0][0], vf[db][u][0][1], vf[db][u][1][0], vf[db][u][1][1]};
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(v), as_bf16x8(pb[u]), o[db], 0, 0, 0);
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(v), as_bf16x8(pl[u]), o[db], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            kf[k / NS][k % NS] = pf_read128<(k / NS) * 32 * ROWB>(sk + (((k % NS) << 5) ^ ke));
+            __builtin_amdgcn_sched_barrier(0);
+        });
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
+        pf_static_for<0, 2 * NS>([&](auto ic) {
+            constexpr int k = decltype(ic)::value;
+            pf_wait_lgkm<2 * NS - 1 - k>(kf[k / NS][k % NS]);
+            sacc[k / NS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[k / NS][k % NS]),
+                                                                   as_bf16x8(qf[k % NS]), sacc[k / NS], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    // The online-softmax step of block i.  Key of (kb, r): kbase + 32 kb +
+    // 8 (r >> 2) + 4 hl + (r & 3).  The block maximum is taken on the raw dot
+    // products and scaled once: c * max(s) = max(c * s) in binary32 (c > 0,
+    // rounding is monotonic).  o holds blocks 0 .. i - 1 here.
+    auto softmax = [&](int i) {
+        const int kbase = kc0 + i * PF_KB;
         const bool need_mask = kbase + PF_KB - 1 > wpos_lo;
         float mb = -INFINITY;
 #pragma unroll
@@ -324,7 +369,6 @@ prefill_chunk_kernel(PfArgs a) {
         // P V carries p to about 2^-17 instead of bfloat16's 2^-9.
         // p = 2^(s * c - m) with one rounding (fused multiply-add).
         float ps = 0.0f;
-        u32x4_t pb[4], pl[4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -345,18 +389,50 @@ prefill_chunk_kernel(PfArgs a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
         }
-        // O^T += V^T P^T over the 4 slices of 16 keys.
-        pf_static_for<0, NDB * 4>([&](auto ic) {
-            constexpr int i = decltype(ic)::value;
-            constexpr int db = i / 4, u = i % 4;
-            pf_wait_lgkm<(NDB * 4 - 1 - i) * 2>(vf[db][u][1]);
-            pf_wait_lgkm<(NDB * 4 - 1 - i) * 2>(vf[db][u][0]);
-            const u32x4_t v = {vf[db][u][0][0], vf[db][u][0][1], vf[db][u][1][0], vf[db][u][1][1]};
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(v), as_bf16x8(pb[u]), o[db], 0, 0, 0);
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(v), as_bf16x8(pl[u]), o[db], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        });
+    };
+
+    // Steps i = 0 .. nblk, each two phases separated by workgroup barriers.
+    // Waves 0-3 run {P.V of block i - 1, S^T of block i} then the softmax
+    // step of block i; waves 4-7 (on the same four SIMDs) run the softmax
+    // step of block i - 1 then {P.V of block i - 1, S^T of block i}, one phase
+    // behind, so that on each SIMD one wave's softmax overlaps the other's
+    // MFMAs.  Block b is copied at the start of step b - 2 into stage b % 4,
+    // whose previous block (b - 4) was last read in the second phase of step
+    // b - 3, and waited for at the end of step b - 1.  Per query the order of
+    // operations is that of a plain loop over blocks (S^T, softmax step,
+    // o = o * alpha + P V), whatever the phase offset.  Each group's steps are
+    // straight-line code (first block, full steps, the last P.V, then steps
+    // with no live block), so no score or P register is live where it is not used.
+    auto begin = [&](int i) {
+        if (i + 2 < nblk) copy_block(i + 2, (i + 2) % PF_NSTAGE);
+    };
+    auto mid = [&]() { __builtin_amdgcn_s_barrier(); };
+    // Block i + 1 landed (block i + 2's four copies may still fly).
+    auto end = [&](int i) {
+        if (i + 2 < nblk) pf_wait_vm<4>();
+        else              pf_wait_vm<0>();
+        __builtin_amdgcn_s_barrier();
+    };
+    copy_block(0, 0);
+    if (nblk > 1) copy_block(1, 1);
+    if (nblk > 1) pf_wait_vm<4>();
+    else          pf_wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    int i = 0;
+    if (wave < PF_WAVES / 2) {
+        if (nlive > 0) {
+            begin(0); qk(0); mid(); softmax(0); end(0);
+            for (i = 1; i < nlive; ++i) { begin(i); pvqk(i); mid(); softmax(i); end(i); }
+            begin(i); pv(i - 1); mid(); end(i); ++i;
+        }
+    } else {
+        if (nlive > 0) {
+            begin(0); mid(); qk(0); end(0);
+            for (i = 1; i < nlive; ++i) { begin(i); softmax(i - 1); mid(); pvqk(i); end(i); }
+            begin(i); softmax(i - 1); mid(); pv(i - 1); end(i); ++i;
+        }
     }
+    for (; i <= nblk; ++i) { begin(i); mid(); end(i); }
 
     // ---- results of this chunk for the queries that have keys in it
     if (!wave_on) return;
