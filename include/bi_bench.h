@@ -37,13 +37,14 @@ int bi_bench_gemm_grid(int64_t G, int64_t M, int64_t N, int64_t K,
                        int in_dtype, int out_dtype, int grid, void* stream);
 
 /*
- * bi_bench_gemm_tile — the invariant 16-bit GEMM of bi_bmm with the kernel
- * forced: tile_rows 0 = the persistent 256x256 kernel, 32 / 64 / 128 = the
- * small-tile kernel with (tile_rows x 32) blocks, one wave each.  bias (or
- * NULL) is indexed by column (bias_rows 0, as bi_addmm) or by row (1, as the
- * convolution's output channels).  Every tile_rows gives the same bits as
- * bi_bmm / bi_addmm, which choose the kernel from the shape (the choice is
- * reported by bi_bench_gemm_tile_rows).  Binary32 operands: BI_ERR_DTYPE.
+ * bi_bench_gemm_tile — the invariant GEMM of bi_bmm with the kernel forced.
+ * 16-bit operands: tile_rows 0 = the persistent 256x256 kernel, 32 / 64 / 128
+ * = the small-tile kernel with (tile_rows x 32) blocks, one wave each.
+ * Binary32 operands: 0 = 64x64 tiles, 32 = 32x32 tiles (others:
+ * BI_ERR_UNSUPPORTED).  bias (or NULL) is indexed by column (bias_rows 0, as
+ * bi_addmm) or by row (1, as the convolution's output channels).  Every
+ * tile_rows gives the same bits as bi_bmm / bi_addmm, which choose the kernel
+ * from the shape (the choice is reported by bi_bench_gemm_tile_rows).
  */
 int bi_bench_gemm_tile(int64_t G, int64_t M, int64_t N, int64_t K,
                        const void* A, int64_t sAg, int64_t sAm, int64_t sAk,
@@ -54,8 +55,8 @@ int bi_bench_gemm_tile(int64_t G, int64_t M, int64_t N, int64_t K,
 
 /*
  * bi_bench_gemm_tile_rows — the tile_rows that bi_bmm (G slices) or
- * bi_addmm / bi_mm (G = 1) pick for a 16-bit M x N x K product on the current
- * device: 0 (persistent kernel) or 32 / 64 / 128.  0 for binary32 operands.
+ * bi_addmm / bi_mm (G = 1) pick for an M x N x K product on the current
+ * device: 0 or 32 / 64 / 128 for 16-bit operands, 0 or 32 for binary32.
  * Negative bi_status on a bad shape or without a gfx950 device.
  */
 int bi_bench_gemm_tile_rows(int64_t G, int64_t M, int64_t N, int64_t K, int in_dtype);

@@ -116,6 +116,9 @@ int gemm_check(const GemmDesc& d) {
 // step plus 2 us when it is latency bound.  Rows past M are not read.
 int gemm_tile_rows(const GemmDesc& d, int cus) {
     const int64_t slices = d.G1 * d.G2;
+    // Binary32: 32x32 tiles (one 16x16 MFMA chain per wave) where the 64x64
+    // tiles do not fill the compute units.
+    if (d.in_dtype == BI_F32) return slices * cdiv(d.M, G32_BM) * cdiv(d.N, G32_BN) < cus ? 32 : 0;
     const int64_t tiles = slices * cdiv(d.M, G16_BM) * cdiv(d.N, G16_BN);
     if (tiles >= cus) return 0;
     const int64_t nk = cdiv(d.K, G16_BK);
@@ -227,19 +230,29 @@ int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override, int tile_r
         p.G2 = d.G2;
         p.sA1 = d.sA1; p.sA2 = d.sA2; p.sB1 = d.sB1; p.sB2 = d.sB2;
         p.sC1 = d.sC1; p.sC2 = d.sC2; p.sBias2 = d.sBias2; p.bias_rows = d.bias_rows;
-        p.tiles_m = (int)cdiv(d.M, G32_BM);
-        p.tiles_n = (int)cdiv(d.N, G32_BN);
+        // 64x64 tiles, or 32x32 tiles where the 64x64 ones do not fill the
+        // compute units (same per-element arithmetic, same bits).
+        const int rows = tile_rows >= 0 ? tile_rows : grid_override > 0 ? 0 : gemm_tile_rows(d, cus);
+        if (rows != 0 && rows != 32) return BI_ERR_UNSUPPORTED;
+        const int bt = rows == 32 ? 32 : G32_BM;
+        p.tiles_m = (int)cdiv(d.M, bt);
+        p.tiles_n = (int)cdiv(d.N, bt);
         p.tiles_per_slice = p.tiles_m * p.tiles_n;
-        p.total_tiles = (int)(p.tiles_per_slice * d.G1 * d.G2);
+        const int64_t total = (int64_t)p.tiles_per_slice * d.G1 * d.G2;
+        if (total > (1ll << 30)) return BI_ERR_UNSUPPORTED;
+        p.total_tiles = (int)total;
         const int cap = 4 * cus;
         const int grid = grid_override > 0 ? grid_override : (p.total_tiles < cap ? p.total_tiles : cap);
         // The K tail variant only where K is not a multiple of the K step (the
         // arithmetic of both is the same MFMA chain over the same zero-padded K).
         const bool ktail = d.K % G32_BK != 0;
         typedef void (*Kern32)(GemmF32Params);
-        static const Kern32 kerns32[2][2] = {{gemm_f32_persistent<0, false>, gemm_f32_persistent<0, true>},
-                                              {gemm_f32_persistent<1, false>, gemm_f32_persistent<1, true>}};
-        hipLaunchKernelGGL(kerns32[out_bf16][ktail], dim3(grid), dim3(G32_THREADS), 0, st, p);
+        static const Kern32 kerns32[2][2][2] = {
+            {{gemm_f32_persistent<0, false, 32>, gemm_f32_persistent<0, true, 32>},
+             {gemm_f32_persistent<1, false, 32>, gemm_f32_persistent<1, true, 32>}},
+            {{gemm_f32_persistent<0, false, 16>, gemm_f32_persistent<0, true, 16>},
+             {gemm_f32_persistent<1, false, 16>, gemm_f32_persistent<1, true, 16>}}};
+        hipLaunchKernelGGL(kerns32[rows == 32][out_bf16][ktail], dim3(grid), dim3(G32_THREADS), 0, st, p);
     }
     return launch_status();
 }

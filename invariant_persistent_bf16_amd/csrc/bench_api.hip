@@ -104,7 +104,7 @@ int bi_bench_gemm_tile(int64_t G, int64_t M, int64_t N, int64_t K, const void* A
                        int64_t sBn, const void* bias, int bias_rows, void* C, int64_t sCg, int64_t sCm,
                        int64_t sCn, int in_dtype, int out_dtype, int tile_rows, void* stream) {
     if (tile_rows != 0 && tile_rows != 32 && tile_rows != 64 && tile_rows != 128) return BI_ERR_UNSUPPORTED;
-    if (in_dtype == BI_F32) return BI_ERR_DTYPE;
+    if (in_dtype == BI_F32 && tile_rows > 32) return BI_ERR_UNSUPPORTED;
     if (bias_rows != 0 && bias_rows != 1) return BI_ERR_UNSUPPORTED;
     GemmDesc d;
     std::memset(&d, 0, sizeof(d));
@@ -121,7 +121,6 @@ int bi_bench_gemm_tile(int64_t G, int64_t M, int64_t N, int64_t K, const void* A
 
 int bi_bench_gemm_tile_rows(int64_t G, int64_t M, int64_t N, int64_t K, int in_dtype) {
     if (G < 1 || M < 1 || N < 1 || K < 0) return BI_ERR_SHAPE;
-    if (in_dtype == BI_F32) return 0;
     GemmDesc d;
     std::memset(&d, 0, sizeof(d));
     d.G1 = G; d.G2 = 1; d.M = M; d.N = N; d.K = K; d.in_dtype = in_dtype;

@@ -10,7 +10,9 @@ convolution's output channels), binary32 and 16-bit outputs, bfloat16 and
 binary16 operands, batched slices and padded output rows; the small-tile
 results are also checked against the fp64 oracle.  The automatic choice is
 checked on the shapes it is for: the batch-1 linear of the addmm workload and
-the batch-1 SigLIP patch convolution.
+the batch-1 SigLIP patch convolution.  Binary32 products have two tile sizes
+of their own (64x64 and 32x32, the same 16x16x4 MFMA chain per element),
+compared the same way.
 """
 import pytest
 import torch
@@ -137,3 +139,31 @@ def test_auto_choice_on_batch1_linear_and_conv():
     torch.cuda.synchronize()
     assert bitwise_equal(auto, forced), "the automatic choice changes the bits"
     assert bitwise_equal(one[0], forced[0]), "row 0 alone differs from row 0 in the batch"
+
+
+@pytest.mark.parametrize("G,M,N,K", [(1, 1, 40, 4), (1, 37, 100, 130), (2, 70, 33, 512), (1, 200, 256, 4096)])
+@pytest.mark.parametrize("layout", ["plain", "transposed"])
+def test_f32_tiles_same_bits(G, M, N, K, layout):
+    # Binary32: 32x32 tiles (one 16x16 MFMA chain per wave) against 64x64
+    # tiles, with the K tail (K % 32 != 0), ragged M and N, transposed views,
+    # column and row bias, binary32 and bfloat16 outputs.
+    A = synth.randn((G, M, K), seed=M + K, dtype=torch.float32)
+    if layout == "plain":
+        B = synth.randn((G, K, N), seed=N + K, dtype=torch.float32, scale=0.05)
+    else:
+        A = synth.randn((G, K, M), seed=M + K, dtype=torch.float32).transpose(1, 2)
+        B = synth.randn((G, N, K), seed=N + K, dtype=torch.float32, scale=0.05).transpose(1, 2)
+    cb = synth.randn((N,), seed=3, dtype=torch.float32, scale=0.02)
+    rb = synth.randn((M,), seed=4, dtype=torch.float32, scale=0.02)
+    Ad, Bd, cbd, rbd = A.to(DEV), B.to(DEV), cb.to(DEV), rb.to(DEV)
+    for bias, rows in ((cbd, False), (rbd, True), (None, False)):
+        for od in (bi.BI_F32, bi.BI_BF16):
+            big = bi_bench.gemm_tile(Ad, Bd, 0, bias=bias, bias_rows=rows, out_dtype=od)
+            small = bi_bench.gemm_tile(Ad, Bd, 32, bias=bias, bias_rows=rows, out_dtype=od)
+            torch.cuda.synchronize()
+            assert bitwise_equal(small, big), f"fp32 32x32 tiles differ (bias_rows={rows}, out {od})"
+    small = bi_bench.gemm_tile(Ad, Bd, 32, bias=cbd, out_dtype=bi.BI_F32)
+    torch.cuda.synchronize()
+    for g in range(G):
+        assert_parity(to64(small[g]), oracle.mm(A[g], B[g], cb), f"fp32 small tile slice {g}")
+    assert bi_bench.gemm_tile_rows(G, M, N, K, bi.BI_F32) == 32
