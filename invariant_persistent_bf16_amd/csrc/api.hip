@@ -105,27 +105,32 @@ int gemm_check(const GemmDesc& d) {
     return BI_OK;
 }
 
-// Rows per block of the small-tile kernel for a 16-bit product, or 0 for the
-// persistent kernel: a function of the shape alone (both kernels give the same
-// bits).  The small tile is considered only where the 256x256 tiles do not
-// fill the compute units; then the estimated times decide.  Measured on
-// MI355X: a 256x256 tile costs about 0.52 us per 32-wide K step plus about
-// 6 us of launch, prologue and epilogue; the small-tile waves sustain about
-// 8 TB/s of operand reads from L2 (each block reads its rows of A and its 32
-// columns of B over the whole of K), and a wave needs about 0.15 us per K
-// step plus 2 us when it is latency bound.  Rows past M are not read.
+// The kernel for a 16-bit product, a function of the shape alone (every
+// choice gives the same bits): 0 = the persistent kernel with 256x256 tiles,
+// 1 = with 128x256 tiles, 32 / 64 / 128 = the small-tile kernel with blocks of
+// that many rows.  Estimated times fitted to measurements on MI355X: a
+// persistent tile costs about 0.52 us (256 rows) or 0.30 us (128 rows) per
+// 32-wide K step, in rounds of one tile per compute unit, plus about 6 us of
+// launch, prologue and epilogue; the small-tile waves sustain about 8 TB/s of
+// operand reads from L2 (each block reads its rows of A and its 32 columns of
+// B over the whole of K) and need about 0.15 us per K step plus 2 us when
+// latency bound.  Only products with at most two rounds of 256x256 tiles are
+// considered for the others (larger ones keep the 256x256 tile).
 int gemm_tile_rows(const GemmDesc& d, int cus) {
     const int64_t slices = d.G1 * d.G2;
     // Binary32: 32x32 tiles (one 16x16 MFMA chain per wave) where the 64x64
     // tiles do not fill the compute units.
     if (d.in_dtype == BI_F32) return slices * cdiv(d.M, G32_BM) * cdiv(d.N, G32_BN) < cus ? 32 : 0;
     const int64_t tiles = slices * cdiv(d.M, G16_BM) * cdiv(d.N, G16_BN);
-    if (tiles >= cus) return 0;
+    if (tiles >= 2 * (int64_t)cus) return 0;
     const int64_t nk = cdiv(d.K, G16_BK);
-    const double t_persistent = 6.0 + 0.52 * (double)nk;
-    const int64_t nblk = cdiv(d.N, 32);
-    double best = t_persistent;
+    const int64_t tiles128 = slices * cdiv(d.M, 128) * cdiv(d.N, G16_BN);
+    double best = 6.0 + 0.52 * (double)nk * (double)cdiv(tiles, cus);
     int best_rows = 0;
+    const double t_p128 = 6.0 + 0.30 * (double)nk * (double)cdiv(tiles128, cus);
+    if (t_p128 < best) { best = t_p128; best_rows = 1; }
+    if (tiles >= cus) return best_rows;
+    const int64_t nblk = cdiv(d.N, 32);
     for (int rows : {32, 64, 128}) {
         if (rows > 32 && d.M <= rows / 2) break;   // a taller block only adds empty rows
         const int64_t blocks = slices * cdiv(d.M, rows) * nblk;
@@ -159,8 +164,8 @@ int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override, int tile_r
         const bool out16 = d.out_dtype != BI_F32;
         const bool kc = d.K == 0 || (d.sBk == 1 && (d.N == 1 || d.sBn % 8 == 0));
         const int rows = tile_rows >= 0 ? tile_rows : grid_override > 0 ? 0 : gemm_tile_rows(d, cus);
-        if (rows != 0 && rows != 32 && rows != 64 && rows != 128) return BI_ERR_UNSUPPORTED;
-        if (rows > 0) {
+        if (rows != 0 && rows != 1 && rows != 32 && rows != 64 && rows != 128) return BI_ERR_UNSUPPORTED;
+        if (rows > 1) {
             GemmParams p;
             p.A = (const uint16_t*)d.A; p.B = (const uint16_t*)d.B;
             p.bias = (const uint16_t*)d.bias; p.C = d.C;
@@ -200,27 +205,32 @@ int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override, int tile_r
         p.G2 = d.G2;
         p.sA1 = d.sA1; p.sA2 = d.sA2; p.sB1 = d.sB1; p.sB2 = d.sB2;
         p.sC1 = d.sC1; p.sC2 = d.sC2; p.sBias2 = d.sBias2; p.bias_rows = d.bias_rows;
-        p.tiles_m = (int)cdiv(d.M, G16_BM);
+        const int bm = rows == 1 ? 128 : G16_BM;
+        p.tiles_m = (int)cdiv(d.M, bm);
         p.tiles_n = (int)cdiv(d.N, G16_BN);
         p.tiles_per_slice = p.tiles_m * p.tiles_n;
-        p.total_tiles = (int)(p.tiles_per_slice * d.G1 * d.G2);
+        const int64_t total = (int64_t)p.tiles_per_slice * d.G1 * d.G2;
+        if (total > (1ll << 30)) return BI_ERR_UNSUPPORTED;
+        p.total_tiles = (int)total;
         const int grid = grid_override > 0 ? grid_override : (p.total_tiles < cus ? p.total_tiles : cus);
         const int osz = out16 ? 2 : 4;
         const int vel = 16 / osz;   // elements per 16-byte chunk
         const bool cvec = aligned(d.C, 16) && d.N % vel == 0 && d.sCm % vel == 0 && d.sC1 % vel == 0 &&
                           d.sC2 % vel == 0;
         typedef void (*Kern)(GemmParams);
-        // [f16][B K-contiguous][16-bit out][vector epilogue]
-        static const Kern kerns[2][2][2][2] = {
-            {{{gemm_bf16_persistent<false, 0, false>, gemm_bf16_persistent<false, 0, true>},
-              {gemm_bf16_persistent<false, 1, false>, gemm_bf16_persistent<false, 1, true>}},
-             {{gemm_bf16_persistent<true, 0, false>, gemm_bf16_persistent<true, 0, true>},
-              {gemm_bf16_persistent<true, 1, false>, gemm_bf16_persistent<true, 1, true>}}},
-            {{{gemm_bf16_persistent<false, 0, false, true>, gemm_bf16_persistent<false, 0, true, true>},
-              {gemm_bf16_persistent<false, 1, false, true>, gemm_bf16_persistent<false, 1, true, true>}},
-             {{gemm_bf16_persistent<true, 0, false, true>, gemm_bf16_persistent<true, 0, true, true>},
-              {gemm_bf16_persistent<true, 1, false, true>, gemm_bf16_persistent<true, 1, true, true>}}}};
-        const Kern kern = kerns[d.in_dtype == BI_F16][kc][out16][cvec];
+        // [128-row tile][f16][B K-contiguous][16-bit out][vector epilogue]
+#define BI_G16_KERNS(BMV)                                                                                     \
+    {{{{gemm_bf16_persistent<false, 0, false, false, BMV>, gemm_bf16_persistent<false, 0, true, false, BMV>},    \
+       {gemm_bf16_persistent<false, 1, false, false, BMV>, gemm_bf16_persistent<false, 1, true, false, BMV>}},   \
+      {{gemm_bf16_persistent<true, 0, false, false, BMV>, gemm_bf16_persistent<true, 0, true, false, BMV>},      \
+       {gemm_bf16_persistent<true, 1, false, false, BMV>, gemm_bf16_persistent<true, 1, true, false, BMV>}}},    \
+     {{{gemm_bf16_persistent<false, 0, false, true, BMV>, gemm_bf16_persistent<false, 0, true, true, BMV>},      \
+       {gemm_bf16_persistent<false, 1, false, true, BMV>, gemm_bf16_persistent<false, 1, true, true, BMV>}},     \
+      {{gemm_bf16_persistent<true, 0, false, true, BMV>, gemm_bf16_persistent<true, 0, true, true, BMV>},        \
+       {gemm_bf16_persistent<true, 1, false, true, BMV>, gemm_bf16_persistent<true, 1, true, true, BMV>}}}}
+        static const Kern kerns[2][2][2][2][2] = {BI_G16_KERNS(256), BI_G16_KERNS(128)};
+#undef BI_G16_KERNS
+        const Kern kern = kerns[rows == 1][d.in_dtype == BI_F16][kc][out16][cvec];
         hipLaunchKernelGGL(kern, dim3(grid), dim3(G16_THREADS), 0, st, p);
     } else {
         GemmF32Params p;

@@ -58,13 +58,23 @@ constexpr int G16_BK = 32;
 constexpr int G16_THREADS = 256;
 constexpr int G16_GROUP_M = 8;
 constexpr int G16_NSTAGE = 4;
-constexpr int G16_STAGE_BYTES = G16_BM * G16_BK * 2;              // one operand tile: 16 KiB
-constexpr int G16_B_BASE = G16_NSTAGE * G16_STAGE_BYTES;          // B stages after the A stages
-constexpr int G16_RING_BYTES = 2 * G16_NSTAGE * G16_STAGE_BYTES;  // 128 KiB
-constexpr int G16_BIAS_BYTES = 2 * G16_BM * 4;                    // one tile's row and column bias, binary32
-constexpr int G16_LDS_BYTES = G16_RING_BYTES + 2 * G16_BIAS_BYTES; // + 4 KiB (double buffered)
-constexpr int G16_DMA_PER_TILE = 8;                               // per wave: 4 for A, 4 for B
 constexpr uint32_t G16_OOB = 0x80000000u;                         // buffer offset that reads as zero
+// Per-tile-height layout: BM = 256 (the tile above) or 128 (each wave 64x128,
+// for products whose 256x256 tiles leave compute units idle).
+template <int BM>
+struct G16Cfg {
+    static constexpr int WROWS = BM / 2;                        // rows of a wave's block
+    static constexpr int IM = WROWS / 32;                       // its 32-row MFMA blocks
+    static constexpr int A_STAGE = BM * G16_BK * 2;             // A tile of one K step
+    static constexpr int B_STAGE = G16_BN * G16_BK * 2;         // B tile of one K step
+    static constexpr int B_BASE = G16_NSTAGE * A_STAGE;         // B stages after the A stages
+    static constexpr int RING = G16_NSTAGE * (A_STAGE + B_STAGE);
+    static constexpr int BIAS = (BM + G16_BN) * 4;              // row and column bias, binary32
+    static constexpr int LDS = RING + 2 * BIAS;                 // bias double buffered
+    static constexpr int NA = BM / 64;                          // A copies per wave and step
+    static constexpr int NDMA = NA + 4;                         // + 4 B copies
+    static constexpr int NMF = 8 * IM;                          // MFMAs per wave and step
+};
 constexpr int32_t G16_RECORDS = 0x7fffffff;
 
 struct GemmParams {
@@ -157,10 +167,14 @@ struct G16Frags {
 // output) instead of bfloat16; the same tile, K order and schedule, the
 // pages' fixed configuration per dtype.  OUT_BF16: 16-bit output in the
 // operands' type (else binary32).
-template <bool B_KCONTIG, int OUT_BF16, bool CVEC, bool F16 = false>
+// BM: tile height, 256 or 128 (G16Cfg); the per-element arithmetic is the
+// same for both.
+template <bool B_KCONTIG, int OUT_BF16, bool CVEC, bool F16 = false, int BM = 256>
 __global__ void __launch_bounds__(G16_THREADS, 1)
 gemm_bf16_persistent(GemmParams p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[G16_LDS_BYTES];
+    using C = G16Cfg<BM>;
+    constexpr int IM = C::IM;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -182,7 +196,7 @@ gemm_bf16_persistent(GemmParams p) {
     const uint32_t lds0 = g16_lds_addr(smem);
     uint32_t a_fb[2], b_fb[4];
     {
-        const int R0 = wm * 128 + (lane & 31);
+        const int R0 = wm * C::WROWS + (lane & 31);
         const int x = (lane >> 5) ^ ((R0 >> 2) & 3);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) a_fb[kk] = lds0 + R0 * 64 + ((x ^ (2 * kk)) << 4);
@@ -190,14 +204,14 @@ gemm_bf16_persistent(GemmParams p) {
             const int N0 = wn * 128 + (lane & 31);
             const int xb = (lane >> 5) ^ ((N0 >> 2) & 3);
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) b_fb[kk] = lds0 + G16_B_BASE + N0 * 64 + ((xb ^ (2 * kk)) << 4);
+            for (int kk = 0; kk < 2; ++kk) b_fb[kk] = lds0 + C::B_BASE + N0 * 64 + ((xb ^ (2 * kk)) << 4);
             b_fb[2] = b_fb[3] = 0;
         } else {
             const int g = lane >> 4, li = lane & 15, z = li >> 2;
             const int y = 2 * (g & 1) + ((li & 3) >> 1);
 #pragma unroll
             for (int in = 0; in < 4; ++in)
-                b_fb[in] = lds0 + G16_B_BASE + (8 * (g >> 1) + z) * 512 +
+                b_fb[in] = lds0 + C::B_BASE + (8 * (g >> 1) + z) * 512 +
                            (16 * wn + 4 * (in ^ z) + y) * 16 + (li & 1) * 8;
         }
     }
@@ -213,7 +227,7 @@ gemm_bf16_persistent(GemmParams p) {
         const int pid_m = first_m + (t % width) % gsz;
         const int pid_n = (t % width) / gsz;
         const int64_t s1 = s / p.G2, s2 = s - (s / p.G2) * p.G2;
-        const int64_t m0 = (int64_t)pid_m * G16_BM, n0 = (int64_t)pid_n * G16_BN;
+        const int64_t m0 = (int64_t)pid_m * BM, n0 = (int64_t)pid_n * G16_BN;
         const uint16_t* Ab = p.A + s1 * p.sA1 + s2 * p.sA2 + m0 * p.sAm;
         const uint16_t* Bb;
         if constexpr (B_KCONTIG) Bb = p.B + s1 * p.sB1 + s2 * p.sB2 + n0 * p.sBn;
@@ -230,18 +244,19 @@ gemm_bf16_persistent(GemmParams p) {
         // physical chunk lane&31 of that row, i.e. logical chunk
         // (lane&31) ^ 4(krow&3), columns clamped to the last valid 8.
         const int a_u = (lane & 3) ^ ((lane >> 4) & 3);
-        const int a_row0 = 64 * wave + (lane >> 2);
-        uint32_t a_off[4], b_off[4];
+        const int a_row0 = (BM / 4) * wave + (lane >> 2);
+        const int b_row0 = 64 * wave + (lane >> 2);
+        uint32_t a_off[C::NA], b_off[4];
         {
             const int64_t a_rows_left = p.M - m0 - a_row0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < C::NA; ++j)
                 a_off[j] = a_rows_left > 16 * j ? (uint32_t)(((a_row0 + 16 * j) * (int)p.sAm + a_u * 8) * 2) : G16_OOB;
             if constexpr (B_KCONTIG) {
-                const int64_t b_rows_left = p.N - n0 - a_row0;
+                const int64_t b_rows_left = p.N - n0 - b_row0;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    b_off[j] = b_rows_left > 16 * j ? (uint32_t)(((a_row0 + 16 * j) * (int)p.sBn + a_u * 8) * 2) : G16_OOB;
+                    b_off[j] = b_rows_left > 16 * j ? (uint32_t)(((b_row0 + 16 * j) * (int)p.sBn + a_u * 8) * 2) : G16_OOB;
             } else {
                 const int ncl = (int)min<int64_t>(p.N - 8 - n0, 248);
 #pragma unroll
@@ -257,47 +272,50 @@ gemm_bf16_persistent(GemmParams p) {
         const __amdgpu_buffer_rsrc_t rsA = g16_rsrc(Ab), rsB = g16_rsrc(Bb);
         const uint32_t kstepB = B_KCONTIG ? 2u * G16_BK : (uint32_t)(2 * G16_BK * p.sBk);
 
-        // DMA copy j (0..7: 0..3 for A, 4..7 for B) of K tile kt into stage st;
-        // lanes past K read zeros.
+        // DMA copy j (0 .. NA-1 for A, NA .. NA+3 for B) of K tile kt into
+        // stage st; lanes past K read zeros.
         auto dma = [&](int kt, int st, auto jc) {
-            constexpr int j = decltype(jc)::value;
+            constexpr int j = decltype(jc)::value, jb = j - C::NA;
             const int kleft = K32 - kt * G16_BK;
-            if constexpr (j < 4) {
-                g16_dma(rsA, smem + st * G16_STAGE_BYTES + (wave * 4 + j) * 1024,
+            if constexpr (j < C::NA) {
+                g16_dma(rsA, smem + st * C::A_STAGE + (wave * C::NA + j) * 1024,
                         a_u8 < kleft ? a_off[j] : G16_OOB, (uint32_t)kt * (2u * G16_BK));
             } else if constexpr (B_KCONTIG) {
-                g16_dma(rsB, smem + G16_B_BASE + st * G16_STAGE_BYTES + (wave * 4 + j - 4) * 1024,
-                        a_u8 < kleft ? b_off[j - 4] : G16_OOB, (uint32_t)kt * kstepB);
+                g16_dma(rsB, smem + C::B_BASE + st * C::B_STAGE + (wave * 4 + jb) * 1024,
+                        a_u8 < kleft ? b_off[jb] : G16_OOB, (uint32_t)kt * kstepB);
             } else {
-                g16_dma(rsB, smem + G16_B_BASE + st * G16_STAGE_BYTES + (wave * 4 + j - 4) * 1024,
-                        bn_krow0 + 2 * (j - 4) < kleft ? b_off[j - 4] : G16_OOB, (uint32_t)kt * kstepB);
+                g16_dma(rsB, smem + C::B_BASE + st * C::B_STAGE + (wave * 4 + jb) * 1024,
+                        bn_krow0 + 2 * jb < kleft ? b_off[jb] : G16_OOB, (uint32_t)kt * kstepB);
             }
         };
-        // LDS read r (0..23) of the fragments of stage ST into F:
-        //  0..7 A [kk = r/4][im = r%4]; 8..23 B: K-contiguous [kk][in] (8..15),
-        //  N-contiguous [kk][in] half hr ((r-8) = kk*8 + in*2 + hr).
+        // LDS read r of the fragments of stage ST into F: 0 .. 2IM-1 A
+        // [kk = r/IM][im = r%IM]; then B (q = r - 2IM): K-contiguous [kk][in]
+        // (q = kk*4 + in), N-contiguous [kk][in] half hr (q = kk*8 + in*2 + hr).
         auto lds_read = [&](G16Frags& F, auto stc, auto rc) {
             constexpr int ST = decltype(stc)::value, r = decltype(rc)::value;
-            if constexpr (r < 8) {
-                constexpr int kk = r / 4, im = r % 4;
-                F.a[kk][im] = g16_read128<ST * G16_STAGE_BYTES + im * 2048>(a_fb[kk]);
+            if constexpr (r < 2 * IM) {
+                constexpr int kk = r / IM, im = r % IM;
+                F.a[kk][im] = g16_read128<ST * C::A_STAGE + im * 2048>(a_fb[kk]);
             } else if constexpr (B_KCONTIG) {
-                if constexpr (r < 16) {
-                    constexpr int kk = (r - 8) / 4, in = (r - 8) % 4;
-                    F.b[kk][in] = g16_read128<ST * G16_STAGE_BYTES + in * 2048>(b_fb[kk]);
+                if constexpr (r < 2 * IM + 8) {
+                    constexpr int kk = (r - 2 * IM) / 4, in = (r - 2 * IM) % 4;
+                    F.b[kk][in] = g16_read128<ST * C::B_STAGE + in * 2048>(b_fb[kk]);
                 }
             } else {
-                constexpr int q = r - 8, kk = q / 8, in = (q % 8) / 2, hr = q % 2;
-                const v2i32_t h = g16_read_tr<ST * G16_STAGE_BYTES + kk * 8192 + hr * 2048>(b_fb[in]);
+                constexpr int q = r - 2 * IM, kk = q / 8, in = (q % 8) / 2, hr = q % 2;
+                const v2i32_t h = g16_read_tr<ST * C::B_STAGE + kk * 8192 + hr * 2048>(b_fb[in]);
                 F.b[kk][in][2 * hr] = (uint32_t)h[0];
                 F.b[kk][in][2 * hr + 1] = (uint32_t)h[1];
             }
         };
         // Make the fragment registers of F depend on the preceding wait.
         auto fence_frags = [&](G16Frags& F) {
-            asm volatile("" : "+v"(F.a[0][0]), "+v"(F.a[0][1]), "+v"(F.a[0][2]), "+v"(F.a[0][3]),
-                              "+v"(F.a[1][0]), "+v"(F.a[1][1]), "+v"(F.a[1][2]), "+v"(F.a[1][3]),
-                              "+v"(F.b[0][0]), "+v"(F.b[0][1]), "+v"(F.b[0][2]), "+v"(F.b[0][3]),
+            if constexpr (IM == 4)
+                asm volatile("" : "+v"(F.a[0][0]), "+v"(F.a[0][1]), "+v"(F.a[0][2]), "+v"(F.a[0][3]),
+                                  "+v"(F.a[1][0]), "+v"(F.a[1][1]), "+v"(F.a[1][2]), "+v"(F.a[1][3]));
+            else
+                asm volatile("" : "+v"(F.a[0][0]), "+v"(F.a[0][1]), "+v"(F.a[1][0]), "+v"(F.a[1][1]));
+            asm volatile("" : "+v"(F.b[0][0]), "+v"(F.b[0][1]), "+v"(F.b[0][2]), "+v"(F.b[0][3]),
                               "+v"(F.b[1][0]), "+v"(F.b[1][1]), "+v"(F.b[1][2]), "+v"(F.b[1][3]));
         };
 
@@ -309,7 +327,7 @@ gemm_bf16_persistent(GemmParams p) {
         // each output still gets exactly one bias addition.  Entries past N
         // (or M) repeat the last valid one and are never stored.
         const uint16_t* bb = p.bias ? p.bias + s2 * p.sBias2 : nullptr;
-        float* bias_lds = (float*)(smem + G16_RING_BYTES + (ti & 1) * G16_BIAS_BYTES);
+        float* bias_lds = (float*)(smem + C::RING + (ti & 1) * C::BIAS);
         float brow_t = -0.0f, bcol_t = -0.0f;
         if (bb) {
             const int64_t b0 = p.bias_rows ? m0 : n0;
@@ -319,16 +337,16 @@ gemm_bf16_persistent(GemmParams p) {
             else             bcol_t = b;
         }
 
-        f32x16_t acc[4][4];
+        f32x16_t acc[IM][4];
 #pragma unroll
-        for (int im = 0; im < 4; ++im)
+        for (int im = 0; im < IM; ++im)
 #pragma unroll
             for (int in = 0; in < 4; ++in)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[im][in][r] = 0.0f;
 
         G16Frags F0, F1;
-        constexpr int NREAD = B_KCONTIG ? 16 : 24;
+        constexpr int NREAD = 2 * IM + (B_KCONTIG ? 8 : 16);
 
         // One K step kt (stage ST = kt % 4): wait for step kt+1's copy and for
         // the reads of step kt's fragments, barrier, then 32 MFMAs on
@@ -341,24 +359,38 @@ gemm_bf16_persistent(GemmParams p) {
             constexpr int ST = decltype(stc)::value;
             G16Frags& cur = (ST & 1) ? F1 : F0;
             G16Frags& nxt = (ST & 1) ? F0 : F1;
-            g16_wait_vm_lgkm0<2 * G16_DMA_PER_TILE>();
+            g16_wait_vm_lgkm0<2 * C::NDMA>();
             __builtin_amdgcn_s_barrier();
             fence_frags(cur);
             __builtin_amdgcn_sched_barrier(0);
-            g16_static_for<0, 32>([&](auto ic) {
+            g16_static_for<0, C::NMF>([&](auto ic) {
                 constexpr int i = decltype(ic)::value;
-                constexpr int kk = i / 16, im = (i / 4) % 4, in = i % 4;
+                constexpr int kk = i / (4 * IM), im = (i / 4) % IM, in = i % 4;
                 if constexpr (F16)
                     acc[im][in] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
                         as_f16x8(cur.b[kk][in]), as_f16x8(cur.a[kk][im]), acc[im][in], 0, 0, 0);
                 else
                     acc[im][in] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         as_bf16x8(cur.b[kk][in]), as_bf16x8(cur.a[kk][im]), acc[im][in], 0, 0, 0);
-                constexpr int slot = g16_slot<B_KCONTIG>(i);
-                if constexpr (slot >= 0 && slot < 32) {
-                    lds_read(nxt, std::integral_constant<int, (ST + 1) % 4>{}, std::integral_constant<int, slot>{});
-                } else if constexpr (slot >= 32) {
-                    dma(kt + 4, ST, std::integral_constant<int, slot - 32>{});
+                if constexpr (BM == 256) {
+                    constexpr int slot = g16_slot<B_KCONTIG>(i);
+                    if constexpr (slot >= 0 && slot < 32) {
+                        lds_read(nxt, std::integral_constant<int, (ST + 1) % 4>{}, std::integral_constant<int, slot>{});
+                    } else if constexpr (slot >= 32) {
+                        dma(kt + 4, ST, std::integral_constant<int, slot - 32>{});
+                    }
+                } else {
+                    // Reads and copies spread evenly over the step's MFMAs: read r
+                    // after MFMA r * NMF / NREAD, copy d after (2d + 1) NMF / (2 NDMA).
+                    g16_static_for<0, NREAD>([&](auto rc) {
+                        constexpr int r = decltype(rc)::value;
+                        if constexpr (r * C::NMF / NREAD == i)
+                            lds_read(nxt, std::integral_constant<int, (ST + 1) % 4>{}, rc);
+                    });
+                    g16_static_for<0, C::NDMA>([&](auto dc) {
+                        constexpr int d = decltype(dc)::value;
+                        if constexpr ((2 * d + 1) * C::NMF / (2 * C::NDMA) == i) dma(kt + 4, ST, dc);
+                    });
                 }
                 __builtin_amdgcn_sched_barrier(0);
             });
@@ -367,11 +399,11 @@ gemm_bf16_persistent(GemmParams p) {
         // Prologue: copies of steps 0..3 into stages 0..3, wait for step 0,
         // read its fragments.
         g16_static_for<0, 4>([&](auto sc) {
-            g16_static_for<0, 8>([&](auto jc) { dma(decltype(sc)::value, decltype(sc)::value, jc); });
+            g16_static_for<0, C::NDMA>([&](auto jc) { dma(decltype(sc)::value, decltype(sc)::value, jc); });
         });
-        g16_wait_vm_lgkm0<3 * G16_DMA_PER_TILE>();
-        bias_lds[tid] = brow_t;
-        bias_lds[G16_BM + tid] = bcol_t;
+        g16_wait_vm_lgkm0<3 * C::NDMA>();
+        if (tid < BM) bias_lds[tid] = brow_t;
+        bias_lds[BM + tid] = bcol_t;
         __builtin_amdgcn_s_barrier();
         g16_static_for<0, NREAD>([&](auto rc) { lds_read(F0, std::integral_constant<int, 0>{}, rc); });
 
@@ -407,10 +439,10 @@ gemm_bf16_persistent(GemmParams p) {
         {
             using OutT = typename std::conditional<OUT_BF16 != 0, uint16_t, float>::type;
             constexpr int ESZ = (int)sizeof(OutT);
-            const int64_t row_w = m0 + wm * 128, col_w = n0 + wn * 128;
+            const int64_t row_w = m0 + wm * C::WROWS, col_w = n0 + wn * 128;
             OutT* Cw = (OutT*)p.C + s1 * p.sC1 + s2 * p.sC2 + row_w * p.sCm + col_w;
             const int sCm = (int)p.sCm;
-            const int rows_valid = (int)min<int64_t>(p.M - row_w, 128);
+            const int rows_valid = (int)min<int64_t>(p.M - row_w, C::WROWS);
             const int cols_valid = (int)min<int64_t>(p.N - col_w, 128);
             if (rows_valid > 0 && cols_valid > 0) {
                 // An opaque copy of the lane id keeps every epilogue value below
@@ -418,8 +450,8 @@ gemm_bf16_persistent(GemmParams p) {
                 int lane_e = lane;
                 asm volatile("" : "+v"(lane_e));
                 const int lrow = lane_e & 31, lh = lane_e >> 5, lcol = 4 * lh;
-                const float* brow_w = bias_lds + wm * 128;
-                const float* bcol_w = bias_lds + G16_BM + wn * 128;
+                const float* brow_w = bias_lds + wm * C::WROWS;
+                const float* bcol_w = bias_lds + BM + wn * 128;
                 const uint64_t cv = (uint64_t)Cw;
                 const uint32_t clo = __builtin_amdgcn_readfirstlane((uint32_t)cv);
                 const uint32_t chi = __builtin_amdgcn_readfirstlane((uint32_t)(cv >> 32));
@@ -427,10 +459,10 @@ gemm_bf16_persistent(GemmParams p) {
                 const __amdgpu_buffer_rsrc_t rsC = __builtin_amdgcn_make_buffer_rsrc(
                     (void*)(((uint64_t)chi << 32) | clo), (short)0, nrec, 0x00020000);
                 // The lane's bias values, read before any staging write.
-                float brv[4];
+                float brv[IM];
                 f32x4_t bcv[16];
 #pragma unroll
-                for (int im = 0; im < 4; ++im) brv[im] = brow_w[im * 32 + lrow];
+                for (int im = 0; im < IM; ++im) brv[im] = brow_w[im * 32 + lrow];
 #pragma unroll
                 for (int q = 0; q < 16; ++q) bcv[q] = *(const f32x4_t*)(bcol_w + (q / 4) * 32 + 8 * (q % 4) + lcol);
                 // Block (im, in), group g with bias added, in binary32.
@@ -447,16 +479,17 @@ gemm_bf16_persistent(GemmParams p) {
                     constexpr int PASSES = OUT_BF16 ? 1 : 2;
                     constexpr int ROWB = 128 * ESZ;       // bytes of one staged row
                     constexpr int NCH = ROWB / 16;        // 16-byte chunks per row
-                    constexpr int RPP = 128 / PASSES;     // rows per pass
+                    constexpr int RPP = C::WROWS / PASSES;  // rows per pass
                     constexpr int RPI = 64 / NCH;         // rows per read instruction
-                    uint8_t* stg = smem + wave * (G16_RING_BYTES / 4);
+                    uint8_t* stg = smem + wave * (C::RING / 4);
+                    static_assert(RPP * ROWB <= C::RING / 4, "a pass fits the wave's share of the ring");
                     const int t = lane_e % NCH, rsub = lane_e / NCH;
                     const bool col_ok = t * (16 / ESZ) < cols_valid;
                     g16_static_for<0, PASSES>([&](auto pc) {
                         constexpr int ps = decltype(pc)::value;
-                        g16_static_for<0, 4 / PASSES>([&](auto ic) {
-                            constexpr int im = ps * (4 / PASSES) + decltype(ic)::value;
-                            const int r = (im % (4 / PASSES)) * 32 + lrow;
+                        g16_static_for<0, IM / PASSES>([&](auto ic) {
+                            constexpr int im = ps * (IM / PASSES) + decltype(ic)::value;
+                            const int r = (im % (IM / PASSES)) * 32 + lrow;
                             g16_static_for<0, 16>([&](auto qc) {
                                 constexpr int in = decltype(qc)::value / 4, g = decltype(qc)::value % 4;
                                 const f32x4_t v = value(std::integral_constant<int, im>{}, qc);
@@ -479,7 +512,7 @@ gemm_bf16_persistent(GemmParams p) {
                         });
                     });
                 } else {
-                    g16_static_for<0, 4>([&](auto imc) {
+                    g16_static_for<0, IM>([&](auto imc) {
                         constexpr int im = decltype(imc)::value;
                         const int vrow = ((im * 32 + lrow) * sCm) * ESZ;
                         g16_static_for<0, 16>([&](auto qc) {

@@ -2,7 +2,8 @@
 
 The library computes a 16-bit product either with the persistent 256x256
 kernel or, where those tiles would leave most compute units idle, with
-one-wave (32, 64 or 128) x 32 blocks; the choice is a function of the shape.
+one-wave (32, 64 or 128) x 32 blocks, or with 128x256 persistent tiles; the
+choice is a function of the shape.
 Both must give the same bits for every element.  Here each forced tile size is
 compared bit for bit with the persistent kernel on ragged shapes (M, N, K
 tails, one row, K = 8), both B layouts, column bias (addmm) and row bias (the
@@ -26,7 +27,7 @@ pytestmark = pytest.mark.gpu
 if torch.cuda.is_available():
     from invariant_persistent_bf16_amd import bi, bi_bench
 DEV = "cuda"
-TILES = (32, 64, 128)
+TILES = (1, 32, 64, 128)   # 1: the persistent kernel with 128-row tiles
 
 
 def _operands(G, M, N, K, b_layout, dtype, seed):
@@ -105,10 +106,12 @@ def test_small_tiles_element_epilogue():
     for od, tdt in ((bi.BI_F32, torch.float32), (bi.BI_BF16, torch.bfloat16)):
         big = torch.full((M, N + 3), 7.0, dtype=tdt, device=DEV)
         ref = bi_bench.gemm_tile(A, B, 0, bias=bias, out_dtype=od)
-        out = bi_bench.gemm_tile(A, B, 32, bias=bias, out_dtype=od, out=big[:, :N])
-        torch.cuda.synchronize()
-        assert bitwise_equal(out, ref), "element epilogue changes the bits"
-        assert torch.all(big[:, N:] == 7.0), "a store landed past N"
+        for t in (1, 32):
+            big.fill_(7.0)
+            out = bi_bench.gemm_tile(A, B, t, bias=bias, out_dtype=od, out=big[:, :N])
+            torch.cuda.synchronize()
+            assert bitwise_equal(out, ref), f"element epilogue changes the bits (tile {t})"
+            assert torch.all(big[:, N:] == 7.0), f"a store landed past N (tile {t})"
 
 
 def test_small_tile_k_zero():
@@ -125,14 +128,14 @@ def test_auto_choice_on_batch1_linear_and_conv():
     # every choice gives row 0 (sample 0) the same bits.
     assert bi_bench.gemm_tile_rows(1, 1, 14336, 4096) == 32
     assert bi_bench.gemm_tile_rows(1, 64, 14336, 4096) == 64
-    assert bi_bench.gemm_tile_rows(1, 96, 14336, 4096) == 128
-    assert bi_bench.gemm_tile_rows(1, 200, 14336, 4096) == 0
+    assert bi_bench.gemm_tile_rows(1, 200, 14336, 4096) == 1      # 128-row persistent tiles
+    assert bi_bench.gemm_tile_rows(1, 512, 14336, 4096) == 1
     assert bi_bench.gemm_tile_rows(1, 8192, 14336, 4096) == 0
     assert bi_bench.gemm_tile_rows(1, 1152, 256, 592) == 32      # conv, one image
     assert bi_bench.gemm_tile_rows(32, 1152, 256, 592) == 0      # conv, 32 images
     W, bias, x0 = synth.addmm_shared()
     Wd, bd = W.to(DEV), bias.to(DEV)
-    X = synth.addmm_batch(x0, 96, device=DEV)
+    X = synth.addmm_batch(x0, 200, device=DEV)
     auto = bi.bi_addmm(bd, X, Wd, out_dtype=bi.BI_F32)
     forced = bi_bench.gemm_tile(X, Wd, 0, bias=bd, out_dtype=bi.BI_F32)
     one = bi.bi_addmm(bd, X[:1].contiguous(), Wd, out_dtype=bi.BI_F32)
