@@ -169,7 +169,11 @@ row_op_kernel(const void* __restrict__ X, int64_t ldx, const void* __restrict__ 
                     f32x4_t y;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) y[e] = (x[e] - m) - ls;
-                    row_store<VEC>(ry, c, y, out_bf16 != 0);
+                    // Non-temporal: log-probabilities over a vocabulary are far
+                    // larger than the caches.  (Inputs, and RMSNorm's output,
+                    // keep the default policy: a layer's activations are
+                    // typically still in the 256 MB cache when the next op reads them.)
+                    row_store<VEC, 2>(ry, c, y, out_bf16 != 0);
                 };
                 if constexpr (NCH > 0) {
 #pragma unroll
