@@ -1,35 +1,53 @@
-"""Build the HIP library (gfx950 only) in-tree: invariant_persistent_bf16_amd/libbi.so.
+"""Build the HIP libraries (gfx950 only) in-tree: invariant_persistent_bf16_amd/libbi.so
+and libbi_bench.so.
 
-One translation unit per library; every kernel is compiled for gfx950 with
--O3, no fast-math, floating-point contraction off (each a*b+c in the source
-is two roundings unless written as fmaf), and the packed-fp32 feature off.
+Every source is compiled to an object of its own (in parallel; the persistent
+GEMM's tile shapes sit in separate sources for that reason), then each library
+is linked from its objects.  Every kernel is compiled for gfx950 with -O3, no
+fast-math, floating-point contraction off (each a*b+c in the source is two
+roundings unless written as fmaf), and the packed-fp32 feature off.
 """
 import os
 import subprocess
+from concurrent.futures import ThreadPoolExecutor
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_HERE)
+_OBJ = os.path.join(_HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
-         "-ffp-contract=off", "-fno-fast-math",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
+CFLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
+          "-ffp-contract=off", "-fno-fast-math",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
+LDFLAGS = [f"--offload-arch={ARCH}", "-fPIC", "-shared"]
 
+GEMM16 = ["csrc/gemm16_256x256.hip", "csrc/gemm16_128x256.hip", "csrc/gemm16_256x128.hip"]
 LIBS = {
-    "libbi.so": ["csrc/api.hip"],
-    "libbi_bench.so": ["csrc/api.hip", "csrc/bench_api.hip"],
+    "libbi.so": ["csrc/api.hip"] + GEMM16,
+    "libbi_bench.so": ["csrc/api.hip", "csrc/bench_api.hip"] + GEMM16,
 }
 
 
-def build_one(name, verbose=False):
-    srcs = [os.path.join(_HERE, s) for s in LIBS[name]]
-    srcs = [s for s in srcs if os.path.exists(s)]
-    if not srcs:
-        return None
+def _obj(src):
+    return os.path.join(_OBJ, os.path.basename(src).replace(".hip", ".o"))
+
+
+def _compile(src, verbose):
+    out = _obj(src)
+    tmp = out + ".tmp.o"
+    cmd = [HIPCC] + CFLAGS + ["-I", os.path.join(_ROOT, "include"), "-c", os.path.join(_HERE, src), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def _link(name, verbose):
     out = os.path.join(_HERE, name)
     tmp = out + ".tmp"
-    cmd = [HIPCC] + FLAGS + ["-I", os.path.join(_ROOT, "include")] + srcs + ["-o", tmp]
+    cmd = [HIPCC] + LDFLAGS + [_obj(s) for s in LIBS[name]] + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
@@ -38,10 +56,11 @@ def build_one(name, verbose=False):
 
 
 def build(verbose=False):
-    from concurrent.futures import ThreadPoolExecutor
-    with ThreadPoolExecutor(max_workers=len(LIBS)) as ex:
-        outs = list(ex.map(lambda n: build_one(n, verbose), LIBS))
-    return [o for o in outs if o]
+    os.makedirs(_OBJ, exist_ok=True)
+    srcs = sorted({s for v in LIBS.values() for s in v})
+    with ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 4)) as ex:
+        list(ex.map(lambda s: _compile(s, verbose), srcs))
+    return [_link(n, verbose) for n in LIBS]
 
 
 if __name__ == "__main__":

@@ -107,9 +107,9 @@ int gemm_check(const GemmDesc& d) {
 
 // The kernel for a 16-bit product, a function of the shape alone (every
 // choice gives the same bits): 0 = the persistent kernel with 256x256 tiles,
-// 1 = with 128x256 tiles, 32 / 64 / 128 = the small-tile kernel with blocks of
-// that many rows.  Estimated times fitted to measurements on MI355X: a
-// persistent tile costs about 0.52 us (256 rows) or 0.30 us (128 rows) per
+// 1 = with 128x256 tiles, 2 = with 256x128 tiles (N <= 128), 32 / 64 / 128 =
+// the small-tile kernel with blocks of that many rows.  Estimated times fitted to measurements on MI355X: a
+// persistent tile costs about 0.52 us (256x256) or 0.30 us (128 rows or columns) per
 // 32-wide K step, in rounds of one tile per compute unit, plus about 6 us of
 // launch, prologue and epilogue; the small-tile waves sustain about 8 TB/s of
 // operand reads from L2 (each block reads its rows of A and its 32 columns of
@@ -122,11 +122,14 @@ int gemm_tile_rows(const GemmDesc& d, int cus) {
     // tiles do not fill the compute units.
     if (d.in_dtype == BI_F32) return slices * cdiv(d.M, G32_BM) * cdiv(d.N, G32_BN) < cus ? 32 : 0;
     const int64_t tiles = slices * cdiv(d.M, G16_BM) * cdiv(d.N, G16_BN);
-    if (tiles >= 2 * (int64_t)cus) return 0;
+    // N <= 128 fills half of a 256-wide tile: the 256x128 tile (returned as 2)
+    // does the same rows with half the MFMA work and B traffic.
+    const bool narrow = d.N <= 128;
+    if (tiles >= 2 * (int64_t)cus) return narrow ? 2 : 0;
     const int64_t nk = cdiv(d.K, G16_BK);
     const int64_t tiles128 = slices * cdiv(d.M, 128) * cdiv(d.N, G16_BN);
-    double best = 6.0 + 0.52 * (double)nk * (double)cdiv(tiles, cus);
-    int best_rows = 0;
+    double best = 6.0 + (narrow ? 0.30 : 0.52) * (double)nk * (double)cdiv(tiles, cus);
+    int best_rows = narrow ? 2 : 0;
     const double t_p128 = 6.0 + 0.30 * (double)nk * (double)cdiv(tiles128, cus);
     if (t_p128 < best) { best = t_p128; best_rows = 1; }
     if (tiles >= cus) return best_rows;
@@ -164,8 +167,9 @@ int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override, int tile_r
         const bool out16 = d.out_dtype != BI_F32;
         const bool kc = d.K == 0 || (d.sBk == 1 && (d.N == 1 || d.sBn % 8 == 0));
         const int rows = tile_rows >= 0 ? tile_rows : grid_override > 0 ? 0 : gemm_tile_rows(d, cus);
-        if (rows != 0 && rows != 1 && rows != 32 && rows != 64 && rows != 128) return BI_ERR_UNSUPPORTED;
-        if (rows > 1) {
+        if (rows != 0 && rows != 1 && rows != 2 && rows != 32 && rows != 64 && rows != 128)
+            return BI_ERR_UNSUPPORTED;
+        if (rows > 2) {
             GemmParams p;
             p.A = (const uint16_t*)d.A; p.B = (const uint16_t*)d.B;
             p.bias = (const uint16_t*)d.bias; p.C = d.C;
@@ -205,9 +209,9 @@ int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override, int tile_r
         p.G2 = d.G2;
         p.sA1 = d.sA1; p.sA2 = d.sA2; p.sB1 = d.sB1; p.sB2 = d.sB2;
         p.sC1 = d.sC1; p.sC2 = d.sC2; p.sBias2 = d.sBias2; p.bias_rows = d.bias_rows;
-        const int bm = rows == 1 ? 128 : G16_BM;
+        const int bm = rows == 1 ? 128 : G16_BM, bn = rows == 2 ? 128 : G16_BN;
         p.tiles_m = (int)cdiv(d.M, bm);
-        p.tiles_n = (int)cdiv(d.N, G16_BN);
+        p.tiles_n = (int)cdiv(d.N, bn);
         p.tiles_per_slice = p.tiles_m * p.tiles_n;
         const int64_t total = (int64_t)p.tiles_per_slice * d.G1 * d.G2;
         if (total > (1ll << 30)) return BI_ERR_UNSUPPORTED;
@@ -217,20 +221,10 @@ int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override, int tile_r
         const int vel = 16 / osz;   // elements per 16-byte chunk
         const bool cvec = aligned(d.C, 16) && d.N % vel == 0 && d.sCm % vel == 0 && d.sC1 % vel == 0 &&
                           d.sC2 % vel == 0;
-        typedef void (*Kern)(GemmParams);
-        // [128-row tile][f16][B K-contiguous][16-bit out][vector epilogue]
-#define BI_G16_KERNS(BMV)                                                                                     \
-    {{{{gemm_bf16_persistent<false, 0, false, false, BMV>, gemm_bf16_persistent<false, 0, true, false, BMV>},    \
-       {gemm_bf16_persistent<false, 1, false, false, BMV>, gemm_bf16_persistent<false, 1, true, false, BMV>}},   \
-      {{gemm_bf16_persistent<true, 0, false, false, BMV>, gemm_bf16_persistent<true, 0, true, false, BMV>},      \
-       {gemm_bf16_persistent<true, 1, false, false, BMV>, gemm_bf16_persistent<true, 1, true, false, BMV>}}},    \
-     {{{gemm_bf16_persistent<false, 0, false, true, BMV>, gemm_bf16_persistent<false, 0, true, true, BMV>},      \
-       {gemm_bf16_persistent<false, 1, false, true, BMV>, gemm_bf16_persistent<false, 1, true, true, BMV>}},     \
-      {{gemm_bf16_persistent<true, 0, false, true, BMV>, gemm_bf16_persistent<true, 0, true, true, BMV>},        \
-       {gemm_bf16_persistent<true, 1, false, true, BMV>, gemm_bf16_persistent<true, 1, true, true, BMV>}}}}
-        static const Kern kerns[2][2][2][2][2] = {BI_G16_KERNS(256), BI_G16_KERNS(128)};
-#undef BI_G16_KERNS
-        const Kern kern = kerns[rows == 1][d.in_dtype == BI_F16][kc][out16][cvec];
+        const int f16 = d.in_dtype == BI_F16;
+        const Gemm16Kern kern = rows == 1 ? gemm16_kernel_128x256(f16, kc, out16, cvec)
+                              : rows == 2 ? gemm16_kernel_256x128(f16, kc, out16, cvec)
+                                          : gemm16_kernel_256x256(f16, kc, out16, cvec);
         hipLaunchKernelGGL(kern, dim3(grid), dim3(G16_THREADS), 0, st, p);
     } else {
         GemmF32Params p;

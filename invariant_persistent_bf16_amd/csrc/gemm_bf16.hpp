@@ -59,21 +59,28 @@ constexpr int G16_THREADS = 256;
 constexpr int G16_GROUP_M = 8;
 constexpr int G16_NSTAGE = 4;
 constexpr uint32_t G16_OOB = 0x80000000u;                         // buffer offset that reads as zero
-// Per-tile-height layout: BM = 256 (the tile above) or 128 (each wave 64x128,
-// for products whose 256x256 tiles leave compute units idle).
-template <int BM>
+// Layout per tile shape: BM x BN = 256 x 256 (the tile above), 128 x 256
+// (each wave 64x128, for products whose 256x256 tiles leave compute units
+// idle) or 256 x 128 (each wave 128x64, for N <= 128, which would fill half
+// of a 256-wide tile).
+template <int BM, int BN>
 struct G16Cfg {
     static constexpr int WROWS = BM / 2;                        // rows of a wave's block
+    static constexpr int WCOLS = BN / 2;                        // its columns
     static constexpr int IM = WROWS / 32;                       // its 32-row MFMA blocks
+    static constexpr int IN = WCOLS / 32;                       // its 32-column MFMA blocks
     static constexpr int A_STAGE = BM * G16_BK * 2;             // A tile of one K step
-    static constexpr int B_STAGE = G16_BN * G16_BK * 2;         // B tile of one K step
+    static constexpr int B_STAGE = BN * G16_BK * 2;             // B tile of one K step
     static constexpr int B_BASE = G16_NSTAGE * A_STAGE;         // B stages after the A stages
     static constexpr int RING = G16_NSTAGE * (A_STAGE + B_STAGE);
-    static constexpr int BIAS = (BM + G16_BN) * 4;              // row and column bias, binary32
+    static constexpr int BIAS = (BM + BN) * 4;                  // row and column bias, binary32
     static constexpr int LDS = RING + 2 * BIAS;                 // bias double buffered
     static constexpr int NA = BM / 64;                          // A copies per wave and step
-    static constexpr int NDMA = NA + 4;                         // + 4 B copies
-    static constexpr int NMF = 8 * IM;                          // MFMAs per wave and step
+    static constexpr int NB = BN / 64;                          // B copies per wave and step
+    static constexpr int NDMA = NA + NB;
+    static constexpr int NMF = 2 * IM * IN;                     // MFMAs per wave and step
+    static constexpr int RB = BN * 2;                           // bytes of an N-contiguous B row in LDS
+    static constexpr int LPR = RB / 16;                         // lanes per such row in one copy
 };
 constexpr int32_t G16_RECORDS = 0x7fffffff;
 
@@ -167,13 +174,13 @@ struct G16Frags {
 // output) instead of bfloat16; the same tile, K order and schedule, the
 // pages' fixed configuration per dtype.  OUT_BF16: 16-bit output in the
 // operands' type (else binary32).
-// BM: tile height, 256 or 128 (G16Cfg); the per-element arithmetic is the
-// same for both.
-template <bool B_KCONTIG, int OUT_BF16, bool CVEC, bool F16 = false, int BM = 256>
+// BM x BN: tile shape, 256 x 256, 128 x 256 or 256 x 128 (G16Cfg); the
+// per-element arithmetic is the same for all.
+template <bool B_KCONTIG, int OUT_BF16, bool CVEC, bool F16 = false, int BM = 256, int BN = 256>
 __global__ void __launch_bounds__(G16_THREADS, 1)
 gemm_bf16_persistent(GemmParams p) {
-    using C = G16Cfg<BM>;
-    constexpr int IM = C::IM;
+    using C = G16Cfg<BM, BN>;
+    constexpr int IM = C::IM, IN = C::IN;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
 
     const int tid = threadIdx.x;
@@ -201,7 +208,7 @@ gemm_bf16_persistent(GemmParams p) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) a_fb[kk] = lds0 + R0 * 64 + ((x ^ (2 * kk)) << 4);
         if constexpr (B_KCONTIG) {
-            const int N0 = wn * 128 + (lane & 31);
+            const int N0 = wn * C::WCOLS + (lane & 31);
             const int xb = (lane >> 5) ^ ((N0 >> 2) & 3);
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) b_fb[kk] = lds0 + C::B_BASE + N0 * 64 + ((xb ^ (2 * kk)) << 4);
@@ -210,9 +217,9 @@ gemm_bf16_persistent(GemmParams p) {
             const int g = lane >> 4, li = lane & 15, z = li >> 2;
             const int y = 2 * (g & 1) + ((li & 3) >> 1);
 #pragma unroll
-            for (int in = 0; in < 4; ++in)
-                b_fb[in] = lds0 + C::B_BASE + (8 * (g >> 1) + z) * 512 +
-                           (16 * wn + 4 * (in ^ z) + y) * 16 + (li & 1) * 8;
+            for (int in = 0; in < IN; ++in)
+                b_fb[in] = lds0 + C::B_BASE + (8 * (g >> 1) + z) * C::RB +
+                           ((((IN * wn + in) ^ z) << 2) + y) * 16 + (li & 1) * 8;
         }
     }
 
@@ -227,7 +234,7 @@ gemm_bf16_persistent(GemmParams p) {
         const int pid_m = first_m + (t % width) % gsz;
         const int pid_n = (t % width) / gsz;
         const int64_t s1 = s / p.G2, s2 = s - (s / p.G2) * p.G2;
-        const int64_t m0 = (int64_t)pid_m * BM, n0 = (int64_t)pid_n * G16_BN;
+        const int64_t m0 = (int64_t)pid_m * BM, n0 = (int64_t)pid_n * BN;
         const uint16_t* Ab = p.A + s1 * p.sA1 + s2 * p.sA2 + m0 * p.sAm;
         const uint16_t* Bb;
         if constexpr (B_KCONTIG) Bb = p.B + s1 * p.sB1 + s2 * p.sB2 + n0 * p.sBn;
@@ -245,8 +252,8 @@ gemm_bf16_persistent(GemmParams p) {
         // (lane&31) ^ 4(krow&3), columns clamped to the last valid 8.
         const int a_u = (lane & 3) ^ ((lane >> 4) & 3);
         const int a_row0 = (BM / 4) * wave + (lane >> 2);
-        const int b_row0 = 64 * wave + (lane >> 2);
-        uint32_t a_off[C::NA], b_off[4];
+        const int b_row0 = (BN / 4) * wave + (lane >> 2);
+        uint32_t a_off[C::NA], b_off[C::NB];
         {
             const int64_t a_rows_left = p.M - m0 - a_row0;
 #pragma unroll
@@ -255,24 +262,24 @@ gemm_bf16_persistent(GemmParams p) {
             if constexpr (B_KCONTIG) {
                 const int64_t b_rows_left = p.N - n0 - b_row0;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < C::NB; ++j)
                     b_off[j] = b_rows_left > 16 * j ? (uint32_t)(((b_row0 + 16 * j) * (int)p.sBn + a_u * 8) * 2) : G16_OOB;
             } else {
-                const int ncl = (int)min<int64_t>(p.N - 8 - n0, 248);
+                const int ncl = (int)min<int64_t>(p.N - 8 - n0, BN - 8);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int krow = 8 * wave + 2 * j + (lane >> 5);
-                    const int col = min(((lane & 31) ^ (4 * (krow & 3))) << 3, ncl);
+                for (int j = 0; j < C::NB; ++j) {
+                    const int krow = 8 * wave + (1024 / C::RB) * j + lane / C::LPR;
+                    const int col = min(((lane % C::LPR) ^ (4 * (krow & 3))) << 3, ncl);
                     b_off[j] = (uint32_t)((krow * (int)p.sBk + col) * 2);
                 }
             }
         }
         const int a_u8 = a_u * 8;
-        const int bn_krow0 = 8 * wave + (lane >> 5);
+        const int bn_krow0 = 8 * wave + lane / C::LPR;
         const __amdgpu_buffer_rsrc_t rsA = g16_rsrc(Ab), rsB = g16_rsrc(Bb);
         const uint32_t kstepB = B_KCONTIG ? 2u * G16_BK : (uint32_t)(2 * G16_BK * p.sBk);
 
-        // DMA copy j (0 .. NA-1 for A, NA .. NA+3 for B) of K tile kt into
+        // DMA copy j (0 .. NA-1 for A, NA .. NA+NB-1 for B) of K tile kt into
         // stage st; lanes past K read zeros.
         auto dma = [&](int kt, int st, auto jc) {
             constexpr int j = decltype(jc)::value, jb = j - C::NA;
@@ -281,29 +288,29 @@ gemm_bf16_persistent(GemmParams p) {
                 g16_dma(rsA, smem + st * C::A_STAGE + (wave * C::NA + j) * 1024,
                         a_u8 < kleft ? a_off[j] : G16_OOB, (uint32_t)kt * (2u * G16_BK));
             } else if constexpr (B_KCONTIG) {
-                g16_dma(rsB, smem + C::B_BASE + st * C::B_STAGE + (wave * 4 + jb) * 1024,
+                g16_dma(rsB, smem + C::B_BASE + st * C::B_STAGE + (wave * C::NB + jb) * 1024,
                         a_u8 < kleft ? b_off[jb] : G16_OOB, (uint32_t)kt * kstepB);
             } else {
-                g16_dma(rsB, smem + C::B_BASE + st * C::B_STAGE + (wave * 4 + jb) * 1024,
-                        bn_krow0 + 2 * jb < kleft ? b_off[jb] : G16_OOB, (uint32_t)kt * kstepB);
+                g16_dma(rsB, smem + C::B_BASE + st * C::B_STAGE + (wave * C::NB + jb) * 1024,
+                        bn_krow0 + (1024 / C::RB) * jb < kleft ? b_off[jb] : G16_OOB, (uint32_t)kt * kstepB);
             }
         };
         // LDS read r of the fragments of stage ST into F: 0 .. 2IM-1 A
         // [kk = r/IM][im = r%IM]; then B (q = r - 2IM): K-contiguous [kk][in]
-        // (q = kk*4 + in), N-contiguous [kk][in] half hr (q = kk*8 + in*2 + hr).
+        // (q = kk*IN + in), N-contiguous [kk][in] half hr (q = kk*2IN + in*2 + hr).
         auto lds_read = [&](G16Frags& F, auto stc, auto rc) {
             constexpr int ST = decltype(stc)::value, r = decltype(rc)::value;
             if constexpr (r < 2 * IM) {
                 constexpr int kk = r / IM, im = r % IM;
                 F.a[kk][im] = g16_read128<ST * C::A_STAGE + im * 2048>(a_fb[kk]);
             } else if constexpr (B_KCONTIG) {
-                if constexpr (r < 2 * IM + 8) {
-                    constexpr int kk = (r - 2 * IM) / 4, in = (r - 2 * IM) % 4;
+                if constexpr (r < 2 * IM + 2 * IN) {
+                    constexpr int kk = (r - 2 * IM) / IN, in = (r - 2 * IM) % IN;
                     F.b[kk][in] = g16_read128<ST * C::B_STAGE + in * 2048>(b_fb[kk]);
                 }
             } else {
-                constexpr int q = r - 2 * IM, kk = q / 8, in = (q % 8) / 2, hr = q % 2;
-                const v2i32_t h = g16_read_tr<ST * C::B_STAGE + kk * 8192 + hr * 2048>(b_fb[in]);
+                constexpr int q = r - 2 * IM, kk = q / (2 * IN), in = (q % (2 * IN)) / 2, hr = q % 2;
+                const v2i32_t h = g16_read_tr<ST * C::B_STAGE + kk * 16 * C::RB + hr * 4 * C::RB>(b_fb[in]);
                 F.b[kk][in][2 * hr] = (uint32_t)h[0];
                 F.b[kk][in][2 * hr + 1] = (uint32_t)h[1];
             }
@@ -315,8 +322,11 @@ gemm_bf16_persistent(GemmParams p) {
                                   "+v"(F.a[1][0]), "+v"(F.a[1][1]), "+v"(F.a[1][2]), "+v"(F.a[1][3]));
             else
                 asm volatile("" : "+v"(F.a[0][0]), "+v"(F.a[0][1]), "+v"(F.a[1][0]), "+v"(F.a[1][1]));
-            asm volatile("" : "+v"(F.b[0][0]), "+v"(F.b[0][1]), "+v"(F.b[0][2]), "+v"(F.b[0][3]),
-                              "+v"(F.b[1][0]), "+v"(F.b[1][1]), "+v"(F.b[1][2]), "+v"(F.b[1][3]));
+            if constexpr (IN == 4)
+                asm volatile("" : "+v"(F.b[0][0]), "+v"(F.b[0][1]), "+v"(F.b[0][2]), "+v"(F.b[0][3]),
+                                  "+v"(F.b[1][0]), "+v"(F.b[1][1]), "+v"(F.b[1][2]), "+v"(F.b[1][3]));
+            else
+                asm volatile("" : "+v"(F.b[0][0]), "+v"(F.b[0][1]), "+v"(F.b[1][0]), "+v"(F.b[1][1]));
         };
 
         // Bias of the tile, staged in LDS as binary32 after the prologue's wait
@@ -337,16 +347,16 @@ gemm_bf16_persistent(GemmParams p) {
             else             bcol_t = b;
         }
 
-        f32x16_t acc[IM][4];
+        f32x16_t acc[IM][IN];
 #pragma unroll
         for (int im = 0; im < IM; ++im)
 #pragma unroll
-            for (int in = 0; in < 4; ++in)
+            for (int in = 0; in < IN; ++in)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[im][in][r] = 0.0f;
 
         G16Frags F0, F1;
-        constexpr int NREAD = 2 * IM + (B_KCONTIG ? 8 : 16);
+        constexpr int NREAD = 2 * IM + (B_KCONTIG ? 2 : 4) * IN;
 
         // One K step kt (stage ST = kt % 4): wait for step kt+1's copy and for
         // the reads of step kt's fragments, barrier, then 32 MFMAs on
@@ -365,14 +375,14 @@ gemm_bf16_persistent(GemmParams p) {
             __builtin_amdgcn_sched_barrier(0);
             g16_static_for<0, C::NMF>([&](auto ic) {
                 constexpr int i = decltype(ic)::value;
-                constexpr int kk = i / (4 * IM), im = (i / 4) % IM, in = i % 4;
+                constexpr int kk = i / (IM * IN), im = (i / IN) % IM, in = i % IN;
                 if constexpr (F16)
                     acc[im][in] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
                         as_f16x8(cur.b[kk][in]), as_f16x8(cur.a[kk][im]), acc[im][in], 0, 0, 0);
                 else
                     acc[im][in] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         as_bf16x8(cur.b[kk][in]), as_bf16x8(cur.a[kk][im]), acc[im][in], 0, 0, 0);
-                if constexpr (BM == 256) {
+                if constexpr (BM == 256 && BN == 256) {
                     constexpr int slot = g16_slot<B_KCONTIG>(i);
                     if constexpr (slot >= 0 && slot < 32) {
                         lds_read(nxt, std::integral_constant<int, (ST + 1) % 4>{}, std::integral_constant<int, slot>{});
@@ -403,7 +413,7 @@ gemm_bf16_persistent(GemmParams p) {
         });
         g16_wait_vm_lgkm0<3 * C::NDMA>();
         if (tid < BM) bias_lds[tid] = brow_t;
-        bias_lds[BM + tid] = bcol_t;
+        if (tid < BN) bias_lds[BM + tid] = bcol_t;
         __builtin_amdgcn_s_barrier();
         g16_static_for<0, NREAD>([&](auto rc) { lds_read(F0, std::integral_constant<int, 0>{}, rc); });
 
@@ -439,11 +449,11 @@ gemm_bf16_persistent(GemmParams p) {
         {
             using OutT = typename std::conditional<OUT_BF16 != 0, uint16_t, float>::type;
             constexpr int ESZ = (int)sizeof(OutT);
-            const int64_t row_w = m0 + wm * C::WROWS, col_w = n0 + wn * 128;
+            const int64_t row_w = m0 + wm * C::WROWS, col_w = n0 + wn * C::WCOLS;
             OutT* Cw = (OutT*)p.C + s1 * p.sC1 + s2 * p.sC2 + row_w * p.sCm + col_w;
             const int sCm = (int)p.sCm;
             const int rows_valid = (int)min<int64_t>(p.M - row_w, C::WROWS);
-            const int cols_valid = (int)min<int64_t>(p.N - col_w, 128);
+            const int cols_valid = (int)min<int64_t>(p.N - col_w, C::WCOLS);
             if (rows_valid > 0 && cols_valid > 0) {
                 // An opaque copy of the lane id keeps every epilogue value below
                 // from being computed before the K loop (where it would stay live).
@@ -451,7 +461,7 @@ gemm_bf16_persistent(GemmParams p) {
                 asm volatile("" : "+v"(lane_e));
                 const int lrow = lane_e & 31, lh = lane_e >> 5, lcol = 4 * lh;
                 const float* brow_w = bias_lds + wm * C::WROWS;
-                const float* bcol_w = bias_lds + BM + wn * 128;
+                const float* bcol_w = bias_lds + BM + wn * C::WCOLS;
                 const uint64_t cv = (uint64_t)Cw;
                 const uint32_t clo = __builtin_amdgcn_readfirstlane((uint32_t)cv);
                 const uint32_t chi = __builtin_amdgcn_readfirstlane((uint32_t)(cv >> 32));
@@ -460,11 +470,11 @@ gemm_bf16_persistent(GemmParams p) {
                     (void*)(((uint64_t)chi << 32) | clo), (short)0, nrec, 0x00020000);
                 // The lane's bias values, read before any staging write.
                 float brv[IM];
-                f32x4_t bcv[16];
+                f32x4_t bcv[4 * IN];
 #pragma unroll
                 for (int im = 0; im < IM; ++im) brv[im] = brow_w[im * 32 + lrow];
 #pragma unroll
-                for (int q = 0; q < 16; ++q) bcv[q] = *(const f32x4_t*)(bcol_w + (q / 4) * 32 + 8 * (q % 4) + lcol);
+                for (int q = 0; q < 4 * IN; ++q) bcv[q] = *(const f32x4_t*)(bcol_w + (q / 4) * 32 + 8 * (q % 4) + lcol);
                 // Block (im, in), group g with bias added, in binary32.
                 auto value = [&](auto imc, auto qc) {
                     constexpr int im = decltype(imc)::value;
@@ -477,7 +487,7 @@ gemm_bf16_persistent(GemmParams p) {
                 };
                 if constexpr (CVEC) {
                     constexpr int PASSES = OUT_BF16 ? 1 : 2;
-                    constexpr int ROWB = 128 * ESZ;       // bytes of one staged row
+                    constexpr int ROWB = C::WCOLS * ESZ;  // bytes of one staged row
                     constexpr int NCH = ROWB / 16;        // 16-byte chunks per row
                     constexpr int RPP = C::WROWS / PASSES;  // rows per pass
                     constexpr int RPI = 64 / NCH;         // rows per read instruction
@@ -490,7 +500,7 @@ gemm_bf16_persistent(GemmParams p) {
                         g16_static_for<0, IM / PASSES>([&](auto ic) {
                             constexpr int im = ps * (IM / PASSES) + decltype(ic)::value;
                             const int r = (im % (IM / PASSES)) * 32 + lrow;
-                            g16_static_for<0, 16>([&](auto qc) {
+                            g16_static_for<0, 4 * IN>([&](auto qc) {
                                 constexpr int in = decltype(qc)::value / 4, g = decltype(qc)::value % 4;
                                 const f32x4_t v = value(std::integral_constant<int, im>{}, qc);
                                 if constexpr (OUT_BF16) {
@@ -515,7 +525,7 @@ gemm_bf16_persistent(GemmParams p) {
                     g16_static_for<0, IM>([&](auto imc) {
                         constexpr int im = decltype(imc)::value;
                         const int vrow = ((im * 32 + lrow) * sCm) * ESZ;
-                        g16_static_for<0, 16>([&](auto qc) {
+                        g16_static_for<0, 4 * IN>([&](auto qc) {
                             constexpr int in = decltype(qc)::value / 4, g = decltype(qc)::value % 4;
                             const f32x4_t v = value(imc, qc);
                             const int col = in * 32 + 8 * g + lcol;
@@ -538,5 +548,11 @@ gemm_bf16_persistent(GemmParams p) {
         if constexpr (CVEC) __builtin_amdgcn_s_barrier();
     }
 }
+
+// The kernel for a tile shape and layout (defined in gemm16_<BM>x<BN>.hip).
+typedef void (*Gemm16Kern)(GemmParams);
+Gemm16Kern gemm16_kernel_256x256(int f16, int kc, int out16, int cvec);
+Gemm16Kern gemm16_kernel_128x256(int f16, int kc, int out16, int cvec);
+Gemm16Kern gemm16_kernel_256x128(int f16, int kc, int out16, int cvec);
 
 }  // namespace bi

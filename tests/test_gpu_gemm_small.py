@@ -27,7 +27,7 @@ pytestmark = pytest.mark.gpu
 if torch.cuda.is_available():
     from invariant_persistent_bf16_amd import bi, bi_bench
 DEV = "cuda"
-TILES = (1, 32, 64, 128)   # 1: the persistent kernel with 128-row tiles
+TILES = (1, 2, 32, 64, 128)   # 1 / 2: the persistent kernel with 128x256 / 256x128 tiles
 
 
 def _operands(G, M, N, K, b_layout, dtype, seed):
@@ -106,7 +106,7 @@ def test_small_tiles_element_epilogue():
     for od, tdt in ((bi.BI_F32, torch.float32), (bi.BI_BF16, torch.bfloat16)):
         big = torch.full((M, N + 3), 7.0, dtype=tdt, device=DEV)
         ref = bi_bench.gemm_tile(A, B, 0, bias=bias, out_dtype=od)
-        for t in (1, 32):
+        for t in (1, 2, 32):
             big.fill_(7.0)
             out = bi_bench.gemm_tile(A, B, t, bias=bias, out_dtype=od, out=big[:, :N])
             torch.cuda.synchronize()
