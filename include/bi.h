@@ -8,8 +8,11 @@
  * whether it is computed alone or inside any batch.  The method follows the
  * persistent matmul of "Unmasking the True Culprit: Why Temperature=0 Doesn't
  * Mean Deterministic LLM Inference" (section "Technical Deep Dive: Batch
- * Invariant Kernels": fixed tile configuration per dtype, float32 tile
- * accumulation, ascending K loop, no split-K), the per-sample Conv2d and
+ * Invariant Kernels": a reduction order fixed per dtype, float32 tile
+ * accumulation, ascending K loop, no split-K; here the order is fixed by the
+ * matrix instruction and the K step, while the output tile may be chosen
+ * from the shape since it never changes an element's order), the per-sample
+ * Conv2d and
  * batched matmul of "Batch-Invariant Kernel Design: Conv2d and Attention BMM"
  * (sections "Kernel 1: Conv2d" and "Kernel 2: Attention BMM"), and the
  * fixed-length split-KV decoding of the deterministic-inference handbook

@@ -5,7 +5,9 @@
 // True Culprit ...", section "Why This Achieves Batch Invariance": fixed block
 // sizes, each output tile reduced inside one core, the same K order, no
 // split-K) holds here by construction:
-//   * one tile shape and one K step for every call (constants below);
+//   * one K step (32) and one MFMA instruction per dtype for every call; the
+//     tile shape (chosen by the host from the shape of the product) only
+//     decides which wave computes which elements;
 //   * output element (i, j) is accumulated by a single chain of
 //     v_mfma_f32_32x32x16_bf16 instructions, one per 16-wide K slice, K
 //     ascending, starting from zero; its operands are row i of A and column j
