@@ -267,11 +267,45 @@ def _graph_us(fn, n=20):
     return best
 
 
+def _graph_us_seq(fns, reps=4):
+    """GPU time per call of the calls fns[0], fns[1], ... captured in order
+    (reps times over) in one graph and replayed: rotating operand copies gives
+    the cold-cache rate of a working set larger than the 256 MB cache."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for f in fns:
+            f()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            for f in fns:
+                f()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = float("inf")
+    for _ in range(3):
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) * 1e3 / (reps * len(fns)))
+    del g
+    return best
+
+
 def small_batch(Wd, bd, x0, cwd, cbd, cx0):
-    """Untimed extra: batch 1 of the addmm and conv workloads, where 256x256
-    tiles leave most compute units idle.  The library then picks the small-tile
-    kernel (same bits); forced persistent-kernel times beside it (GPU time from
-    graph replay)."""
+    """Untimed extra: small batches of the addmm, conv and decode workloads,
+    where 256x256 tiles (or one request's chunks) leave most compute units
+    idle.  The library then picks the small-tile or 128-row kernels (same
+    bits); forced 256x256 persistent-kernel times beside them.  GPU time from
+    graph replay: warm (the same operands every call; a 117 MB W or a 64 MiB
+    request stays in the 256 MB cache) and cold (3 W copies, 5 KV copies
+    rotating)."""
     import torch
 
     import synth
@@ -280,14 +314,20 @@ def small_batch(Wd, bd, x0, cwd, cbd, cx0):
     dev = Wd.device
     K, N = ADDMM["K"], ADDMM["N"]
     res = {}
-    for M in (1, 64):
+    # Three copies of W (352 MB) rotate for the cold rate: one W fits the cache.
+    Wcopies = [Wd] + [Wd.clone() for _ in range(2)]
+    for M in (1, 64, 200):
         X = synth.addmm_batch(x0, M, device=dev)
         y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
         ta = _graph_us(lambda: bi.bi_addmm(bd, X, Wd, out=y))
+        tc = _graph_us_seq([lambda W=W: bi.bi_addmm(bd, X, W, out=y) for W in Wcopies])
         tp = _graph_us(lambda: bi_bench.gemm_tile(X, Wd, 0, bias=bd, out=y))
-        res[f"addmm_M{M}"] = {"us": round(ta, 2), "tile_rows": bi_bench.gemm_tile_rows(1, M, N, K),
+        res[f"addmm_M{M}"] = {"us": round(ta, 2), "cold_us": round(tc, 2),
+                              "tile_rows": bi_bench.gemm_tile_rows(1, M, N, K),
                               "persistent_us": round(tp, 2),
-                              "W_GBps": round(K * N * 2 / (ta * 1e-6) / 1e9, 1)}
+                              "W_GBps": round(K * N * 2 / (ta * 1e-6) / 1e9, 1),
+                              "W_GBps_cold": round(K * N * 2 / (tc * 1e-6) / 1e9, 1)}
+    del Wcopies
     cx = synth.conv_batch(cx0, 1, device=dev)
     cy = torch.empty(1, 1152, 16, 16, dtype=torch.bfloat16, device=dev)
     ws = torch.empty(bi.bi_conv2d_workspace_bytes(cx.shape, cwd.shape, (14, 14)), dtype=torch.uint8, device=dev)
@@ -303,6 +343,18 @@ def small_batch(Wd, bd, x0, cwd, cbd, cx0):
     res["conv2d_B1"] = {"us": round(tc, 2), "gemm_tile_rows": bi_bench.gemm_tile_rows(1, 1152, 256, 592),
                         "gemm_us": round(min(v for r, v in tg.items() if r != 0), 2),
                         "gemm_persistent_us": round(tg[0], 2)}
+    H, S, D = DEC["H"], DEC["S"], DEC["D"]
+    q1 = torch.randn(1, H, D, device=dev).to(torch.bfloat16)
+    kv = [(torch.randn(1, H, S, D, device=dev).to(torch.bfloat16), torch.randn(1, H, S, D, device=dev).to(torch.bfloat16))
+          for _ in range(5)]
+    o1 = torch.empty(1, H, D, dtype=torch.float32, device=dev)
+    ws1 = torch.empty(bi.bi_decode_attn_workspace_bytes(1, H, S, D) // 4 + 1, dtype=torch.float32, device=dev)
+    tw = _graph_us(lambda: bi.bi_decode_attn(q1, kv[0][0], kv[0][1], 0.125, out=o1, workspace=ws1))
+    tcd = _graph_us_seq([lambda k=k, v=v: bi.bi_decode_attn(q1, k, v, 0.125, out=o1, workspace=ws1) for k, v in kv])
+    nb = 2 * H * S * D * 2
+    res["decode_B1"] = {"us": round(tw, 2), "cold_us": round(tcd, 2), "GBps": round(nb / (tw * 1e-6) / 1e9, 1),
+                        "GBps_cold": round(nb / (tcd * 1e-6) / 1e9, 1)}
+    del kv
     return res
 
 

@@ -133,11 +133,12 @@ int gemm_tile_rows(const GemmDesc& d, int cus) {
     const double t_p128 = 6.0 + 0.30 * (double)nk * (double)cdiv(tiles128, cus);
     if (t_p128 < best) { best = t_p128; best_rows = 1; }
     if (tiles >= cus) return best_rows;
-    const int64_t nblk = cdiv(d.N, 32);
+    // Small tiles: A is read once per GS_COLS columns, B once per row block.
+    const int64_t nblk = cdiv(d.N, GS_COLS);
     for (int rows : {32, 64, 128}) {
         if (rows > 32 && d.M <= rows / 2) break;   // a taller block only adds empty rows
         const int64_t blocks = slices * cdiv(d.M, rows) * nblk;
-        const double bytes = (double)(slices * d.M * nblk + blocks * 32) * (double)(nk * G16_BK) * 2.0;
+        const double bytes = (double)(slices * d.M * nblk + blocks * GS_COLS) * (double)(nk * G16_BK) * 2.0;
         const double t = std::max(bytes / 8.0e6, 2.0 + 0.15 * (double)nk);
         if (t < best) { best = t; best_rows = rows; }
     }
@@ -179,7 +180,7 @@ int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override, int tile_r
             p.sA1 = d.sA1; p.sA2 = d.sA2; p.sB1 = d.sB1; p.sB2 = d.sB2;
             p.sC1 = d.sC1; p.sC2 = d.sC2; p.sBias2 = d.sBias2; p.bias_rows = d.bias_rows;
             p.tiles_m = (int)cdiv(d.M, rows);
-            p.tiles_n = (int)cdiv(d.N, 32);
+            p.tiles_n = (int)cdiv(d.N, GS_COLS);
             p.tiles_per_slice = p.tiles_m * p.tiles_n;
             const int64_t total = (int64_t)p.tiles_per_slice * d.G1 * d.G2;
             if (total > (1ll << 30)) return BI_ERR_UNSUPPORTED;

@@ -2,7 +2,7 @@
 
 The library computes a 16-bit product either with the persistent 256x256
 kernel or, where those tiles would leave most compute units idle, with
-one-wave (32, 64 or 128) x 32 blocks, or with 128x256 persistent tiles; the
+one-wave (32, 64 or 128) x 64 blocks, or with 128x256 persistent tiles; the
 choice is a function of the shape.
 Both must give the same bits for every element.  Here each forced tile size is
 compared bit for bit with the persistent kernel on ragged shapes (M, N, K
