@@ -107,15 +107,18 @@ int gemm_check(const GemmDesc& d) {
 
 // The kernel for a 16-bit product, a function of the shape alone (every
 // choice gives the same bits): 0 = the persistent kernel with 256x256 tiles,
-// 1 = with 128x256 tiles, 2 = with 256x128 tiles (N <= 128), 32 / 64 / 128 =
-// the small-tile kernel with blocks of that many rows.  Estimated times fitted to measurements on MI355X: a
-// persistent tile costs about 0.52 us (256x256) or 0.30 us (128 rows or columns) per
-// 32-wide K step, in rounds of one tile per compute unit, plus about 6 us of
+// 1 = with 128x256 tiles, 2 = with 256x128 tiles (N <= 128), 3 = with 128x128
+// tiles, 32 / 64 / 128 = the small-tile kernel with blocks of that many rows.
+// Estimated times fitted to measurements on MI355X: a persistent tile costs
+// about 0.52 us (256x256), 0.30 us (128 rows or columns) or 0.24 us (128x128)
+// per 32-wide K step, in rounds of one tile per compute unit, plus about 6 us
+// (3 us for 128x128, considered only while its tiles fit in one round) of
 // launch, prologue and epilogue; the small-tile waves sustain about 8 TB/s of
-// operand reads from L2 (each block reads its rows of A and its 32 columns of
-// B over the whole of K) and need about 0.15 us per K step plus 2 us when
-// latency bound.  Only products with at most two rounds of 256x256 tiles are
-// considered for the others (larger ones keep the 256x256 tile).
+// operand reads from L2 (each block reads its rows of A and its 64 columns of
+// B over the whole of K) and need 0.16 / 0.20 / 0.38 us per K step (32, 64,
+// 128 rows) for each block per compute unit, plus 2 us, when latency bound.
+// Only products with at most two rounds of 256x256 tiles are considered for
+// the others (larger ones keep the 256x256 tile).
 int gemm_tile_rows(const GemmDesc& d, int cus) {
     const int64_t slices = d.G1 * d.G2;
     // Binary32: 32x32 tiles (one 16x16 MFMA chain per wave) where the 64x64
@@ -132,14 +135,22 @@ int gemm_tile_rows(const GemmDesc& d, int cus) {
     int best_rows = narrow ? 2 : 0;
     const double t_p128 = 6.0 + 0.30 * (double)nk * (double)cdiv(tiles128, cus);
     if (t_p128 < best) { best = t_p128; best_rows = 1; }
+    // 128x128 tiles (returned as 3), only while they fit in one round.
+    const int64_t tiles3 = slices * cdiv(d.M, 128) * cdiv(d.N, 128);
+    if (tiles3 <= cus) {
+        const double t3 = 3.0 + 0.24 * (double)nk;
+        if (t3 < best) { best = t3; best_rows = 3; }
+    }
     if (tiles >= cus) return best_rows;
-    // Small tiles: A is read once per GS_COLS columns, B once per row block.
+    // Small tiles: A is read once per GS_COLS columns, B once per row block;
+    // a K step costs more for taller blocks and when blocks outnumber the CUs.
     const int64_t nblk = cdiv(d.N, GS_COLS);
     for (int rows : {32, 64, 128}) {
         if (rows > 32 && d.M <= rows / 2) break;   // a taller block only adds empty rows
         const int64_t blocks = slices * cdiv(d.M, rows) * nblk;
         const double bytes = (double)(slices * d.M * nblk + blocks * GS_COLS) * (double)(nk * G16_BK) * 2.0;
-        const double t = std::max(bytes / 8.0e6, 2.0 + 0.15 * (double)nk);
+        const double per_step = rows == 32 ? 0.16 : rows == 64 ? 0.20 : 0.38;
+        const double t = std::max(bytes / 8.0e6, 2.0 + per_step * (double)nk * (double)cdiv(blocks, cus));
         if (t < best) { best = t; best_rows = rows; }
     }
     return best_rows;
@@ -168,9 +179,9 @@ int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override, int tile_r
         const bool out16 = d.out_dtype != BI_F32;
         const bool kc = d.K == 0 || (d.sBk == 1 && (d.N == 1 || d.sBn % 8 == 0));
         const int rows = tile_rows >= 0 ? tile_rows : grid_override > 0 ? 0 : gemm_tile_rows(d, cus);
-        if (rows != 0 && rows != 1 && rows != 2 && rows != 32 && rows != 64 && rows != 128)
+        if (rows != 0 && rows != 1 && rows != 2 && rows != 3 && rows != 32 && rows != 64 && rows != 128)
             return BI_ERR_UNSUPPORTED;
-        if (rows > 2) {
+        if (rows > 3) {
             GemmParams p;
             p.A = (const uint16_t*)d.A; p.B = (const uint16_t*)d.B;
             p.bias = (const uint16_t*)d.bias; p.C = d.C;
@@ -210,7 +221,7 @@ int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override, int tile_r
         p.G2 = d.G2;
         p.sA1 = d.sA1; p.sA2 = d.sA2; p.sB1 = d.sB1; p.sB2 = d.sB2;
         p.sC1 = d.sC1; p.sC2 = d.sC2; p.sBias2 = d.sBias2; p.bias_rows = d.bias_rows;
-        const int bm = rows == 1 ? 128 : G16_BM, bn = rows == 2 ? 128 : G16_BN;
+        const int bm = rows == 1 || rows == 3 ? 128 : G16_BM, bn = rows == 2 || rows == 3 ? 128 : G16_BN;
         p.tiles_m = (int)cdiv(d.M, bm);
         p.tiles_n = (int)cdiv(d.N, bn);
         p.tiles_per_slice = p.tiles_m * p.tiles_n;
@@ -225,6 +236,7 @@ int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override, int tile_r
         const int f16 = d.in_dtype == BI_F16;
         const Gemm16Kern kern = rows == 1 ? gemm16_kernel_128x256(f16, kc, out16, cvec)
                               : rows == 2 ? gemm16_kernel_256x128(f16, kc, out16, cvec)
+                              : rows == 3 ? gemm16_kernel_128x128(f16, kc, out16, cvec)
                                           : gemm16_kernel_256x256(f16, kc, out16, cvec);
         hipLaunchKernelGGL(kern, dim3(grid), dim3(G16_THREADS), 0, st, p);
     } else {

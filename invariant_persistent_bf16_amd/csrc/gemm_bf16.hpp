@@ -67,9 +67,9 @@ constexpr int G16_GROUP_M = 8;
 constexpr int G16_NSTAGE = 4;
 constexpr uint32_t G16_OOB = 0x80000000u;                         // buffer offset that reads as zero
 // Layout per tile shape: BM x BN = 256 x 256 (the tile above), 128 x 256
-// (each wave 64x128, for products whose 256x256 tiles leave compute units
-// idle) or 256 x 128 (each wave 128x64, for N <= 128, which would fill half
-// of a 256-wide tile).
+// (each wave 64x128) and 128 x 128 (each wave 64x64), for products whose
+// 256x256 tiles leave compute units idle, or 256 x 128 (each wave 128x64,
+// for N <= 128, which would fill half of a 256-wide tile).
 template <int BM, int BN>
 struct G16Cfg {
     static constexpr int WROWS = BM / 2;                        // rows of a wave's block
@@ -181,7 +181,7 @@ struct G16Frags {
 // output) instead of bfloat16; the same tile, K order and schedule, the
 // pages' fixed configuration per dtype.  OUT_BF16: 16-bit output in the
 // operands' type (else binary32).
-// BM x BN: tile shape, 256 x 256, 128 x 256 or 256 x 128 (G16Cfg); the
+// BM x BN: tile shape, 256 x 256, 128 x 256, 256 x 128 or 128 x 128 (G16Cfg); the
 // per-element arithmetic is the same for all.
 template <bool B_KCONTIG, int OUT_BF16, bool CVEC, bool F16 = false, int BM = 256, int BN = 256>
 __global__ void __launch_bounds__(G16_THREADS, 1)
@@ -561,5 +561,6 @@ typedef void (*Gemm16Kern)(GemmParams);
 Gemm16Kern gemm16_kernel_256x256(int f16, int kc, int out16, int cvec);
 Gemm16Kern gemm16_kernel_128x256(int f16, int kc, int out16, int cvec);
 Gemm16Kern gemm16_kernel_256x128(int f16, int kc, int out16, int cvec);
+Gemm16Kern gemm16_kernel_128x128(int f16, int kc, int out16, int cvec);
 
 }  // namespace bi

@@ -2,8 +2,8 @@
 
 The library computes a 16-bit product either with the persistent 256x256
 kernel or, where those tiles would leave most compute units idle, with
-one-wave (32, 64 or 128) x 64 blocks, or with 128x256 persistent tiles; the
-choice is a function of the shape.
+one-wave (32, 64 or 128) x 64 blocks, or with 128x256 or 128x128 persistent
+tiles; the choice is a function of the shape.
 Both must give the same bits for every element.  Here each forced tile size is
 compared bit for bit with the persistent kernel on ragged shapes (M, N, K
 tails, one row, K = 8), both B layouts, column bias (addmm) and row bias (the
@@ -27,7 +27,7 @@ pytestmark = pytest.mark.gpu
 if torch.cuda.is_available():
     from invariant_persistent_bf16_amd import bi, bi_bench
 DEV = "cuda"
-TILES = (1, 2, 32, 64, 128)   # 1 / 2: the persistent kernel with 128x256 / 256x128 tiles
+TILES = (1, 2, 3, 32, 64, 128)   # 1 / 2 / 3: the persistent kernel with 128x256 / 256x128 / 128x128 tiles
 
 
 def _operands(G, M, N, K, b_layout, dtype, seed):
@@ -128,10 +128,11 @@ def test_auto_choice_on_batch1_linear_and_conv():
     # every choice gives row 0 (sample 0) the same bits.
     assert bi_bench.gemm_tile_rows(1, 1, 14336, 4096) == 32
     assert bi_bench.gemm_tile_rows(1, 64, 14336, 4096) == 64
-    assert bi_bench.gemm_tile_rows(1, 200, 14336, 4096) == 1      # 128-row persistent tiles
-    assert bi_bench.gemm_tile_rows(1, 512, 14336, 4096) == 1
+    assert bi_bench.gemm_tile_rows(1, 200, 14336, 4096) == 3      # 128x128 persistent tiles
+    assert bi_bench.gemm_tile_rows(1, 512, 14336, 4096) == 1      # 128x256
     assert bi_bench.gemm_tile_rows(1, 8192, 14336, 4096) == 0
     assert bi_bench.gemm_tile_rows(1, 1152, 256, 592) == 32      # conv, one image
+    assert bi_bench.gemm_tile_rows(4, 1152, 256, 592) == 3       # conv, 4 images
     assert bi_bench.gemm_tile_rows(32, 1152, 256, 592) == 0      # conv, 32 images
     W, bias, x0 = synth.addmm_shared()
     Wd, bd = W.to(DEV), bias.to(DEV)
