@@ -74,6 +74,10 @@ CASES = [
     (2, 6, 24, 24, 12, 3, 3, (1, 2), (2, 1), (2, 2), 3),
     (1, 8, 9, 33, 300, 5, 1, (3, 1), (2, 0), (1, 3), 1),
     (2, 16, 12, 12, 16, 3, 3, (1, 1), (1, 1), (1, 1), 16),
+    # Non-overlapping patches (stride = kernel, no padding), with groups and
+    # an input height that leaves rows unused; then rows of 20 elements.
+    (2, 4, 35, 48, 20, 4, 8, (4, 8), (0, 0), (1, 1), 2),
+    (1, 3, 20, 20, 8, 5, 5, (5, 5), (0, 0), (1, 1), 1),
 ]
 
 
