@@ -81,7 +81,12 @@ struct G16Cfg {
     static constexpr int B_BASE = G16_NSTAGE * A_STAGE;         // B stages after the A stages
     static constexpr int RING = G16_NSTAGE * (A_STAGE + B_STAGE);
     static constexpr int BIAS = (BM + BN) * 4;                  // row and column bias, binary32
-    static constexpr int LDS = RING + 2 * BIAS;                 // bias double buffered
+    // Bias double buffered after the ring.  At least 81 KiB in all, so that
+    // two workgroups never share a compute unit: every shape then runs one
+    // workgroup (one wave per SIMD) per compute unit, the regime the kernel
+    // is verified in.  With two 128x128 workgroups per unit (66 KiB each)
+    // some accumulator values reached the output corrupted.
+    static constexpr int LDS = RING + 2 * BIAS > 81 * 1024 ? RING + 2 * BIAS : 81 * 1024;
     static constexpr int NA = BM / 64;                          // A copies per wave and step
     static constexpr int NB = BN / 64;                          // B copies per wave and step
     static constexpr int NDMA = NA + NB;
