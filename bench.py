@@ -517,16 +517,27 @@ def prefill():
 def gemm_traffic(path):
     """Counter-measured bytes per GEMM launch, or None if the kernel source
     changed since the counters were taken (or no record exists)."""
-    import hashlib
     try:
         rec = dict(line.split(":", 1) for line in open(path) if ":" in line and not line.startswith("#"))
-        src = b"".join(open(os.path.join(ROOT, "invariant_persistent_bf16_amd", "csrc", f), "rb").read()
-                       for f in ("gemm_bf16.hpp", "common.hpp"))
-        if hashlib.sha256(src).hexdigest() != rec["source_sha256"].strip():
+        if gemm_code_hash() != rec["source_sha256"].strip():
             return None
         return int(rec["bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
+
+
+def gemm_code_hash():
+    """sha256 of the GEMM kernel's code lines (gemm_bf16.hpp + common.hpp,
+    // comments and blank lines dropped), so that only a code change voids a
+    stored counter record."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemm_bf16.hpp", "common.hpp"):
+        for line in open(os.path.join(ROOT, "invariant_persistent_bf16_amd", "csrc", f), encoding="utf-8"):
+            code = line.split("//", 1)[0].strip()
+            if code:
+                h.update(code.encode() + b"\n")
+    return h.hexdigest()
 
 
 def cpu_baseline(W, bias, x0, target_s):

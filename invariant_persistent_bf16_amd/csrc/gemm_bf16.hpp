@@ -21,12 +21,13 @@
 //
 // Hardware mapping.  A 256x256 output tile per workgroup of 4 waves (2x2),
 // each wave owning 128x128 = 4x4 MFMA blocks of 32x32 (256 binary32
-// accumulators per lane, held in AGPRs).  Two other tile shapes run the same
-// per-element chain (G16Cfg): 128x256 (each wave 64x128) for products whose
-// 256x256 tiles would leave compute units idle, and 256x128 (each wave
-// 128x64) for N <= 128; the description below is of the 256x256 tile, the
-// others scale the copy counts, LDS rows and fragment counts with the shape
-// and spread their reads and copies evenly over the step's MFMAs.  K advances in steps of 32 through a
+// accumulators per lane, held in AGPRs).  Three other tile shapes run the
+// same per-element chain (G16Cfg): 128x256 (each wave 64x128) and 128x128
+// (each wave 64x64) for products whose 256x256 tiles would leave compute
+// units idle, and 256x128 (each wave 128x64) for N <= 128; the description
+// below is of the 256x256 tile, the others scale the copy counts, LDS rows
+// and fragment counts with the shape and spread their reads and copies evenly
+// over the step's MFMAs.  K advances in steps of 32 through a
 // 4-stage LDS ring (4 x (16 + 16) KiB): operand tiles are copied HBM -> LDS by
 // buffer_load_dwordx4 ... lds (no staging registers; a lane whose 16 bytes
 // fall outside the operand gets an out-of-range offset and the hardware
