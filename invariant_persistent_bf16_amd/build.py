@@ -23,7 +23,7 @@ CFLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
 LDFLAGS = [f"--offload-arch={ARCH}", "-fPIC", "-shared"]
 
 GEMM16 = ["csrc/gemm16_256x256.hip", "csrc/gemm16_128x256.hip", "csrc/gemm16_256x128.hip",
-          "csrc/gemm16_128x128.hip"]
+          "csrc/gemm16_128x128.hip", "csrc/gemm16_192x256.hip"]
 LIBS = {
     "libbi.so": ["csrc/api.hip"] + GEMM16,
     "libbi_bench.so": ["csrc/api.hip", "csrc/bench_api.hip"] + GEMM16,

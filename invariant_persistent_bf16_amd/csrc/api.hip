@@ -108,17 +108,21 @@ int gemm_check(const GemmDesc& d) {
 // The kernel for a 16-bit product, a function of the shape alone (every
 // choice gives the same bits): 0 = the persistent kernel with 256x256 tiles,
 // 1 = with 128x256 tiles, 2 = with 256x128 tiles (N <= 128), 3 = with 128x128
-// tiles, 32 / 64 / 128 = the small-tile kernel with blocks of that many rows.
-// Estimated times fitted to measurements on MI355X: a persistent tile costs
-// about 0.52 us (256x256), 0.30 us (128 rows or columns) or 0.24 us (128x128)
-// per 32-wide K step, in rounds of one tile per compute unit, plus about 6 us
-// (3 us for 128x128, considered only while its tiles fit in one round) of
-// launch, prologue and epilogue; the small-tile waves sustain about 8 TB/s of
-// operand reads from L2 (each block reads its rows of A and its 64 columns of
-// B over the whole of K) and need 0.16 / 0.20 / 0.38 us per K step (32, 64,
-// 128 rows) for each block per compute unit, plus 2 us, when latency bound.
-// Only products with at most two rounds of 256x256 tiles are considered for
-// the others (larger ones keep the 256x256 tile).
+// tiles, 4 = with 192x256 tiles, 32 / 64 / 128 = the small-tile kernel with
+// blocks of that many rows.  Estimated times fitted to measurements on MI355X
+// (GPU time of the addmm with K = 4096, N = 14336 and of the patch
+// convolution's GEMM, K = 592): a persistent tile costs, per round of one
+// tile per compute unit, a fixed part (launch, prologue and epilogue, growing
+// with the tile's area) plus a part per 32-wide K step: 13.1 + 0.464 nk us
+// (256x256), 10.3 + 0.456 nk (192x256), 8.2 + 0.296 nk (128x256), 4.7 +
+// 0.225 nk (128x128); the 192x256 and 128x128 tiles are considered only while
+// their tiles fit in one round; N <= 128 compares 256x128 and 128x256 tiles
+// at 6 + 0.30 nk per round.  The small-tile waves sustain about 8 TB/s of
+// operand reads from L2 (each block reads its rows of A and its 64 columns
+// of B over the whole of K) and need 0.16 / 0.20 / 0.38 us per K step (32,
+// 64, 128 rows) for each block per compute unit, plus 2 us, when latency
+// bound.  Only products with at most two rounds of 256x256 tiles are
+// considered for the others (larger ones keep the 256x256 tile).
 int gemm_tile_rows(const GemmDesc& d, int cus) {
     const int64_t slices = d.G1 * d.G2;
     // Binary32: 32x32 tiles (one 16x16 MFMA chain per wave) where the 64x64
@@ -129,16 +133,27 @@ int gemm_tile_rows(const GemmDesc& d, int cus) {
     // does the same rows with half the MFMA work and B traffic.
     const bool narrow = d.N <= 128;
     if (tiles >= 2 * (int64_t)cus) return narrow ? 2 : 0;
-    const int64_t nk = cdiv(d.K, G16_BK);
+    const double nk = (double)cdiv(d.K, G16_BK);
     const int64_t tiles128 = slices * cdiv(d.M, 128) * cdiv(d.N, G16_BN);
-    double best = 6.0 + (narrow ? 0.30 : 0.52) * (double)nk * (double)cdiv(tiles, cus);
-    int best_rows = narrow ? 2 : 0;
-    const double t_p128 = 6.0 + 0.30 * (double)nk * (double)cdiv(tiles128, cus);
-    if (t_p128 < best) { best = t_p128; best_rows = 1; }
-    // 128x128 tiles (returned as 3), only while they fit in one round.
-    const int64_t tiles3 = slices * cdiv(d.M, 128) * cdiv(d.N, 128);
-    if (tiles3 <= cus) {
-        const double t3 = 3.0 + 0.24 * (double)nk;
+    double best;
+    int best_rows;
+    if (narrow) {
+        best = 6.0 + 0.30 * nk * (double)cdiv(tiles, cus);
+        best_rows = 2;
+        const double t1 = 6.0 + 0.30 * nk * (double)cdiv(tiles128, cus);
+        if (t1 < best) { best = t1; best_rows = 1; }
+    } else {
+        best = (double)cdiv(tiles, cus) * (13.1 + 0.464 * nk);
+        best_rows = 0;
+        const double t1 = (double)cdiv(tiles128, cus) * (8.2 + 0.296 * nk);
+        if (t1 < best) { best = t1; best_rows = 1; }
+        if (slices * cdiv(d.M, 192) * cdiv(d.N, G16_BN) <= cus) {
+            const double t4 = 10.3 + 0.456 * nk;
+            if (t4 < best) { best = t4; best_rows = 4; }
+        }
+    }
+    if (slices * cdiv(d.M, 128) * cdiv(d.N, 128) <= cus) {
+        const double t3 = 4.7 + 0.225 * nk;
         if (t3 < best) { best = t3; best_rows = 3; }
     }
     if (tiles >= cus) return best_rows;
@@ -179,9 +194,10 @@ int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override, int tile_r
         const bool out16 = d.out_dtype != BI_F32;
         const bool kc = d.K == 0 || (d.sBk == 1 && (d.N == 1 || d.sBn % 8 == 0));
         const int rows = tile_rows >= 0 ? tile_rows : grid_override > 0 ? 0 : gemm_tile_rows(d, cus);
-        if (rows != 0 && rows != 1 && rows != 2 && rows != 3 && rows != 32 && rows != 64 && rows != 128)
+        if (rows != 0 && rows != 1 && rows != 2 && rows != 3 && rows != 4 && rows != 32 && rows != 64 &&
+            rows != 128)
             return BI_ERR_UNSUPPORTED;
-        if (rows > 3) {
+        if (rows > 4) {
             GemmParams p;
             p.A = (const uint16_t*)d.A; p.B = (const uint16_t*)d.B;
             p.bias = (const uint16_t*)d.bias; p.C = d.C;
@@ -221,7 +237,8 @@ int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override, int tile_r
         p.G2 = d.G2;
         p.sA1 = d.sA1; p.sA2 = d.sA2; p.sB1 = d.sB1; p.sB2 = d.sB2;
         p.sC1 = d.sC1; p.sC2 = d.sC2; p.sBias2 = d.sBias2; p.bias_rows = d.bias_rows;
-        const int bm = rows == 1 || rows == 3 ? 128 : G16_BM, bn = rows == 2 || rows == 3 ? 128 : G16_BN;
+        const int bm = rows == 1 || rows == 3 ? 128 : rows == 4 ? 192 : G16_BM;
+        const int bn = rows == 2 || rows == 3 ? 128 : G16_BN;
         p.tiles_m = (int)cdiv(d.M, bm);
         p.tiles_n = (int)cdiv(d.N, bn);
         p.tiles_per_slice = p.tiles_m * p.tiles_n;
@@ -237,6 +254,7 @@ int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override, int tile_r
         const Gemm16Kern kern = rows == 1 ? gemm16_kernel_128x256(f16, kc, out16, cvec)
                               : rows == 2 ? gemm16_kernel_256x128(f16, kc, out16, cvec)
                               : rows == 3 ? gemm16_kernel_128x128(f16, kc, out16, cvec)
+                              : rows == 4 ? gemm16_kernel_192x256(f16, kc, out16, cvec)
                                           : gemm16_kernel_256x256(f16, kc, out16, cvec);
         hipLaunchKernelGGL(kern, dim3(grid), dim3(G16_THREADS), 0, st, p);
     } else {

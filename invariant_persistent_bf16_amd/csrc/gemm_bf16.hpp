@@ -21,10 +21,11 @@
 //
 // Hardware mapping.  A 256x256 output tile per workgroup of 4 waves (2x2),
 // each wave owning 128x128 = 4x4 MFMA blocks of 32x32 (256 binary32
-// accumulators per lane, held in AGPRs).  Three other tile shapes run the
-// same per-element chain (G16Cfg): 128x256 (each wave 64x128) and 128x128
-// (each wave 64x64) for products whose 256x256 tiles would leave compute
-// units idle, and 256x128 (each wave 128x64) for N <= 128; the description
+// accumulators per lane, held in AGPRs).  Four other tile shapes run the
+// same per-element chain (G16Cfg): 128x256 (each wave 64x128), 128x128
+// (each wave 64x64) and 192x256 (each wave 96x128) for products whose
+// 256x256 tiles would leave compute units idle, and 256x128 (each wave
+// 128x64) for N <= 128; the description
 // below is of the 256x256 tile, the others scale the copy counts, LDS rows
 // and fragment counts with the shape and spread their reads and copies evenly
 // over the step's MFMAs.  K advances in steps of 32 through a
@@ -69,8 +70,10 @@ constexpr int G16_NSTAGE = 4;
 constexpr uint32_t G16_OOB = 0x80000000u;                         // buffer offset that reads as zero
 // Layout per tile shape: BM x BN = 256 x 256 (the tile above), 128 x 256
 // (each wave 64x128) and 128 x 128 (each wave 64x64), for products whose
-// 256x256 tiles leave compute units idle, or 256 x 128 (each wave 128x64,
-// for N <= 128, which would fill half of a 256-wide tile).
+// 256x256 tiles leave compute units idle, 192 x 256 (each wave 96x128, for
+// M a multiple of 192, such as the 1152 output channels of the patch
+// convolution), or 256 x 128 (each wave 128x64, for N <= 128, which would
+// fill half of a 256-wide tile).
 template <int BM, int BN>
 struct G16Cfg {
     static constexpr int WROWS = BM / 2;                        // rows of a wave's block
@@ -187,7 +190,7 @@ struct G16Frags {
 // output) instead of bfloat16; the same tile, K order and schedule, the
 // pages' fixed configuration per dtype.  OUT_BF16: 16-bit output in the
 // operands' type (else binary32).
-// BM x BN: tile shape, 256 x 256, 128 x 256, 256 x 128 or 128 x 128 (G16Cfg); the
+// BM x BN: tile shape, 256 x 256, 128 x 256, 256 x 128, 128 x 128 or 192 x 256 (G16Cfg); the
 // per-element arithmetic is the same for all.
 template <bool B_KCONTIG, int OUT_BF16, bool CVEC, bool F16 = false, int BM = 256, int BN = 256>
 __global__ void __launch_bounds__(G16_THREADS, 1)
@@ -333,6 +336,9 @@ gemm_bf16_persistent(GemmParams p) {
             if constexpr (IM == 4)
                 asm volatile("" : "+v"(F.a[0][0]), "+v"(F.a[0][1]), "+v"(F.a[0][2]), "+v"(F.a[0][3]),
                                   "+v"(F.a[1][0]), "+v"(F.a[1][1]), "+v"(F.a[1][2]), "+v"(F.a[1][3]));
+            else if constexpr (IM == 3)
+                asm volatile("" : "+v"(F.a[0][0]), "+v"(F.a[0][1]), "+v"(F.a[0][2]),
+                                  "+v"(F.a[1][0]), "+v"(F.a[1][1]), "+v"(F.a[1][2]));
             else
                 asm volatile("" : "+v"(F.a[0][0]), "+v"(F.a[0][1]), "+v"(F.a[1][0]), "+v"(F.a[1][1]));
             if constexpr (IN == 4)
@@ -499,7 +505,9 @@ gemm_bf16_persistent(GemmParams p) {
                     return v;
                 };
                 if constexpr (CVEC) {
-                    constexpr int PASSES = OUT_BF16 ? 1 : 2;
+                    // binary32: two passes, or one per 32-row block when the
+                    // wave has an odd number of them
+                    constexpr int PASSES = OUT_BF16 ? 1 : (IM % 2 == 0 ? 2 : IM);
                     constexpr int ROWB = C::WCOLS * ESZ;  // bytes of one staged row
                     constexpr int NCH = ROWB / 16;        // 16-byte chunks per row
                     constexpr int RPP = C::WROWS / PASSES;  // rows per pass
@@ -568,5 +576,6 @@ Gemm16Kern gemm16_kernel_256x256(int f16, int kc, int out16, int cvec);
 Gemm16Kern gemm16_kernel_128x256(int f16, int kc, int out16, int cvec);
 Gemm16Kern gemm16_kernel_256x128(int f16, int kc, int out16, int cvec);
 Gemm16Kern gemm16_kernel_128x128(int f16, int kc, int out16, int cvec);
+Gemm16Kern gemm16_kernel_192x256(int f16, int kc, int out16, int cvec);
 
 }  // namespace bi

@@ -2,8 +2,8 @@
 
 The library computes a 16-bit product either with the persistent 256x256
 kernel or, where those tiles would leave most compute units idle, with
-one-wave (32, 64 or 128) x 64 blocks, or with 128x256 or 128x128 persistent
-tiles; the choice is a function of the shape.
+one-wave (32, 64 or 128) x 64 blocks, or with 128x256, 128x128 or 192x256
+persistent tiles; the choice is a function of the shape.
 Both must give the same bits for every element.  Here each forced tile size is
 compared bit for bit with the persistent kernel on ragged shapes (M, N, K
 tails, one row, K = 8), both B layouts, column bias (addmm) and row bias (the
@@ -27,7 +27,7 @@ pytestmark = pytest.mark.gpu
 if torch.cuda.is_available():
     from invariant_persistent_bf16_amd import bi, bi_bench
 DEV = "cuda"
-TILES = (1, 2, 3, 32, 64, 128)   # 1 / 2 / 3: the persistent kernel with 128x256 / 256x128 / 128x128 tiles
+TILES = (1, 2, 3, 4, 32, 64, 128)   # 1 / 2 / 3 / 4: the persistent kernel with 128x256 / 256x128 / 128x128 / 192x256 tiles
 
 
 def _operands(G, M, N, K, b_layout, dtype, seed):
@@ -106,7 +106,7 @@ def test_small_tiles_element_epilogue():
     for od, tdt in ((bi.BI_F32, torch.float32), (bi.BI_BF16, torch.bfloat16)):
         big = torch.full((M, N + 3), 7.0, dtype=tdt, device=DEV)
         ref = bi_bench.gemm_tile(A, B, 0, bias=bias, out_dtype=od)
-        for t in (1, 2, 32):
+        for t in (1, 2, 4, 32):
             big.fill_(7.0)
             out = bi_bench.gemm_tile(A, B, t, bias=bias, out_dtype=od, out=big[:, :N])
             torch.cuda.synchronize()
@@ -133,7 +133,9 @@ def test_auto_choice_on_batch1_linear_and_conv():
     assert bi_bench.gemm_tile_rows(1, 8192, 14336, 4096) == 0
     assert bi_bench.gemm_tile_rows(1, 1152, 256, 592) == 32      # conv, one image
     assert bi_bench.gemm_tile_rows(4, 1152, 256, 592) == 3       # conv, 4 images
-    assert bi_bench.gemm_tile_rows(32, 1152, 256, 592) == 0      # conv, 32 images
+    assert bi_bench.gemm_tile_rows(1, 768, 14336, 4096) == 4      # 192x256, one round
+    assert bi_bench.gemm_tile_rows(32, 1152, 256, 592) == 4      # conv, 32 images: 192x256
+    assert bi_bench.gemm_tile_rows(48, 1152, 256, 592) == 0      # conv, 48 images
     W, bias, x0 = synth.addmm_shared()
     Wd, bd = W.to(DEV), bias.to(DEV)
     X = synth.addmm_batch(x0, 200, device=DEV)
