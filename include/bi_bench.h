@@ -40,8 +40,8 @@ int bi_bench_gemm_grid(int64_t G, int64_t M, int64_t N, int64_t K,
  * bi_bench_gemm_tile — the invariant GEMM of bi_bmm with the kernel forced.
  * 16-bit operands: tile_rows 0 = the persistent kernel with 256x256 tiles,
  * 1 = the persistent kernel with 128x256 tiles, 2 = with 256x128 tiles,
- * 3 = with 128x128 tiles, 32 / 64 / 128 = the small-tile kernel with
- * (tile_rows x 64) blocks, one wave each.
+ * 3 = with 128x128 tiles, 4 = with 192x256 tiles, 32 / 64 / 128 = the
+ * small-tile kernel with (tile_rows x 64) blocks, one wave each.
  * Binary32 operands: 0 = 64x64 tiles, 32 = 32x32 tiles (others:
  * BI_ERR_UNSUPPORTED).  bias (or NULL) is indexed by column (bias_rows 0, as
  * bi_addmm) or by row (1, as the convolution's output channels).  Every

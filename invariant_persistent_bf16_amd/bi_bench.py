@@ -71,8 +71,8 @@ def gemm_grid(A, B, grid, bias=None, out=None, out_dtype=None, stream=None):
 
 def gemm_tile(A, B, tile_rows, bias=None, bias_rows=False, out=None, out_dtype=None, stream=None):
     """The invariant 16-bit batched GEMM (A [G,M,K] or [M,K]) with the kernel
-    forced: tile_rows 0 / 1 / 2 / 3 = persistent 256x256 / 128x256 / 256x128 /
-    128x128, 32 / 64 / 128 = small tile."""
+    forced: tile_rows 0 / 1 / 2 / 3 / 4 = persistent 256x256 / 128x256 / 256x128 /
+    128x128 / 192x256, 32 / 64 / 128 = small tile."""
     squeeze = A.dim() == 2
     if squeeze:
         A, B = A.unsqueeze(0), B.unsqueeze(0)
