@@ -1,6 +1,8 @@
 // Kernel table of the persistent 16-bit GEMM for one tile shape.  Each tile
 // shape is instantiated in its own translation unit (gemm16_*.hip) so that
-// the library's sources compile in parallel.
+// the library's sources compile in parallel.  Every shape must need more than
+// half of a compute unit's 160 KiB of LDS, so that two of its workgroups never
+// share a compute unit (the regime the kernel is verified in).
 #pragma once
 
 #include "gemm_bf16.hpp"
@@ -8,6 +10,8 @@
 // [f16][B K-contiguous][16-bit out][vector epilogue]
 #define BI_GEMM16_TABLE(BMV, BNV)                                                                          \
     namespace bi {                                                                                         \
+    static_assert(2 * G16Cfg<BMV, BNV>::LDS > 160 * 1024 && G16Cfg<BMV, BNV>::LDS <= 160 * 1024,          \
+                  "exactly one workgroup per compute unit");                                               \
     Gemm16Kern gemm16_kernel_##BMV##x##BNV(int f16, int kc, int out16, int cvec) {                         \
         static const Gemm16Kern t[2][2][2][2] = {                                                          \
             {{{gemm_bf16_persistent<false, 0, false, false, BMV, BNV>,                                     \
