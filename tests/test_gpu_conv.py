@@ -78,6 +78,7 @@ CASES = [
     # an input height that leaves rows unused; then rows of 20 elements.
     (2, 4, 35, 48, 20, 4, 8, (4, 8), (0, 0), (1, 1), 2),
     (1, 3, 20, 20, 8, 5, 5, (5, 5), (0, 0), (1, 1), 1),
+    (2, 5, 27, 24, 16, 4, 6, (4, 6), (0, 0), (1, 1), 1),
 ]
 
 
