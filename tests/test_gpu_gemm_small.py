@@ -106,7 +106,7 @@ def test_small_tiles_element_epilogue():
     for od, tdt in ((bi.BI_F32, torch.float32), (bi.BI_BF16, torch.bfloat16)):
         big = torch.full((M, N + 3), 7.0, dtype=tdt, device=DEV)
         ref = bi_bench.gemm_tile(A, B, 0, bias=bias, out_dtype=od)
-        for t in (1, 2, 4, 32):
+        for t in (1, 2, 3, 4, 32):
             big.fill_(7.0)
             out = bi_bench.gemm_tile(A, B, t, bias=bias, out_dtype=od, out=big[:, :N])
             torch.cuda.synchronize()
