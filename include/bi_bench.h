@@ -58,10 +58,17 @@ int bi_bench_gemm_tile(int64_t G, int64_t M, int64_t N, int64_t K,
 /*
  * bi_bench_gemm_tile_rows — the tile_rows that bi_bmm (G slices) or
  * bi_addmm / bi_mm (G = 1) pick for an M x N x K product on the current
- * device: 0, 1, 2, 32, 64 or 128 for 16-bit operands, 0 or 32 for binary32.
- * Negative bi_status on a bad shape or without a gfx950 device.
+ * device: 0, 1, 2, 3, 4, 32, 64 or 128 for 16-bit operands, 0 or 32 for
+ * binary32.  Negative bi_status on a bad shape or without a gfx950 device.
  */
 int bi_bench_gemm_tile_rows(int64_t G, int64_t M, int64_t N, int64_t K, int in_dtype);
+
+/*
+ * bi_bench_gemm_tile_rows_for — the same choice for a device with `cus`
+ * compute units (host arithmetic only: callable without a GPU).
+ * BI_ERR_SHAPE on a bad shape or cus < 1, BI_ERR_DTYPE on an unknown dtype.
+ */
+int bi_bench_gemm_tile_rows_for(int64_t G, int64_t M, int64_t N, int64_t K, int in_dtype, int cus);
 
 /*
  * bi_bench_splitk_policy — the number of K splits a batch-size-tuned GEMM

@@ -21,6 +21,7 @@ _SIGS = {
     "bi_bench_gemm_tile": (_int, [_i64] * 4 + [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _int, _vp,
                                              _i64, _i64, _i64, _int, _int, _int, _vp]),
     "bi_bench_gemm_tile_rows": (_int, [_i64, _i64, _i64, _i64, _int]),
+    "bi_bench_gemm_tile_rows_for": (_int, [_i64, _i64, _i64, _i64, _int, _int]),
     "bi_bench_splitk_policy": (_int, [_i64, _i64, _i64, _int]),
     "bi_bench_addmm_splitk_workspace_bytes": (_sz, [_i64, _i64, _int]),
     "bi_bench_addmm_splitk": (_int, [_i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i64,
@@ -90,10 +91,18 @@ def gemm_tile(A, B, tile_rows, bias=None, bias_rows=False, out=None, out_dtype=N
 
 
 def gemm_tile_rows(G, M, N, K, in_dtype=_bi.BI_BF16):
-    """The kernel bi_bmm / bi_addmm pick for the shape: 0 (persistent) or 32 / 64 / 128."""
+    """The kernel bi_bmm / bi_addmm pick for the shape: 0..4 (persistent tile shapes) or 32 / 64 / 128."""
     r = lib().bi_bench_gemm_tile_rows(G, M, N, K, in_dtype)
     if r < 0:
         raise RuntimeError(f"bi_bench_gemm_tile_rows: {_bi.lib().bi_status_string(r).decode()}")
+    return r
+
+
+def gemm_tile_rows_for(G, M, N, K, cus, in_dtype=_bi.BI_BF16):
+    """The same choice for a device with `cus` compute units (no GPU needed)."""
+    r = lib().bi_bench_gemm_tile_rows_for(G, M, N, K, in_dtype, cus)
+    if r < 0:
+        raise RuntimeError(f"bi_bench_gemm_tile_rows_for: {_bi.lib().bi_status_string(r).decode()}")
     return r
 
 

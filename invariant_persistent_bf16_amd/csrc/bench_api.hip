@@ -122,15 +122,21 @@ int bi_bench_gemm_tile(int64_t G, int64_t M, int64_t N, int64_t K, const void* A
     return gemm_launch(d, (hipStream_t)stream, 0, tile_rows);
 }
 
-int bi_bench_gemm_tile_rows(int64_t G, int64_t M, int64_t N, int64_t K, int in_dtype) {
-    if (G < 1 || M < 1 || N < 1 || K < 0) return BI_ERR_SHAPE;
+int bi_bench_gemm_tile_rows_for(int64_t G, int64_t M, int64_t N, int64_t K, int in_dtype, int cus) {
+    if (G < 1 || M < 1 || N < 1 || K < 0 || cus < 1) return BI_ERR_SHAPE;
+    if (in_dtype != BI_F32 && in_dtype != BI_BF16 && in_dtype != BI_F16) return BI_ERR_DTYPE;
     GemmDesc d;
     std::memset(&d, 0, sizeof(d));
     d.G1 = G; d.G2 = 1; d.M = M; d.N = N; d.K = K; d.in_dtype = in_dtype;
+    return gemm_tile_rows(d, cus);
+}
+
+int bi_bench_gemm_tile_rows(int64_t G, int64_t M, int64_t N, int64_t K, int in_dtype) {
+    if (G < 1 || M < 1 || N < 1 || K < 0) return BI_ERR_SHAPE;
     int cus = 0;
     int rc = device_cu_count(&cus);
     if (rc != BI_OK) return rc;
-    return gemm_tile_rows(d, cus);
+    return bi_bench_gemm_tile_rows_for(G, M, N, K, in_dtype, cus);
 }
 
 int bi_bench_splitk_policy(int64_t M, int64_t N, int64_t K, int rule) {
