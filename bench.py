@@ -56,8 +56,8 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(every operation shards by request with no exchange; see DESIGN.md).", file=sys.stderr)
+        print("bench.py measures one GPU: there is no multi-GPU path (every operation would shard by "
+              "request, head or output tile with no exchange between GPUs).", file=sys.stderr)
         sys.exit(2)
 
     import torch
