@@ -112,9 +112,10 @@ int bi_addmm(int64_t M, int64_t N, int64_t K,
 /*
  * bi_bmm — C[g] = A[g] @ B[g] for g in [0, G).
  * Source: "Batch-Invariant Kernel Design: Conv2d and Attention BMM", section
- * "Kernel 2: Attention BMM": every batch element gets its own base pointers
- * and the same ordered K reduction, so adding elements adds independent work.
- * Slice g of the result is bit-identical to bi_mm on A[g], B[g] alone.
+ * "Kernel 2: Attention BMM".  Slice g is a product of its own: its operands
+ * start g slice strides into A, B and C, and its K sum runs in the order any
+ * other slice uses, so G never enters its arithmetic.  Slice g of the result
+ * is bit-identical to bi_mm on A[g], B[g] alone.
  * Element strides sAg, sBg, sCg step between slices (0 broadcasts an operand).
  * Layout rules per slice: as bi_mm, and for 16-bit dtypes sAg % 8 == sBg % 8 == 0.
  */

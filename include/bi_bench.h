@@ -56,6 +56,22 @@ int bi_bench_gemm_tile(int64_t G, int64_t M, int64_t N, int64_t K,
                        int in_dtype, int out_dtype, int tile_rows, void* stream);
 
 /*
+ * bi_bench_gemm_shared_cu — the invariant GEMM of bi_bmm (bfloat16 operands,
+ * optional column bias as bi_addmm) on the persistent kernel with 128x128
+ * tiles compiled without its LDS reservation (66 KiB per workgroup instead of
+ * 81), launched on `grid` workgroups (1 <= grid <= 65535): with a grid above
+ * the compute-unit count two of its workgroups share a compute unit.  Output
+ * layouts that allow 16-byte row stores only (else BI_ERR_LAYOUT).  Its
+ * results must equal bi_bmm's bit for bit.
+ */
+int bi_bench_gemm_shared_cu(int64_t G, int64_t M, int64_t N, int64_t K,
+                            const void* A, int64_t sAg, int64_t sAm, int64_t sAk,
+                            const void* B, int64_t sBg, int64_t sBk, int64_t sBn,
+                            const void* bias,
+                            void* C, int64_t sCg, int64_t sCm, int64_t sCn,
+                            int in_dtype, int out_dtype, int grid, void* stream);
+
+/*
  * bi_bench_gemm_tile_rows — the tile_rows that bi_bmm (G slices) or
  * bi_addmm / bi_mm (G = 1) pick for an M x N x K product on the current
  * device: 0, 1, 2, 3, 4, 32, 64 or 128 for 16-bit operands, 0 or 32 for

@@ -103,10 +103,21 @@ def _check(fn, rc):
         raise BIError(fn, rc)
 
 
-def _out(shape, out_dtype, device, out):
+def _empty(shape, dtype, device, stream):
+    """A new device tensor owned by the stream the kernels run on.  torch's
+    caching allocator hands a freed block only to later allocations on the
+    stream that owns it; a workspace allocated on another stream than the
+    kernel's could be reused there while the kernel still reads it."""
+    if stream is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
+def _out(shape, out_dtype, device, out, stream=None):
     if out is not None:
         return out
-    return torch.empty(shape, dtype=_tdt(out_dtype), device=device)
+    return _empty(shape, _tdt(out_dtype), device, stream)
 
 
 def bi_mm(A, B, out=None, out_dtype=None, stream=None):
@@ -114,7 +125,7 @@ def bi_mm(A, B, out=None, out_dtype=None, stream=None):
     M, K = A.shape
     N = B.shape[1]
     od = _dt(A) if out_dtype is None else out_dtype
-    C = _out((M, N), od, A.device, out)
+    C = _out((M, N), od, A.device, out, stream)
     _check("bi_mm", lib().bi_mm(M, N, K, _p(A), A.stride(0), A.stride(1), _p(B), B.stride(0),
                                 B.stride(1), _p(C), C.stride(0), C.stride(1), _dt(A), _dt(C),
                                 _stream(stream)))
@@ -126,7 +137,7 @@ def bi_addmm(bias, A, B, out=None, out_dtype=None, stream=None):
     M, K = A.shape
     N = B.shape[1]
     od = _dt(A) if out_dtype is None else out_dtype
-    C = _out((M, N), od, A.device, out)
+    C = _out((M, N), od, A.device, out, stream)
     _check("bi_addmm", lib().bi_addmm(M, N, K, _p(A), A.stride(0), A.stride(1), _p(B), B.stride(0),
                                       B.stride(1), _p(bias), _p(C), C.stride(0), C.stride(1),
                                       _dt(A), _dt(C), _stream(stream)))
@@ -138,7 +149,7 @@ def bi_bmm(A, B, out=None, out_dtype=None, stream=None):
     G, M, K = A.shape
     N = B.shape[2]
     od = _dt(A) if out_dtype is None else out_dtype
-    C = _out((G, M, N), od, A.device, out)
+    C = _out((G, M, N), od, A.device, out, stream)
     _check("bi_bmm", lib().bi_bmm(G, M, N, K, _p(A), A.stride(0), A.stride(1), A.stride(2),
                                   _p(B), B.stride(0), B.stride(1), B.stride(2),
                                   _p(C), C.stride(0), C.stride(1), C.stride(2),
@@ -168,10 +179,10 @@ def bi_conv2d(x, w, bias=None, stride=(1, 1), padding=(0, 0), dilation=(1, 1), g
     Cout, _, Kh, Kw = w.shape
     OH, OW = conv_out_hw(H, W, Kh, Kw, stride, padding, dilation)
     od = _dt(x) if out_dtype is None else out_dtype
-    y = _out((N, Cout, OH, OW), od, x.device, out)
+    y = _out((N, Cout, OH, OW), od, x.device, out, stream)
     need = bi_conv2d_workspace_bytes(x.shape, w.shape, stride, padding, dilation, groups, _dt(x))
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+        workspace = _empty(max(need, 1), torch.uint8, x.device, stream)
     _check("bi_conv2d", lib().bi_conv2d(N, Cin, H, W, _p(x), Cout, Kh, Kw, _p(w), _p(bias),
                                         stride[0], stride[1], padding[0], padding[1], dilation[0],
                                         dilation[1], groups, _p(y), _p(workspace),
@@ -191,10 +202,10 @@ def bi_decode_attn_workspace_bytes(B, H, S, D):
 def bi_decode_attn(q, k, v, scale, out=None, out_dtype=BI_F32, workspace=None, stream=None):
     """Fixed-chunk split-KV decode attention: q [B,H,D], k, v [B,H,S,D] -> out [B,H,D]."""
     B, H, S, D = k.shape
-    o = _out((B, H, D), out_dtype, q.device, out)
+    o = _out((B, H, D), out_dtype, q.device, out, stream)
     need = bi_decode_attn_workspace_bytes(B, H, S, D)
     if workspace is None:
-        workspace = torch.empty(max(need // 4, 1), dtype=torch.float32, device=q.device)
+        workspace = _empty(max(need // 4, 1), torch.float32, q.device, stream)
     _check("bi_decode_attn", lib().bi_decode_attn(B, H, S, D, _p(q), _p(k), _p(v), _p(o),
                                                   float(scale), _p(workspace),
                                                   workspace.numel() * workspace.element_size(),
@@ -214,10 +225,10 @@ def bi_decode_attn_paged(q, k_cache, v_cache, block_table, seq_lens, max_seq_len
     num_pages, _, P, _ = k_cache.shape
     if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
         raise TypeError("block_table and seq_lens must be int32")
-    o = _out((B, H, D), out_dtype, q.device, out)
+    o = _out((B, H, D), out_dtype, q.device, out, stream)
     need = bi_decode_attn_paged_workspace_bytes(B, H, max_seq_len, D)
     if workspace is None:
-        workspace = torch.empty(max(need // 4, 1), dtype=torch.float32, device=q.device)
+        workspace = _empty(max(need // 4, 1), torch.float32, q.device, stream)
     _check("bi_decode_attn_paged", lib().bi_decode_attn_paged(
         B, H, D, _p(q), _p(k_cache), _p(v_cache), num_pages, P, _p(block_table), block_table.shape[1],
         _p(seq_lens), int(max_seq_len), _p(o), float(scale), _p(workspace),
@@ -240,10 +251,10 @@ def bi_prefill_attn_paged(q, cu_q, q_pos0, max_q, k_cache, v_cache, block_table,
     for t in (cu_q, q_pos0, block_table):
         if t.dtype != torch.int32:
             raise TypeError("cu_q, q_pos0 and block_table must be int32")
-    o = _out((T, H, D), out_dtype, q.device, out)
+    o = _out((T, H, D), out_dtype, q.device, out, stream)
     need = bi_prefill_attn_paged_workspace_bytes(T, H, max_kv_len, D)
     if workspace is None and need > 0:
-        workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+        workspace = _empty(need // 4, torch.float32, q.device, stream)
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("bi_prefill_attn_paged", lib().bi_prefill_attn_paged(
         B, H, D, _p(q), T, _p(cu_q), _p(q_pos0), int(max_q), _p(k_cache), _p(v_cache), num_pages, P,
@@ -255,7 +266,7 @@ def bi_prefill_attn_paged(q, cu_q, q_pos0, max_q, k_cache, v_cache, block_table,
 def bi_softmax_rows(S, scale, out=None, out_dtype=BI_BF16, stream=None):
     """P = softmax(scale * S) row-wise; S a float32 matrix [rows, cols]."""
     rows, cols = S.shape
-    P = _out((rows, cols), out_dtype, S.device, out)
+    P = _out((rows, cols), out_dtype, S.device, out, stream)
     _check("bi_softmax_rows", lib().bi_softmax_rows(rows, cols, _p(S), S.stride(0), float(scale), _p(P),
                                                     P.stride(0), _dt(P), _stream(stream)))
     return P
@@ -265,7 +276,7 @@ def bi_rms_norm(x, w, eps=1e-6, out=None, out_dtype=None, stream=None):
     """y = RMSNorm(x) * w over the last dimension of x [rows, cols]."""
     rows, cols = x.shape
     od = _dt(x) if out_dtype is None else out_dtype
-    y = _out((rows, cols), od, x.device, out)
+    y = _out((rows, cols), od, x.device, out, stream)
     _check("bi_rms_norm", lib().bi_rms_norm(rows, cols, _p(x), x.stride(0), _p(w), float(eps), _p(y),
                                             y.stride(0), _dt(x), _dt(y), _stream(stream)))
     return y
@@ -275,7 +286,7 @@ def bi_log_softmax_rows(x, out=None, out_dtype=None, stream=None):
     """log-softmax over the last dimension of x [rows, cols]."""
     rows, cols = x.shape
     od = _dt(x) if out_dtype is None else out_dtype
-    y = _out((rows, cols), od, x.device, out)
+    y = _out((rows, cols), od, x.device, out, stream)
     _check("bi_log_softmax_rows", lib().bi_log_softmax_rows(rows, cols, _p(x), x.stride(0), _p(y), y.stride(0),
                                                             _dt(x), _dt(y), _stream(stream)))
     return y
@@ -284,7 +295,7 @@ def bi_log_softmax_rows(x, out=None, out_dtype=None, stream=None):
 def bi_mean_rows(x, out=None, out_dtype=BI_F32, stream=None):
     """Mean over the last dimension of x [rows, cols] -> [rows]."""
     rows, cols = x.shape
-    y = _out((rows,), out_dtype, x.device, out)
+    y = _out((rows,), out_dtype, x.device, out, stream)
     _check("bi_mean_rows", lib().bi_mean_rows(rows, cols, _p(x), x.stride(0), _p(y), _dt(x), _dt(y),
                                               _stream(stream)))
     return y

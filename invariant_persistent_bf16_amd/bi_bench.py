@@ -20,6 +20,8 @@ _SIGS = {
                                              _i64, _i64, _i64, _int, _int, _int, _vp]),
     "bi_bench_gemm_tile": (_int, [_i64] * 4 + [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _int, _vp,
                                              _i64, _i64, _i64, _int, _int, _int, _vp]),
+    "bi_bench_gemm_shared_cu": (_int, [_i64] * 4 + [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _vp,
+                                                  _i64, _i64, _i64, _int, _int, _int, _vp]),
     "bi_bench_gemm_tile_rows": (_int, [_i64, _i64, _i64, _i64, _int]),
     "bi_bench_gemm_tile_rows_for": (_int, [_i64, _i64, _i64, _i64, _int, _int]),
     "bi_bench_splitk_policy": (_int, [_i64, _i64, _i64, _int]),
@@ -49,7 +51,7 @@ def lib():
     return _lib
 
 
-_p, _dt, _stream, _check = _bi._p, _bi._dt, _bi._stream, _bi._check
+_p, _dt, _stream, _check, _empty = _bi._p, _bi._dt, _bi._stream, _bi._check, _bi._empty
 
 
 def gemm_grid(A, B, grid, bias=None, out=None, out_dtype=None, stream=None):
@@ -60,10 +62,29 @@ def gemm_grid(A, B, grid, bias=None, out=None, out_dtype=None, stream=None):
     G, M, K = A.shape
     N = B.shape[2]
     od = _dt(A) if out_dtype is None else out_dtype
-    C = out if out is not None else torch.empty((G, M, N), dtype=_bi._tdt(od), device=A.device)
+    C = out if out is not None else _empty((G, M, N), _bi._tdt(od), A.device, stream)
     if C.dim() == 2:
         C = C.unsqueeze(0)
     _check("bi_bench_gemm_grid", lib().bi_bench_gemm_grid(
+        G, M, N, K, _p(A), A.stride(0), A.stride(1), A.stride(2), _p(B), B.stride(0), B.stride(1),
+        B.stride(2), _p(bias), _p(C), C.stride(0), C.stride(1), C.stride(2), _dt(A), _dt(C), grid,
+        _stream(stream)))
+    return C[0] if squeeze else C
+
+
+def gemm_shared_cu(A, B, grid, bias=None, out=None, out_dtype=None, stream=None):
+    """The invariant batched bf16 GEMM on the 128x128-tile kernel without its
+    LDS reservation, on a forced grid (two workgroups may share a CU)."""
+    squeeze = A.dim() == 2
+    if squeeze:
+        A, B = A.unsqueeze(0), B.unsqueeze(0)
+    G, M, K = A.shape
+    N = B.shape[2]
+    od = _dt(A) if out_dtype is None else out_dtype
+    C = out if out is not None else _empty((G, M, N), _bi._tdt(od), A.device, stream)
+    if C.dim() == 2:
+        C = C.unsqueeze(0)
+    _check("bi_bench_gemm_shared_cu", lib().bi_bench_gemm_shared_cu(
         G, M, N, K, _p(A), A.stride(0), A.stride(1), A.stride(2), _p(B), B.stride(0), B.stride(1),
         B.stride(2), _p(bias), _p(C), C.stride(0), C.stride(1), C.stride(2), _dt(A), _dt(C), grid,
         _stream(stream)))
@@ -80,7 +101,7 @@ def gemm_tile(A, B, tile_rows, bias=None, bias_rows=False, out=None, out_dtype=N
     G, M, K = A.shape
     N = B.shape[2]
     od = _dt(A) if out_dtype is None else out_dtype
-    C = out if out is not None else torch.empty((G, M, N), dtype=_bi._tdt(od), device=A.device)
+    C = out if out is not None else _empty((G, M, N), _bi._tdt(od), A.device, stream)
     if C.dim() == 2:
         C = C.unsqueeze(0)
     _check("bi_bench_gemm_tile", lib().bi_bench_gemm_tile(
@@ -117,10 +138,10 @@ def addmm_splitk(bias, A, B, splits, out=None, out_dtype=None, workspace=None, s
     M, K = A.shape
     N = B.shape[1]
     od = _dt(A) if out_dtype is None else out_dtype
-    C = out if out is not None else torch.empty((M, N), dtype=_bi._tdt(od), device=A.device)
+    C = out if out is not None else _empty((M, N), _bi._tdt(od), A.device, stream)
     need = lib().bi_bench_addmm_splitk_workspace_bytes(M, N, splits)
     if workspace is None:
-        workspace = torch.empty(max(need // 4, 1), dtype=torch.float32, device=A.device)
+        workspace = _empty(max(need // 4, 1), torch.float32, A.device, stream)
     _check("bi_bench_addmm_splitk", lib().bi_bench_addmm_splitk(
         M, N, K, _p(A), A.stride(0), A.stride(1), _p(B), B.stride(0), B.stride(1), _p(bias), _p(C),
         C.stride(0), C.stride(1), _dt(A), _dt(C), splits, _p(workspace),
@@ -135,10 +156,10 @@ def decode_splits_policy(B, sms):
 def decode_attn_splits(q, k, v, scale, splits, out=None, out_dtype=_bi.BI_F32, workspace=None,
                        stream=None):
     B, H, S, D = k.shape
-    o = out if out is not None else torch.empty((B, H, D), dtype=_bi._tdt(out_dtype), device=q.device)
+    o = out if out is not None else _empty((B, H, D), _bi._tdt(out_dtype), q.device, stream)
     need = lib().bi_bench_decode_attn_splits_workspace_bytes(B, H, S, D, splits)
     if workspace is None:
-        workspace = torch.empty(max(need // 4, 1), dtype=torch.float32, device=q.device)
+        workspace = _empty(max(need // 4, 1), torch.float32, q.device, stream)
     _check("bi_bench_decode_attn_splits", lib().bi_bench_decode_attn_splits(
         B, H, S, D, _p(q), _p(k), _p(v), _p(o), float(scale), _p(workspace),
         workspace.numel() * workspace.element_size(), _dt(q), _dt(o), splits, _stream(stream)))

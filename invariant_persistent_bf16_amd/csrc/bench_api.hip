@@ -122,6 +122,41 @@ int bi_bench_gemm_tile(int64_t G, int64_t M, int64_t N, int64_t K, const void* A
     return gemm_launch(d, (hipStream_t)stream, 0, tile_rows);
 }
 
+int bi_bench_gemm_shared_cu(int64_t G, int64_t M, int64_t N, int64_t K, const void* A, int64_t sAg,
+                            int64_t sAm, int64_t sAk, const void* B, int64_t sBg, int64_t sBk,
+                            int64_t sBn, const void* bias, void* C, int64_t sCg, int64_t sCm,
+                            int64_t sCn, int in_dtype, int out_dtype, int grid, void* stream) {
+    if (grid < 1 || grid > 65535) return BI_ERR_UNSUPPORTED;
+    if (in_dtype != BI_BF16) return BI_ERR_DTYPE;
+    GemmDesc d;
+    std::memset(&d, 0, sizeof(d));
+    d.G1 = G; d.G2 = 1; d.M = M; d.N = N; d.K = K;
+    d.A = A; d.sA1 = sAg; d.sAm = sAm; d.sAk = sAk;
+    d.B = B; d.sB1 = sBg; d.sBk = sBk; d.sBn = sBn;
+    d.bias = bias; d.C = C; d.sC1 = sCg; d.sCm = sCm; d.sCn = sCn;
+    d.in_dtype = in_dtype; d.out_dtype = out_dtype;
+    int rc = gemm_check(d);
+    if (rc != BI_OK) return rc;
+    if (G == 0 || M == 0 || N == 0) return BI_OK;
+    const int osz = out_dtype == BI_F32 ? 4 : 2, vel = 16 / osz;
+    // The vector epilogue only (16-byte row stores).
+    if ((uintptr_t)C % 16 || N % vel || sCm % vel || sCg % vel) return BI_ERR_LAYOUT;
+    const bool kc = K == 0 || (sBk == 1 && (N == 1 || sBn % 8 == 0));
+    GemmParams p;
+    p.A = (const uint16_t*)A; p.B = (const uint16_t*)B; p.bias = (const uint16_t*)bias; p.C = C;
+    p.M = M; p.N = N; p.K = K;
+    p.sAm = sAm; p.sBk = sBk; p.sBn = sBn; p.sCm = sCm;
+    p.G2 = 1;
+    p.sA1 = sAg; p.sA2 = 0; p.sB1 = sBg; p.sB2 = 0; p.sC1 = sCg; p.sC2 = 0; p.sBias2 = 0; p.bias_rows = 0;
+    p.tiles_m = (int)cdiv(M, 128);
+    p.tiles_n = (int)cdiv(N, 128);
+    p.tiles_per_slice = p.tiles_m * p.tiles_n;
+    p.total_tiles = (int)(p.tiles_per_slice * G);
+    hipLaunchKernelGGL(gemm16_kernel_128x128_shared(kc ? 1 : 0, out_dtype == BI_F32 ? 0 : 1), dim3(grid),
+                       dim3(G16_THREADS), 0, (hipStream_t)stream, p);
+    return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_LAUNCH;
+}
+
 int bi_bench_gemm_tile_rows_for(int64_t G, int64_t M, int64_t N, int64_t K, int in_dtype, int cus) {
     if (G < 1 || M < 1 || N < 1 || K < 0 || cus < 1) return BI_ERR_SHAPE;
     if (in_dtype != BI_F32 && in_dtype != BI_BF16 && in_dtype != BI_F16) return BI_ERR_DTYPE;

@@ -1,8 +1,8 @@
 // Kernel table of the persistent 16-bit GEMM for one tile shape.  Each tile
 // shape is instantiated in its own translation unit (gemm16_*.hip) so that
-// the library's sources compile in parallel.  Every shape must need more than
-// half of a compute unit's 160 KiB of LDS, so that two of its workgroups never
-// share a compute unit (the regime the kernel is verified in).
+// the library's sources compile in parallel.  Every shape reserves more than
+// half of a compute unit's 160 KiB of LDS, so that the persistent grid (at
+// most one workgroup per compute unit) lands one workgroup on each unit.
 #pragma once
 
 #include "gemm_bf16.hpp"

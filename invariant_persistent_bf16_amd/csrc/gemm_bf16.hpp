@@ -74,7 +74,7 @@ constexpr uint32_t G16_OOB = 0x80000000u;                         // buffer offs
 // M a multiple of 192, such as the 1152 output channels of the patch
 // convolution), or 256 x 128 (each wave 128x64, for N <= 128, which would
 // fill half of a 256-wide tile).
-template <int BM, int BN>
+template <int BM, int BN, bool ONE_PER_CU = true>
 struct G16Cfg {
     static constexpr int WROWS = BM / 2;                        // rows of a wave's block
     static constexpr int WCOLS = BN / 2;                        // its columns
@@ -85,12 +85,14 @@ struct G16Cfg {
     static constexpr int B_BASE = G16_NSTAGE * A_STAGE;         // B stages after the A stages
     static constexpr int RING = G16_NSTAGE * (A_STAGE + B_STAGE);
     static constexpr int BIAS = (BM + BN) * 4;                  // row and column bias, binary32
-    // Bias double buffered after the ring.  At least 81 KiB in all, so that
-    // two workgroups never share a compute unit: every shape then runs one
-    // workgroup (one wave per SIMD) per compute unit, the regime the kernel
-    // is verified in.  With two 128x128 workgroups per unit (66 KiB each)
-    // some accumulator values reached the output corrupted.
-    static constexpr int LDS = RING + 2 * BIAS > 81 * 1024 ? RING + 2 * BIAS : 81 * 1024;
+    // Bias double buffered after the ring.  ONE_PER_CU: at least 81 KiB in
+    // all, so that two of the kernel's workgroups never share a compute unit.
+    // The grid is at most one workgroup per compute unit, and the dispatcher
+    // does not promise to spread it: two 128x128 workgroups (66 KiB each) on
+    // one unit would run at half speed beside an idle one.  The arithmetic
+    // does not depend on it (ONE_PER_CU = false, a test-only variant, runs
+    // two workgroups per unit and gives the same bits).
+    static constexpr int LDS = (ONE_PER_CU && RING + 2 * BIAS < 81 * 1024) ? 81 * 1024 : RING + 2 * BIAS;
     static constexpr int NA = BM / 64;                          // A copies per wave and step
     static constexpr int NB = BN / 64;                          // B copies per wave and step
     static constexpr int NDMA = NA + NB;
@@ -192,10 +194,11 @@ struct G16Frags {
 // operands' type (else binary32).
 // BM x BN: tile shape, 256 x 256, 128 x 256, 256 x 128, 128 x 128 or 192 x 256 (G16Cfg); the
 // per-element arithmetic is the same for all.
-template <bool B_KCONTIG, int OUT_BF16, bool CVEC, bool F16 = false, int BM = 256, int BN = 256>
+template <bool B_KCONTIG, int OUT_BF16, bool CVEC, bool F16 = false, int BM = 256, int BN = 256,
+          bool ONE_PER_CU = true>
 __global__ void __launch_bounds__(G16_THREADS, 1)
 gemm_bf16_persistent(GemmParams p) {
-    using C = G16Cfg<BM, BN>;
+    using C = G16Cfg<BM, BN, ONE_PER_CU>;
     constexpr int IM = C::IM, IN = C::IN;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
 
@@ -443,8 +446,15 @@ gemm_bf16_persistent(GemmParams p) {
             if (kt + 3 < nk) step(kt + 3, std::integral_constant<int, 3>{});
         }
         // Drain every copy (including the ones past the last step) and every
-        // read before the next tile reuses the stages.
+        // read before the next tile reuses the stages.  The last step's reads
+        // of the next fragments are dead, but the hardware still writes their
+        // registers when they return; the fences keep both fragment sets
+        // allocated until after the wait, so the compiler cannot place an
+        // epilogue value (an accumulator copied out of its AGPR) in one of
+        // them before the late read lands there.
         g16_wait_vm_lgkm0<0>();
+        fence_frags(F0);
+        fence_frags(F1);
         __builtin_amdgcn_s_barrier();
 
         // ---- epilogue: + bias (binary32, once), round once, store.
@@ -577,5 +587,8 @@ Gemm16Kern gemm16_kernel_128x256(int f16, int kc, int out16, int cvec);
 Gemm16Kern gemm16_kernel_256x128(int f16, int kc, int out16, int cvec);
 Gemm16Kern gemm16_kernel_128x128(int f16, int kc, int out16, int cvec);
 Gemm16Kern gemm16_kernel_192x256(int f16, int kc, int out16, int cvec);
+// 128x128 tiles without the 81 KiB reservation (two workgroups per compute
+// unit; bfloat16 operands, vector epilogue; benchmark library only).
+Gemm16Kern gemm16_kernel_128x128_shared(int kc, int out16);
 
 }  // namespace bi

@@ -152,43 +152,57 @@ def test_decode_request_subset():
 
 
 # ---------------------------------------------- the handbook's experiments
+# Both experiments are driven by the fixture: its setup holds the sizes, the
+# seed and the parameters of the two split rules, and its booleans are the
+# ones the page prints.  The binary32 simulations are the oracle's C code.
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _row0_pattern(X, W, x0, batches, split_rule):
+    """For each batch size M: does row 0 of the split-K product of X[M] equal
+    the product of x0 alone, each with the split count split_rule gives?"""
+    alone = oracle.sim_splitk_gemm_f32(x0, W, split_rule(1))[0].numpy()
+    return [bool(np.array_equal(oracle.sim_splitk_gemm_f32(X[m], W, split_rule(m))[0].numpy(), alone))
+            for m in batches]
+
+
 def test_handbook_splitk_pattern():
-    g = json.load(open(os.path.join(GOLDEN, "handbook_splitk_gemm.json")))
-    K, N = g["setup"]["K"], g["setup"]["N"]
-    W, X = synth.mm_inputs(Ms=g["batches"], K=K, N=N, seed=g["setup"]["seed"])
-    mine = X[g["batches"][0]][:1]
-    for invariant, key in ((False, "row0_equals_alone_by_batch"), (True, "row0_equals_alone_fixed")):
-        def splits(M):
-            return 1 if invariant or M >= 64 else 4
-        alone = oracle.sim_splitk_gemm_f32(mine, W, splits(1))[0]
-        got = [bool(torch.equal(oracle.sim_splitk_gemm_f32(X[M], W, splits(M))[0], alone))
-               for M in g["batches"]]
-        assert got == g[key]
+    g = _golden("handbook_splitk_gemm.json")
+    st = g["setup"]
+    W, X = synth.mm_inputs(Ms=g["batches"], K=st["K"], N=st["N"], seed=st["seed"])
+    x0 = X[g["batches"][0]][:1]
+    tuned = st["tuned"]
+    rules = {
+        "row0_equals_alone_by_batch": lambda m: tuned["splits"] if m < tuned["below_batch"] else 1,
+        "row0_equals_alone_fixed": lambda m: st["fixed_splits"],
+    }
+    for key, rule in rules.items():
+        assert _row0_pattern(X, W, x0, g["batches"], rule) == g[key], key
 
 
 def test_handbook_decode_pattern():
-    g = json.load(open(os.path.join(GOLDEN, "handbook_decode_splits.json")))
-    D, S = g["setup"]["D"], g["setup"]["S"]
-    gen = torch.Generator().manual_seed(g["setup"]["seed"])
-    q = torch.randn(D, generator=gen)
-    K = torch.randn(S, D, generator=gen)
-    V = torch.randn(S, D, generator=gen)
+    g = _golden("handbook_decode_splits.json")
+    st = g["setup"]
+    D, S = st["D"], st["S"]
+    gen = torch.Generator().manual_seed(st["seed"])
+    q, K, V = (torch.randn(shape, generator=gen) for shape in ((D,), (S, D), (S, D)))
     scale = 1 / D ** 0.5
-
-    def by_load(b, sms=132):
-        return max(1, min(64, sms // b))
-
-    assert [by_load(b) for b in g["batches"]] == g["splits_by_load"]
-    ref = oracle.sim_decode_splits_f32(q, K, V, scale, by_load(1))
-    got = [bool(torch.equal(oracle.sim_decode_splits_f32(q, K, V, scale, by_load(b)), ref))
-           for b in g["batches"]]
-    assert got == g["equal_to_batch1_by_load"]
-    nfix = -(-S // 2048)
-    assert nfix == g["splits_fixed"]
-    fixed = [oracle.sim_decode_splits_f32(q, K, V, scale, nfix) for _ in g["batches"]]
-    assert all(torch.equal(f, fixed[0]) for f in fixed) == g["fixed_all_equal"]
-    unsplit = torch.softmax(K @ q / D ** 0.5, 0) @ V
-    assert torch.allclose(fixed[0], unsplit, atol=g["fixed_allclose_unsplit_atol"]) == g["fixed_allclose_unsplit"]
-    # The fixed-chunk fp64 oracle agrees with the binary32 simulation to binary32 accuracy.
-    o64 = oracle.decode_chunked(q.to(torch.float32)[None, None], K[None, None], V[None, None], scale)[0, 0]
-    np.testing.assert_allclose(fixed[0].double().numpy(), o64, rtol=0, atol=1e-5)
+    by_load = st["by_load"]
+    parts = [min(by_load["max_parts"], max(1, by_load["units"] // b)) for b in g["batches"]]
+    assert parts == g["splits_by_load"]
+    results = {n: oracle.sim_decode_splits_f32(q, K, V, scale, n).numpy() for n in sorted(set(parts))}
+    assert [bool(np.array_equal(results[n], results[parts[0]])) for n in parts] == g["equal_to_batch1_by_load"]
+    # fixed-length chunks: the part count is a function of S only
+    n_fixed = -(-S // st["fixed_chunk"])
+    assert n_fixed == g["splits_fixed"]
+    fixed = [oracle.sim_decode_splits_f32(q, K, V, scale, n_fixed).numpy() for _ in g["batches"]]
+    assert (len({f.tobytes() for f in fixed}) == 1) == g["fixed_all_equal"]
+    # against unsplit attention (the fp64 oracle, one query)
+    unsplit = oracle.decode(q[None, None], K[None, None], V[None, None], scale)[0, 0]
+    close = bool(np.max(np.abs(fixed[0].astype(np.float64) - unsplit)) <= g["fixed_allclose_unsplit_atol"])
+    assert close == g["fixed_allclose_unsplit"]
+    # the fixed-chunk fp64 oracle agrees with the binary32 simulation to binary32 accuracy
+    o64 = oracle.decode_chunked(q[None, None], K[None, None], V[None, None], scale)[0, 0]
+    np.testing.assert_allclose(fixed[0].astype(np.float64), o64, rtol=0, atol=1e-5)
