@@ -58,7 +58,8 @@ typedef enum {
     BI_ERR_UNSUPPORTED = -5, /* valid request outside what is implemented */
     BI_ERR_WORKSPACE = -6,   /* workspace NULL, too small or misaligned */
     BI_ERR_LAUNCH = -7,      /* the HIP runtime refused a launch or query */
-    BI_ERR_DEVICE = -8       /* no usable gfx950 device is current */
+    BI_ERR_DEVICE = -8,      /* no usable gfx950 device is current */
+    BI_ERR_SCRATCH = -9      /* more than a no-allocation entry point's static scratch */
 } bi_status;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -183,6 +184,29 @@ int bi_decode_attn(int64_t B, int64_t H, int64_t S, int64_t D,
                    const void* q, const void* k, const void* v, void* out,
                    float scale, void* ws, size_t ws_bytes,
                    int in_dtype, int out_dtype, void* stream);
+
+/*
+ * bi_decode_attn_noalloc — bi_decode_attn without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops that must not call hipMalloc, harnesses that forbid it).
+ * Same arguments, layouts, kernels and bits as bi_decode_attn; the chunk
+ * triples go to a static device array of BI_DECODE_SCRATCH_BYTES per GPU
+ * (held from the library's first use on that GPU until the process ends).
+ * The call allocates nothing: no hipMalloc, no hipFree, no allocating
+ * library routine.  Its first call on a device looks up that device's copy
+ * of the array (hipGetSymbolAddress).
+ * Errors: those of bi_decode_attn except BI_ERR_WORKSPACE, and
+ * BI_ERR_SCRATCH when bi_decode_attn_workspace_bytes(B, H, S, D) exceeds
+ * BI_DECODE_SCRATCH_BYTES, i.e. B * H * ceil(S / 2048) above 127100 chunks
+ * at D = 64 or 64527 at D = 128 (B = 256, H = 32, S = 8192 is 32768).
+ * Calls on one GPU share its array: two calls whose kernels overlap on that
+ * GPU (different streams, or different host threads without ordering) race
+ * and may return wrong results; calls ordered on one stream are safe.
+ */
+#define BI_DECODE_SCRATCH_BYTES (32u << 20)
+int bi_decode_attn_noalloc(int64_t B, int64_t H, int64_t S, int64_t D,
+                           const void* q, const void* k, const void* v, void* out,
+                           float scale, int in_dtype, int out_dtype, void* stream);
 
 /* The fixed KV chunk length of bi_decode_attn (2048, the handbook's decode split). */
 int bi_decode_chunk_tokens(void);

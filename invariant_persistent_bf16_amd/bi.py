@@ -28,6 +28,7 @@ _SIGS = {
                   [_vp, _vp, _sz, _int, _int, _vp]),
     "bi_decode_attn_workspace_bytes": (_sz, [_i64] * 4),
     "bi_decode_attn": (_int, [_i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _f32, _vp, _sz, _int, _int, _vp]),
+    "bi_decode_attn_noalloc": (_int, [_i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _f32, _int, _int, _vp]),
     "bi_decode_chunk_tokens": (_int, []),
     "bi_decode_attn_paged_workspace_bytes": (_sz, [_i64] * 4),
     "bi_decode_attn_paged": (_int, [_i64, _i64, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp,
@@ -211,6 +212,16 @@ def bi_decode_attn(q, k, v, scale, out=None, out_dtype=BI_F32, workspace=None, s
                                                   workspace.numel() * workspace.element_size(),
                                                   _dt(q), _dt(o), _stream(stream)))
     return o
+
+
+def bi_decode_attn_noalloc(q, k, v, scale, out, stream=None):
+    """bi_decode_attn with the chunk triples in the library's static scratch
+    (the call allocates nothing; out [B, H, D] fp32 or bf16 is the caller's)."""
+    B, H, S, D = k.shape
+    _check("bi_decode_attn_noalloc", lib().bi_decode_attn_noalloc(B, H, S, D, _p(q), _p(k), _p(v), _p(out),
+                                                                  float(scale), _dt(q), _dt(out),
+                                                                  _stream(stream)))
+    return out
 
 
 def bi_decode_attn_paged_workspace_bytes(B, H, max_seq_len, D):

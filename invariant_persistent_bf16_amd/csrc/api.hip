@@ -418,6 +418,7 @@ const char* bi_status_string(int status) {
         case BI_ERR_WORKSPACE: return "BI_ERR_WORKSPACE: workspace NULL, too small or misaligned";
         case BI_ERR_LAUNCH: return "BI_ERR_LAUNCH: the HIP runtime refused a launch";
         case BI_ERR_DEVICE: return "BI_ERR_DEVICE: no usable gfx950 device is current";
+        case BI_ERR_SCRATCH: return "BI_ERR_SCRATCH: the call needs more than the library's static scratch";
         default: return "unknown bi_status";
     }
 }
@@ -539,25 +540,34 @@ size_t bi_decode_attn_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t D
     return (size_t)(B * H * cdiv(S, DEC_CHUNK) * (2 + D) * 4);
 }
 
-int bi_decode_attn(int64_t B, int64_t H, int64_t S, int64_t D, const void* q, const void* k,
-                   const void* v, void* out, float scale, void* ws, size_t ws_bytes,
-                   int in_dtype, int out_dtype, void* stream) {
+}  // extern "C"
+
+namespace bi {
+
+// Checks of bi_decode_attn's arguments other than the workspace (1: nothing
+// to compute).
+static int decode_check(int64_t B, int64_t H, int64_t S, int64_t D, const void* q, const void* k,
+                        const void* v, void* out, int in_dtype, int out_dtype) {
     if (in_dtype != BI_BF16) return BI_ERR_DTYPE;
     if (out_dtype != BI_F32 && out_dtype != BI_BF16) return BI_ERR_DTYPE;
     if (B < 0 || H < 0 || S < 1) return BI_ERR_SHAPE;
     if (D != 64 && D != 128) return BI_ERR_UNSUPPORTED;
-    if (B == 0 || H == 0) return BI_OK;
+    if (B == 0 || H == 0) return 1;
     if (!q || !k || !v || !out) return BI_ERR_NULL;
-    if (!ws) return BI_ERR_WORKSPACE;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
         !aligned(out, out_dtype == BI_BF16 ? 2 : 4))
         return BI_ERR_LAYOUT;
-    const int64_t nchunk = cdiv(S, DEC_CHUNK);
-    if (ws_bytes < bi_decode_attn_workspace_bytes(B, H, S, D) || !aligned(ws, 16))
-        return BI_ERR_WORKSPACE;
-    if (B * H * nchunk > (1ll << 31) - 1 || B * H * D > (1ll << 40)) return BI_ERR_UNSUPPORTED;
+    if (B * H * cdiv(S, DEC_CHUNK) > (1ll << 31) - 1 || B * H * D > (1ll << 40)) return BI_ERR_UNSUPPORTED;
     // Per-(b, h) K and V byte offsets (up to one chunk past S) are 32-bit.
     if ((S + DEC_CHUNK) * D * 2 >= (1ll << 31)) return BI_ERR_UNSUPPORTED;
+    return BI_OK;
+}
+
+// The chunk and merge launches of an already checked decode, with the chunk
+// triples in wsf.
+static int decode_launch(int64_t B, int64_t H, int64_t S, int64_t D, const void* q, const void* k,
+                         const void* v, void* out, float scale, float* wsf, int out_dtype, void* stream) {
+    const int64_t nchunk = cdiv(S, DEC_CHUNK);
     int cus = 0;
     int rc = device_cu_count(&cus);
     if (rc != BI_OK) return rc;
@@ -565,7 +575,6 @@ int bi_decode_attn(int64_t B, int64_t H, int64_t S, int64_t D, const void* q, co
     const int64_t BH = B * H;
     const dim3 g1((unsigned)(BH * nchunk));
     const dim3 g2((unsigned)cdiv(BH * D, 256));
-    float* wsf = (float*)ws;
     const int sn = (int)nchunk;
     if (D == 64) {
         hipLaunchKernelGGL((decode_chunk_kernel<64>), g1, dim3(DEC_THREADS), 0, st,
@@ -579,6 +588,57 @@ int bi_decode_attn(int64_t B, int64_t H, int64_t S, int64_t D, const void* q, co
         else                      hipLaunchKernelGGL((decode_merge_kernel<128, 0>), g2, dim3(256), 0, st, wsf, out, BH, sn, nullptr, 1, 0);
     }
     return launch_status();
+}
+
+// Device memory of bi_decode_attn_noalloc's chunk triples: one copy per GPU,
+// allocated when the code object is loaded and held until the process ends.
+// Host code never passes this name to a kernel (on the host it is only a
+// handle): the device address comes from hipGetSymbolAddress, once per
+// device, on that device's first call.
+static __device__ __align__(256) float scratch[BI_DECODE_SCRATCH_BYTES / 4];
+static std::atomic<float*> g_scratch_ptr[64];
+
+static int scratch_ptr(float** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return BI_ERR_DEVICE;
+    float* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        void* a = nullptr;
+        if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || !a) return BI_ERR_DEVICE;
+        p = (float*)a;
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return BI_OK;
+}
+
+}  // namespace bi
+
+extern "C" {
+
+int bi_decode_attn(int64_t B, int64_t H, int64_t S, int64_t D, const void* q, const void* k,
+                   const void* v, void* out, float scale, void* ws, size_t ws_bytes,
+                   int in_dtype, int out_dtype, void* stream) {
+    int rc = decode_check(B, H, S, D, q, k, v, out, in_dtype, out_dtype);
+    if (rc != BI_OK) return rc == 1 ? BI_OK : rc;
+    if (!ws) return BI_ERR_WORKSPACE;
+    if (ws_bytes < bi_decode_attn_workspace_bytes(B, H, S, D) || !aligned(ws, 16))
+        return BI_ERR_WORKSPACE;
+    return decode_launch(B, H, S, D, q, k, v, out, scale, (float*)ws, out_dtype, stream);
+}
+
+int bi_decode_attn_noalloc(int64_t B, int64_t H, int64_t S, int64_t D, const void* q, const void* k,
+                           const void* v, void* out, float scale, int in_dtype, int out_dtype,
+                           void* stream) {
+    int rc = decode_check(B, H, S, D, q, k, v, out, in_dtype, out_dtype);
+    if (rc != BI_OK) return rc == 1 ? BI_OK : rc;
+    if (bi_decode_attn_workspace_bytes(B, H, S, D) > (size_t)BI_DECODE_SCRATCH_BYTES) return BI_ERR_SCRATCH;
+    float* wsf = nullptr;
+    rc = scratch_ptr(&wsf);
+    if (rc != BI_OK) return rc;
+    // Every chunk writes its triple before the merge reads it: nothing in the
+    // scratch needs clearing between calls.
+    return decode_launch(B, H, S, D, q, k, v, out, scale, wsf, out_dtype, stream);
 }
 
 size_t bi_decode_attn_paged_workspace_bytes(int64_t B, int64_t H, int64_t max_seq_len, int64_t D) {
