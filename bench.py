@@ -45,9 +45,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="target host time of the oracle CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=2.0,
+                    help="target host time of each leg (workload x thread count) of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default="",
+                    help="comma-separated subset of the step's operations (addmm, conv2d, attention, decode, "
+                         "mm_fp32) to run, with no untimed extras and no CPU baseline: for profiler runs")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "gemm_bf16_addmm_M8192_traffic.txt"),
                     help="HBM-side bytes per GEMM launch measured with rocprofv3 counters")
     return ap.parse_args()
@@ -70,6 +73,14 @@ def main():
     bi.lib()
     print(f"# device: {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
 
+    known = ("addmm", "conv2d", "attention", "decode", "mm_fp32")
+    only = [n for n in args.only.split(",") if n]
+    for n in only:
+        if n not in known:
+            print(f"--only: unknown operation {n}; choose from {', '.join(known)}", file=sys.stderr)
+            sys.exit(2)
+    want = lambda n: not only or n in only
+
     # ------------------------------------------------ inputs (resident in HBM)
     W, bias, x0 = synth.addmm_shared()
     Wd, bd = W.to(dev), bias.to(dev)
@@ -84,17 +95,21 @@ def main():
                       device=dev)
 
     G = ATT["B"] * ATT["H"]
-    Q, Kt, V = synth.attn_batch(synth.attn_shared(), ATT["B"], device=dev)
-    Sb = torch.empty(G, ATT["T"], ATT["T"], dtype=torch.float32, device=dev)
-    Pb = torch.empty(G, ATT["T"], ATT["T"], dtype=torch.bfloat16, device=dev)
-    Ob = torch.empty(G, ATT["T"], ATT["D"], dtype=torch.float32, device=dev)
     att_scale = float(torch.tensor(1 / math.sqrt(ATT["D"]), dtype=torch.float32))
+    Q = Kt = V = Sb = Pb = Ob = None
+    if want("attention"):
+        Q, Kt, V = synth.attn_batch(synth.attn_shared(), ATT["B"], device=dev)
+        Sb = torch.empty(G, ATT["T"], ATT["T"], dtype=torch.float32, device=dev)
+        Pb = torch.empty(G, ATT["T"], ATT["T"], dtype=torch.bfloat16, device=dev)
+        Ob = torch.empty(G, ATT["T"], ATT["D"], dtype=torch.float32, device=dev)
 
-    dq0 = synth.decode_shared()
-    dq, dk, dv = synth.decode_batch(dq0, DEC["B"], device=dev)
-    dout = torch.empty(DEC["B"], DEC["H"], DEC["D"], dtype=torch.float32, device=dev)
-    dws = torch.empty(bi.bi_decode_attn_workspace_bytes(DEC["B"], DEC["H"], DEC["S"], DEC["D"]) // 4,
-                      dtype=torch.float32, device=dev)
+    dq = dk = dv = dout = dws = None
+    if want("decode"):
+        dq0 = synth.decode_shared()
+        dq, dk, dv = synth.decode_batch(dq0, DEC["B"], device=dev)
+        dout = torch.empty(DEC["B"], DEC["H"], DEC["D"], dtype=torch.float32, device=dev)
+        dws = torch.empty(bi.bi_decode_attn_workspace_bytes(DEC["B"], DEC["H"], DEC["S"], DEC["D"]) // 4,
+                          dtype=torch.float32, device=dev)
 
     mW, mX = synth.mm_inputs(Ms=(MM32["M"],))
     mWd, mXd = mW.to(dev), mX[MM32["M"]].to(dev)
@@ -118,7 +133,7 @@ def main():
         "decode": lambda: bi.bi_decode_attn(dq, dk, dv, 0.125, out=dout, workspace=dws),
         "mm_fp32": lambda: bi.bi_mm(mXd, mWd, out=mY),
     }
-    names = list(ops)
+    names = only or list(ops)
 
     def step(events=None):
         for i, n in enumerate(names):
@@ -165,10 +180,21 @@ def main():
         t = ms[n] * 1e-3
         detail[n] = {"ms": round(ms[n], 5), "TFLOP/s": round(flops[n] / t / 1e12, 2),
                      "GB/s": round(bytes_[n] / t / 1e9, 1)}
-    detail["addmm"]["frac_bf16_peak"] = round(flops["addmm"] / (ms["addmm"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
-    detail["decode"]["frac_hbm_peak"] = round(bytes_["decode"] / (ms["decode"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
-    detail["mm_fp32"]["frac_fp32_mfma_peak"] = round(
-        flops["mm_fp32"] / (ms["mm_fp32"] * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4)
+    if "addmm" in ms:
+        detail["addmm"]["frac_bf16_peak"] = round(flops["addmm"] / (ms["addmm"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+    if "decode" in ms:
+        detail["decode"]["frac_hbm_peak"] = round(bytes_["decode"] / (ms["decode"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+    if "mm_fp32" in ms:
+        detail["mm_fp32"]["frac_fp32_mfma_peak"] = round(
+            flops["mm_fp32"] / (ms["mm_fp32"] * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4)
+    if only:
+        # profiler runs: the timings of the selected operations only
+        tf = flops["addmm"] / (ms["addmm"] * 1e-3) / 1e12 if "addmm" in ms else None
+        print(json.dumps({"metric": "batch-invariant GEMM TFLOP/s & % bf16 MFMA peak; decode-attn GB/s; "
+                                    "bitwise match", "value": None if tf is None else round(tf, 2),
+                          "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                          "only": only, "ops": detail}), flush=True)
+        return
 
     # ------------------------------------------- bitwise invariance (untimed)
     y1 = bi.bi_addmm(bd, X[:1], Wd)
@@ -177,6 +203,8 @@ def main():
     torch.cuda.synchronize()
     bit_gemm = torch.equal(y1[0].view(torch.int16), Y[0].view(torch.int16))
     bit_dec = torch.equal(o1[0].view(torch.int32), dout[0].view(torch.int32))
+    invariance_records = {"addmm_row0_M1_vs_M8192": comparison_record(Y[:1], y1),
+                          "decode_req0_B1_vs_B256": comparison_record(dout[:1], o1)}
 
     tflops = flops["addmm"] / (ms["addmm"] * 1e-3) / 1e12
     dec_gbs = bytes_["decode"] / (ms["decode"] * 1e-3) / 1e9
@@ -206,6 +234,7 @@ def main():
         "decode_attn_GBps": round(dec_gbs, 1),
         "bitwise_match": {"addmm_row0_M1_vs_M8192": bool(bit_gemm),
                           "decode_req0_B1_vs_B256": bool(bit_dec)},
+        "comparison": {"invariance": invariance_records},
         "ops": detail,
     }
 
@@ -216,11 +245,34 @@ def main():
     out["prefill"] = prefill()
     out["f16_addmm"] = f16_addmm(W, bias, X, Y)
 
+    if not args.no_cpu_baseline:
+        cpu, parity = cpu_baseline(args.cpu_seconds, dict(W=W, bias=bias, x0=x0, Wd=Wd, bd=bd, X=X),
+                                   dict(cw=cw, cb=cb, cx=cx, cy_dev=None, cwd=cwd, cbd=cbd),
+                                   dict(Q=Q, K=Kt, V=V, O=Ob, scale=att_scale),
+                                   dict(q=dq, k=dk, v=dv, out=dout), dict(W=mW, X=mX[MM32["M"]], Y=mY))
+        out["cpu_baseline"] = cpu
+        out["comparison"]["oracle_parity_sample"] = parity
     del X, Y, Q, Kt, V, Sb, Pb, Ob, dq, dk, dv
     torch.cuda.empty_cache()
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(W, bias, x0, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def comparison_record(got, ref):
+    """The comparison figures of the VLA page's tracer ("Batch-Invariant
+    VLAs", section "Profiling batch-invariance") between two device tensors
+    whose first axis is the sample: max_abs_diff, mean_abs_diff, rmse,
+    relative_l2_mean / _max (per sample, then mean and max over samples),
+    output_abs_max (of got)."""
+    import torch
+    g = got.double().reshape(got.shape[0], -1)
+    r = ref.double().reshape(ref.shape[0], -1).to(g.device)
+    d = g - r
+    nr = r.norm(dim=1)
+    rel = d.norm(dim=1) / torch.where(nr > 0, nr, torch.ones_like(nr))
+    return {"samples": int(g.shape[0]), "max_abs_diff": float(d.abs().max()),
+            "mean_abs_diff": float(d.abs().mean()), "rmse": float(d.pow(2).mean().sqrt()),
+            "relative_l2_mean": float(rel.mean()), "relative_l2_max": float(rel.max()),
+            "output_abs_max": float(g.abs().max())}
 
 
 def _time_ms(fn, iters=20):
@@ -475,19 +527,34 @@ def paged_decode(dq, dk, dv, dout):
 
 def f16_addmm(W, bias, X, Y):
     """Untimed extra: the fp16 configuration of the same addmm (M=8192, K=4096,
-    N=14336, fp16 operands and output; the workload's values converted to fp16)."""
+    N=14336, fp16 operands and output; the workload's values converted to
+    fp16), timed in alternating blocks of 20 calls with the bf16 addmm on the
+    same shape, after a warm-up of both, so that the two see the same clock
+    and power state; the best block of each is reported."""
     import torch
 
     from invariant_persistent_bf16_amd import bi
 
     dev = X.device
     Wh, bh, Xh = W.to(dev, torch.float16), bias.to(dev, torch.float16), X.to(torch.float16)
+    Wb, bb = W.to(dev), bias.to(dev)
     Yh = torch.empty(Y.shape, dtype=torch.float16, device=dev)
-    t = _time_ms(lambda: bi.bi_addmm(bh, Xh, Wh, out=Yh, out_dtype=bi.BI_F16), iters=20)
+    f16 = lambda: bi.bi_addmm(bh, Xh, Wh, out=Yh, out_dtype=bi.BI_F16)
+    b16 = lambda: bi.bi_addmm(bb, X, Wb, out=Y)
+    for _ in range(10):
+        f16()
+        b16()
+    t16, tb = float("inf"), float("inf")
+    for _ in range(4):
+        t16 = min(t16, _time_ms(f16, iters=20))
+        tb = min(tb, _time_ms(b16, iters=20))
     M, K, N = ADDMM["M"], ADDMM["K"], ADDMM["N"]
-    tf = 2 * M * N * K / (t * 1e-3) / 1e12
+    fl = 2 * M * N * K
     del Wh, Xh, Yh
-    return {"ms": round(t, 4), "TFLOP/s": round(tf, 1), "frac_f16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    return {"ms": round(t16, 4), "TFLOP/s": round(fl / (t16 * 1e-3) / 1e12, 1),
+            "frac_f16_peak": round(fl / (t16 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "bf16_same_blocks_ms": round(tb, 4),
+            "bf16_same_blocks_frac_peak": round(fl / (tb * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
 def prefill():
@@ -540,26 +607,103 @@ def gemm_code_hash():
     return h.hexdigest()
 
 
-def cpu_baseline(W, bias, x0, target_s):
-    """The fp64 oracle on a row sample of the addmm workload, on the host cores."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _time_units(fn, units, target_s, first=1):
+    """Run fn(list of unit indices) on growing batches of units until about
+    target_s seconds of host time; returns (units done, seconds, outputs)."""
+    done, t, n, outs = 0, 0.0, first, []
+    while done < len(units) and (t < target_s or done == 0):
+        sel = units[done:done + n]
+        t0 = time.perf_counter()
+        outs.append((sel, fn(sel)))
+        t += time.perf_counter() - t0
+        done += len(sel)
+        if t < target_s:
+            per = t / done
+            n = max(1, min(len(units) - done, int((target_s - t) / per * 0.6)))
+    return done, t, outs
+
+
+def cpu_baseline(target_s, addmm, conv, att, dec, mm32):
+    """The fp64 oracle (test infrastructure, as it stands) timed on the host,
+    per workload, at one thread and at all of the host's threads, each on a
+    bounded sample of about target_s seconds: rows of the addmm, images of the
+    convolution, slices of the attention, requests of the decode, and the
+    whole binary32 mm.  Each leg reports its units, the seconds, the oracle's
+    rate in the workload's unit, and a labelled linear extrapolation of the
+    host time to the full workload.  Also returns the comparison record of the
+    GPU's outputs on the all-core addmm sample and decode sample against the
+    oracle (GPU rows recomputed alone: by row invariance the same bits)."""
+    import numpy as np
     import torch
 
     import oracle
-    import synth
+    from invariant_persistent_bf16_amd import bi
 
-    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
-    Xs = synth.addmm_batch(x0, 8192, device="cpu")
-    rows, t, r = 0, 0.0, 16
-    while t < target_s and rows + r <= Xs.shape[0]:
-        sel = list(range(rows, rows + r))
-        t0 = time.perf_counter()
-        oracle.mm(Xs, W, bias, rows=sel)
-        t += time.perf_counter() - t0
-        rows += r
-        r = min(max(r, int(r * max(1.0, (target_s - t) / max(t, 1e-3) * 0.5))), 512)
-    flops = 2.0 * rows * ADDMM["K"] * ADDMM["N"]
-    return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{rows} rows of the addmm workload (K=4096, N=14336, fp64 loops), {t:.1f} s"}
+    dev = addmm["Wd"].device
+    all_threads = oracle.set_threads()
+    res = {"cpu_model": _cpu_model(), "host_threads": all_threads, "legs": {}}
+    g = torch.Generator().manual_seed(4242)
+
+    def order(n):
+        return [0] + (torch.randperm(n - 1, generator=g) + 1).tolist()
+
+    M, K, N = ADDMM["M"], ADDMM["K"], ADDMM["N"]
+    Xh = addmm["X"].cpu()
+    G = ATT["B"] * ATT["H"]
+    T, Dh = ATT["T"], ATT["D"]
+    legs = {
+        "addmm": (order(M), M, 2.0 * K * N, "row",
+                  lambda sel: oracle.mm(Xh[sel], addmm["W"], addmm["bias"])),
+        "conv2d": (order(CONV_B), CONV_B, 2.0 * 1152 * 256 * 588, "image",
+                   lambda sel: oracle.conv2d_direct(conv["cx"][sel].cpu(), conv["cw"], conv["cb"], stride=(14, 14))),
+        "attention": (order(G), G, 4.0 * T * T * Dh, "slice",
+                      lambda sel: oracle.attention(att["Q"][sel].cpu(), att["K"][sel].cpu(), att["V"][sel].cpu(),
+                                                   att["scale"], p_bf16=True)),
+        "decode": (order(DEC["B"]), DEC["B"], 4.0 * DEC["H"] * DEC["S"] * DEC["D"], "request",
+                   lambda sel: oracle.decode(dec["q"][sel].cpu(), dec["k"][sel].cpu(), dec["v"][sel].cpu(), 0.125)),
+        "mm_fp32": ([0], 1, 2.0 * MM32["M"] * MM32["N"] * MM32["K"], "whole product",
+                    lambda sel: oracle.mm(mm32["X"], mm32["W"])),
+    }
+    parity = {}
+    try:
+        for name, (units, total, flop_per_unit, unit_name, fn) in legs.items():
+            res["legs"][name] = {}
+            for threads in (1, all_threads):
+                oracle.set_threads(threads)
+                done, t, outs = _time_units(fn, units, target_s)
+                rate = flop_per_unit * done / t
+                res["legs"][name][f"threads_{threads}"] = {
+                    "units": done, "unit": unit_name, "seconds": round(t, 3),
+                    "GFLOP/s": round(rate / 1e9, 3),
+                    "full_workload_seconds_extrapolated": round(t / done * total, 2)}
+                if threads == all_threads and name in ("addmm", "decode"):
+                    sel = [u for s_, _ in outs for u in s_]
+                    ref = np.concatenate([o for _, o in outs])
+                    if name == "addmm":
+                        got = bi.bi_addmm(addmm["bd"], addmm["X"][sel], addmm["Wd"], out_dtype=bi.BI_F32)
+                    else:
+                        got = bi.bi_decode_attn(dec["q"][sel], dec["k"][sel], dec["v"][sel], 0.125)
+                    torch.cuda.synchronize()
+                    parity[name] = comparison_record(got, torch.from_numpy(ref))
+                    parity[name]["units"] = sel[:8] + (["..."] if len(sel) > 8 else [])
+    finally:
+        oracle.set_threads(all_threads)
+    a = res["legs"]["addmm"][f"threads_{all_threads}"]
+    cpu = {"value": round(a["GFLOP/s"] / 1e3, 6), "unit": "TFLOP/s", "cores": all_threads, "kind": "oracle",
+           "sample": f"{a['units']} rows of the addmm workload (K=4096, N=14336, fp64 loops), {a['seconds']} s; "
+                     f"per-workload legs at 1 and {all_threads} threads below",
+           "cpu_model": res["cpu_model"], "per_workload": res["legs"]}
+    return cpu, parity
 
 
 if __name__ == "__main__":

@@ -70,6 +70,12 @@ def _out(shape):
     return o, o.ctypes.data_as(_dp)
 
 
+def set_threads(n=0):
+    """Threads of the oracle's parallel loops (n < 1: unchanged); returns the
+    count in force.  Timing only: no result depends on it."""
+    return int(_load().oracle_set_threads(ctypes.c_int(int(n))))
+
+
 def bf16_rne(x):
     """Nearest bfloat16 value of a double, ties to even (single rounding)."""
     return _load().oracle_bf16_rne(float(x))

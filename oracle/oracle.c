@@ -43,6 +43,7 @@
  * pages print.  No function here is "parity unpinned".
  */
 #include <math.h>
+#include <omp.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <string.h>
@@ -606,4 +607,12 @@ void sim_decode_splits_f32(int64_t S, int64_t D, const float* q, const float* Kc
 /* Element-wise oracle_bf16_rne over an array (tests round many values). */
 void oracle_bf16_rne_array(const double* x, double* out, int64_t n) {
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_bf16_rne(x[i]);
+}
+
+/* Thread count of the OpenMP loops over independent outputs, for timing the
+ * oracle on one core or on all of them; no result depends on it.  n < 1
+ * leaves it unchanged.  Returns the count now in force. */
+int oracle_set_threads(int n) {
+    if (n > 0) omp_set_num_threads(n);
+    return omp_get_max_threads();
 }

@@ -7,6 +7,9 @@ relative L2 error <= 1e-5 over the checked tensor and, for every output row
 element must equal RNE(x) for some x within that same per-row bound of the
 oracle value, i.e. lie between RNE(ref - band) and RNE(ref + band).
 """
+import json
+import os
+
 import numpy as np
 import torch
 
@@ -81,3 +84,30 @@ def assert_within_dot_bound(got, ref, mag, K, what=""):
     err = np.abs(np.asarray(got) - np.asarray(ref))
     bound = gamma * np.asarray(mag)
     assert np.all(err <= bound), f"{what}: error {err.max():.3e} exceeds gamma_K bound"
+
+
+def comparison_record(got, ref, what=""):
+    """The comparison figures of the VLA page's tracer ("Batch-Invariant
+    VLAs", section "Profiling batch-invariance"): max_abs_diff, mean_abs_diff,
+    rmse, relative_l2_mean / relative_l2_max (relative L2 per sample, the
+    first axis, then the mean and maximum over samples) and output_abs_max.
+    got, ref: arrays of the same shape, first axis = sample.  When the
+    environment names a file in BI_COMPARISON_RECORD the record is appended
+    to it as one JSON line."""
+    g = np.asarray(got, dtype=np.float64).reshape(len(got), -1)
+    r = np.asarray(ref, dtype=np.float64).reshape(len(ref), -1)
+    d = g - r
+    nr = np.linalg.norm(r, axis=1)
+    rel = np.linalg.norm(d, axis=1) / np.where(nr > 0, nr, 1.0)
+    rec = {"what": what, "samples": int(g.shape[0]),
+           "max_abs_diff": float(np.abs(d).max()) if d.size else 0.0,
+           "mean_abs_diff": float(np.abs(d).mean()) if d.size else 0.0,
+           "rmse": float(np.sqrt((d * d).mean())) if d.size else 0.0,
+           "relative_l2_mean": float(rel.mean()) if rel.size else 0.0,
+           "relative_l2_max": float(rel.max()) if rel.size else 0.0,
+           "output_abs_max": float(np.abs(g).max()) if g.size else 0.0}
+    path = os.environ.get("BI_COMPARISON_RECORD")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(rec) + "\n")
+    return rec

@@ -133,3 +133,18 @@ def test_bias_added_after_sum():
     bias = torch.tensor([2.0 ** 24], dtype=torch.float32)
     got = oracle.mm(A, B, bias)[0, 0]
     assert got == 2.0 ** 24 + 4 * 2.0 ** -30
+
+
+def test_thread_count_changes_no_result():
+    # the benchmark times the oracle on one core and on all of them
+    A = synth.randn((37, 300), seed=91, dtype=torch.bfloat16)
+    B = synth.randn((300, 50), seed=92, dtype=torch.bfloat16)
+    n = oracle.set_threads()
+    try:
+        oracle.set_threads(1)
+        one = oracle.mm(A, B)
+        oracle.set_threads(max(n, 4))
+        many = oracle.mm(A, B)
+    finally:
+        oracle.set_threads(n)
+    assert np.array_equal(one, many)
