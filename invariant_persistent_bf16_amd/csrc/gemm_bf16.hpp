@@ -10,7 +10,8 @@
 //     decides which wave computes which elements;
 //   * output element (i, j) is accumulated by a single chain of
 //     v_mfma_f32_32x32x16_bf16 instructions, one per 16-wide K slice, K
-//     ascending, starting from zero; its operands are row i of A and column j
+//     ascending, starting from +0.0 (the first MFMA's literal accumulator
+//     input; K = 0 runs one step of zeros); its operands are row i of A and column j
 //     of B only, so neither the other rows of the tile nor M, the slice count
 //     or the grid can change its bits;
 //   * rows past M, columns past N and K past K are loaded as zeros (or, for
@@ -84,7 +85,7 @@ struct G16Cfg {
     static constexpr int B_STAGE = BN * G16_BK * 2;             // B tile of one K step
     static constexpr int B_BASE = G16_NSTAGE * A_STAGE;         // B stages after the A stages
     static constexpr int RING = G16_NSTAGE * (A_STAGE + B_STAGE);
-    static constexpr int BIAS = (BM + BN) * 4;                  // row and column bias, binary32
+    static constexpr int BIAS = (4 * BM > BN ? 4 * BM : BN) * 4; // the tile's bias values, binary32 (single buffer)
     // Bias double buffered after the ring.  ONE_PER_CU: at least 81 KiB in
     // all, so that two of the kernel's workgroups never share a compute unit.
     // The grid is at most one workgroup per compute unit, and the dispatcher
@@ -92,7 +93,7 @@ struct G16Cfg {
     // one unit would run at half speed beside an idle one.  The arithmetic
     // does not depend on it (ONE_PER_CU = false, a test-only variant, runs
     // two workgroups per unit and gives the same bits).
-    static constexpr int LDS = (ONE_PER_CU && RING + 2 * BIAS < 81 * 1024) ? 81 * 1024 : RING + 2 * BIAS;
+    static constexpr int LDS = (ONE_PER_CU && RING + BIAS < 81 * 1024) ? 81 * 1024 : RING + BIAS;
     static constexpr int NA = BM / 64;                          // A copies per wave and step
     static constexpr int NB = BN / 64;                          // B copies per wave and step
     static constexpr int NDMA = NA + NB;
@@ -207,43 +208,52 @@ gemm_bf16_persistent(GemmParams p) {
     // Wave index as a scalar so that LDS destinations are wave-uniform.
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-    const int nk = (int)((p.K + G16_BK - 1) / G16_BK);
+    // At least one K step: with K = 0 it loads only zeros (every copy is
+    // out of range) and its MFMAs give the +0.0 sums of an empty product.
+    const int nk = max(1, (int)((p.K + G16_BK - 1) / G16_BK));
     const int K32 = (int)p.K;   // the host bounds K below 2^30
 
     const int grid = gridDim.x;
     const int w = blockIdx.x;
     const int wr = (grid % 8 == 0) ? (w % 8) * (grid / 8) + (w / 8) : w;
 
-    // ---- per-lane LDS fragment addresses (stage 0; stages add 16 KiB each)
-    //  A row r = R0 + 32 im, R0 = 128 wm + lane%32: f(r) = f(R0), so chunk
-    //  (2kk + lane/32) ^ f(r) = x ^ 2kk with x = lane/32 ^ f(R0).
-    //  N-contiguous B: K row kk*16 + 8(g/2) + 4hr + z (z = li/4, k&3 = z),
-    //  chunk (16wn + 4in + y) ^ 4z = 16wn + 4(in ^ z) + y.
-    const uint32_t lds0 = g16_lds_addr(smem);
-    uint32_t a_fb[2], b_fb[4];
-    {
-        const int R0 = wm * C::WROWS + (lane & 31);
-        const int x = (lane >> 5) ^ ((R0 >> 2) & 3);
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) a_fb[kk] = lds0 + R0 * 64 + ((x ^ (2 * kk)) << 4);
-        if constexpr (B_KCONTIG) {
-            const int N0 = wn * C::WCOLS + (lane & 31);
-            const int xb = (lane >> 5) ^ ((N0 >> 2) & 3);
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) b_fb[kk] = lds0 + C::B_BASE + N0 * 64 + ((xb ^ (2 * kk)) << 4);
-            b_fb[2] = b_fb[3] = 0;
-        } else {
-            const int g = lane >> 4, li = lane & 15, z = li >> 2;
-            const int y = 2 * (g & 1) + ((li & 3) >> 1);
-#pragma unroll
-            for (int in = 0; in < IN; ++in)
-                b_fb[in] = lds0 + C::B_BASE + (8 * (g >> 1) + z) * C::RB +
-                           ((((IN * wn + in) ^ z) << 2) + y) * 16 + (li & 1) * 8;
-        }
-    }
-
-    int ti = 0;   // tiles done by this workgroup (bias staging buffer parity)
+    int ti = 0;   // tiles done by this workgroup
     for (int tile = wr; tile < p.total_tiles; tile += grid, ++ti) {
+        // An opaque copy of the lane id, so that the per-lane addresses and
+        // offsets below are recomputed each tile (a few VALU instructions)
+        // instead of being kept live across the epilogue, where the compiler
+        // would spill them and reload them before the next tile's copies.
+        int lane_t = lane;
+        asm volatile("" : "+v"(lane_t));
+        const int tid_t = wave * 64 + lane_t;
+        // ---- per-lane LDS fragment addresses (stage 0; stages add 16 KiB each)
+        //  A row r = R0 + 32 im, R0 = 128 wm + lane%32: f(r) = f(R0), so chunk
+        //  (2kk + lane/32) ^ f(r) = x ^ 2kk with x = lane/32 ^ f(R0).
+        //  N-contiguous B: K row kk*16 + 8(g/2) + 4hr + z (z = li/4, k&3 = z),
+        //  chunk (16wn + 4in + y) ^ 4z = 16wn + 4(in ^ z) + y.
+        const uint32_t lds0 = g16_lds_addr(smem);
+        uint32_t a_fb[2], b_fb[4];
+        {
+            const int R0 = wm * C::WROWS + (lane_t & 31);
+            const int x = (lane_t >> 5) ^ ((R0 >> 2) & 3);
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) a_fb[kk] = lds0 + R0 * 64 + ((x ^ (2 * kk)) << 4);
+            if constexpr (B_KCONTIG) {
+                const int N0 = wn * C::WCOLS + (lane_t & 31);
+                const int xb = (lane_t >> 5) ^ ((N0 >> 2) & 3);
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) b_fb[kk] = lds0 + C::B_BASE + N0 * 64 + ((xb ^ (2 * kk)) << 4);
+                b_fb[2] = b_fb[3] = 0;
+            } else {
+                const int g = lane_t >> 4, li = lane_t & 15, z = li >> 2;
+                const int y = 2 * (g & 1) + ((li & 3) >> 1);
+#pragma unroll
+                for (int in = 0; in < IN; ++in)
+                    b_fb[in] = lds0 + C::B_BASE + (8 * (g >> 1) + z) * C::RB +
+                               ((((IN * wn + in) ^ z) << 2) + y) * 16 + (li & 1) * 8;
+            }
+        }
+
         // ---- tile coordinates (scheduling only; no effect on arithmetic)
         const int s = tile / p.tiles_per_slice;
         const int t = tile - s * p.tiles_per_slice;
@@ -269,9 +279,9 @@ gemm_bf16_persistent(GemmParams p) {
         // N-contiguous B: copy j covers K rows 8w + 2j + lane/32; the lane writes
         // physical chunk lane&31 of that row, i.e. logical chunk
         // (lane&31) ^ 4(krow&3), columns clamped to the last valid 8.
-        const int a_u = (lane & 3) ^ ((lane >> 4) & 3);
-        const int a_row0 = (BM / 4) * wave + (lane >> 2);
-        const int b_row0 = (BN / 4) * wave + (lane >> 2);
+        const int a_u = (lane_t & 3) ^ ((lane_t >> 4) & 3);
+        const int a_row0 = (BM / 4) * wave + (lane_t >> 2);
+        const int b_row0 = (BN / 4) * wave + (lane_t >> 2);
         uint32_t a_off[C::NA], b_off[C::NB];
         {
             const int64_t a_rows_left = p.M - m0 - a_row0;
@@ -287,14 +297,14 @@ gemm_bf16_persistent(GemmParams p) {
                 const int ncl = (int)min<int64_t>(p.N - 8 - n0, BN - 8);
 #pragma unroll
                 for (int j = 0; j < C::NB; ++j) {
-                    const int krow = 8 * wave + (1024 / C::RB) * j + lane / C::LPR;
-                    const int col = min(((lane % C::LPR) ^ (4 * (krow & 3))) << 3, ncl);
+                    const int krow = 8 * wave + (1024 / C::RB) * j + lane_t / C::LPR;
+                    const int col = min(((lane_t % C::LPR) ^ (4 * (krow & 3))) << 3, ncl);
                     b_off[j] = (uint32_t)((krow * (int)p.sBk + col) * 2);
                 }
             }
         }
         const int a_u8 = a_u * 8;
-        const int bn_krow0 = 8 * wave + lane / C::LPR;
+        const int bn_krow0 = 8 * wave + lane_t / C::LPR;
         const __amdgpu_buffer_rsrc_t rsA = g16_rsrc(Ab), rsB = g16_rsrc(Bb);
         const uint32_t kstepB = B_KCONTIG ? 2u * G16_BK : (uint32_t)(2 * G16_BK * p.sBk);
 
@@ -351,31 +361,27 @@ gemm_bf16_persistent(GemmParams p) {
                 asm volatile("" : "+v"(F.b[0][0]), "+v"(F.b[0][1]), "+v"(F.b[1][0]), "+v"(F.b[1][1]));
         };
 
-        // Bias of the tile, staged in LDS as binary32 after the prologue's wait
-        // (the load is older than the copies that wait covers): a row part
-        // [256] and a column part [256].  The part not in use holds -0.0,
-        // which added to any binary32 value x gives x exactly (-0 and NaN
-        // included), so the epilogue adds both parts without branching and
-        // each output still gets exactly one bias addition.  Entries past N
-        // (or M) repeat the last valid one and are never stored.
-        const uint16_t* bb = p.bias ? p.bias + s2 * p.sBias2 : nullptr;
-        float* bias_lds = (float*)(smem + C::RING + (ti & 1) * C::BIAS);
-        float brow_t = -0.0f, bcol_t = -0.0f;
-        if (bb) {
+        // Bias of the tile (by row for bias_rows, else by column): one
+        // element per thread, loaded before the operand copies and written
+        // to LDS only after the K loop's final wait (so no wait is spent on
+        // it), in binary32: one value per column (column bias), each row's
+        // value four times (row bias, so that the epilogue reads four bias
+        // values per output group either way), or -0.0 without bias (x + -0.0
+        // is x exactly).  Entries past M (or N) repeat the last valid one and
+        // are never stored.  One buffer: the next tile writes it only after
+        // its own K loop, whose barriers every wave passes after its epilogue.
+        float* bias_lds = (float*)(smem + C::RING);
+        uint32_t braw = 0;
+        if (p.bias) {
             const int64_t b0 = p.bias_rows ? m0 : n0;
-            const int64_t nb = (p.bias_rows ? p.M : p.N) - b0;
-            const float b = h16_to_f32<F16>(bb[b0 + min<int64_t>(tid, nb - 1)]);
-            if (p.bias_rows) brow_t = b;
-            else             bcol_t = b;
+            const int nb = (int)min<int64_t>((p.bias_rows ? p.M : p.N) - b0, 256);
+            braw = p.bias[s2 * p.sBias2 + b0 + min(tid_t, nb - 1)];
         }
 
+        // Accumulators: the first K step's first MFMA of each block starts
+        // from a literal +0.0 (no separate zeroing pass, no zero values kept
+        // live across the tile loop).
         f32x16_t acc[IM][IN];
-#pragma unroll
-        for (int im = 0; im < IM; ++im)
-#pragma unroll
-            for (int in = 0; in < IN; ++in)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[im][in][r] = 0.0f;
 
         G16Frags F0, F1;
         constexpr int NREAD = 2 * IM + (B_KCONTIG ? 2 : 4) * IN;
@@ -387,8 +393,9 @@ gemm_bf16_persistent(GemmParams p) {
         // kt+4 into stage ST (its data now lives in registers).  Copies and reads past
         // the last step are harmless (zeros into an unused stage, reads of an
         // unused stage) and keep the step a single straight-line block.
-        auto step = [&](int kt, auto stc) {
+        auto step = [&](int kt, auto stc, auto firstc) {
             constexpr int ST = decltype(stc)::value;
+            constexpr bool FIRST = decltype(firstc)::value;
             G16Frags& cur = (ST & 1) ? F1 : F0;
             G16Frags& nxt = (ST & 1) ? F0 : F1;
             g16_wait_vm_lgkm0<2 * C::NDMA>();
@@ -398,12 +405,14 @@ gemm_bf16_persistent(GemmParams p) {
             g16_static_for<0, C::NMF>([&](auto ic) {
                 constexpr int i = decltype(ic)::value;
                 constexpr int kk = i / (IM * IN), im = (i / IN) % IM, in = i % IN;
+                const f32x16_t zero = {};
+                const f32x16_t& c_in = (FIRST && kk == 0) ? zero : acc[im][in];
                 if constexpr (F16)
                     acc[im][in] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                        as_f16x8(cur.b[kk][in]), as_f16x8(cur.a[kk][im]), acc[im][in], 0, 0, 0);
+                        as_f16x8(cur.b[kk][in]), as_f16x8(cur.a[kk][im]), c_in, 0, 0, 0);
                 else
                     acc[im][in] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        as_bf16x8(cur.b[kk][in]), as_bf16x8(cur.a[kk][im]), acc[im][in], 0, 0, 0);
+                        as_bf16x8(cur.b[kk][in]), as_bf16x8(cur.a[kk][im]), c_in, 0, 0, 0);
                 if constexpr (BM == 256 && BN == 256) {
                     constexpr int slot = g16_slot<B_KCONTIG>(i);
                     if constexpr (slot >= 0 && slot < 32) {
@@ -434,16 +443,16 @@ gemm_bf16_persistent(GemmParams p) {
             g16_static_for<0, C::NDMA>([&](auto jc) { dma(decltype(sc)::value, decltype(sc)::value, jc); });
         });
         g16_wait_vm_lgkm0<3 * C::NDMA>();
-        if (tid < BM) bias_lds[tid] = brow_t;
-        if (tid < BN) bias_lds[BM + tid] = bcol_t;
         __builtin_amdgcn_s_barrier();
         g16_static_for<0, NREAD>([&](auto rc) { lds_read(F0, std::integral_constant<int, 0>{}, rc); });
 
-        for (int kt = 0; kt < nk; kt += 4) {
-            step(kt, std::integral_constant<int, 0>{});
-            if (kt + 1 < nk) step(kt + 1, std::integral_constant<int, 1>{});
-            if (kt + 2 < nk) step(kt + 2, std::integral_constant<int, 2>{});
-            if (kt + 3 < nk) step(kt + 3, std::integral_constant<int, 3>{});
+        using NF = std::false_type;
+        step(0, std::integral_constant<int, 0>{}, std::true_type{});
+        for (int kt = 1; kt < nk; kt += 4) {
+            step(kt, std::integral_constant<int, 1>{}, NF{});
+            if (kt + 1 < nk) step(kt + 1, std::integral_constant<int, 2>{}, NF{});
+            if (kt + 2 < nk) step(kt + 2, std::integral_constant<int, 3>{}, NF{});
+            if (kt + 3 < nk) step(kt + 3, std::integral_constant<int, 0>{}, NF{});
         }
         // Drain every copy (including the ones past the last step) and every
         // read before the next tile reuses the stages.  The last step's reads
@@ -455,6 +464,15 @@ gemm_bf16_persistent(GemmParams p) {
         g16_wait_vm_lgkm0<0>();
         fence_frags(F0);
         fence_frags(F1);
+        {
+            asm volatile("" : "+v"(braw));
+            const float bv = p.bias ? h16_to_f32<F16>((uint16_t)braw) : -0.0f;
+            if (p.bias_rows) {
+                if (tid_t < BM) *(f32x4_t*)(bias_lds + 4 * tid_t) = f32x4_t{bv, bv, bv, bv};
+            } else if (tid_t < BN) {
+                bias_lds[tid_t] = bv;
+            }
+        }
         __builtin_amdgcn_s_barrier();
 
         // ---- epilogue: + bias (binary32, once), round once, store.
@@ -475,6 +493,13 @@ gemm_bf16_persistent(GemmParams p) {
         // offset; out-of-range buffer stores are dropped.  The host bounds
         // 128 * sCm * 4 below 2^31 and, with CVEC, makes N a multiple of the
         // 16-byte chunk, so a chunk is all valid or all not.
+#ifdef STUB_EPI
+#pragma unroll
+        for (int im = 0; im < IM; ++im)
+#pragma unroll
+            for (int in = 0; in < IN; ++in) asm volatile("" :: "a"(acc[im][in]));
+        if (false)
+#endif
         {
             using OutT = typename std::conditional<OUT_BF16 != 0, uint16_t, float>::type;
             constexpr int ESZ = (int)sizeof(OutT);
@@ -483,35 +508,44 @@ gemm_bf16_persistent(GemmParams p) {
             const int sCm = (int)p.sCm;
             const int rows_valid = (int)min<int64_t>(p.M - row_w, C::WROWS);
             const int cols_valid = (int)min<int64_t>(p.N - col_w, C::WCOLS);
-            if (rows_valid > 0 && cols_valid > 0) {
+            // Every wave runs the epilogue; a wave with no valid row or
+            // column gets an empty store range, so all its stores are dropped.
+            {
                 // An opaque copy of the lane id keeps every epilogue value below
                 // from being computed before the K loop (where it would stay live).
                 int lane_e = lane;
                 asm volatile("" : "+v"(lane_e));
                 const int lrow = lane_e & 31, lh = lane_e >> 5, lcol = 4 * lh;
-                const float* brow_w = bias_lds + wm * C::WROWS;
-                const float* bcol_w = bias_lds + BM + wn * C::WCOLS;
                 const uint64_t cv = (uint64_t)Cw;
                 const uint32_t clo = __builtin_amdgcn_readfirstlane((uint32_t)cv);
                 const uint32_t chi = __builtin_amdgcn_readfirstlane((uint32_t)(cv >> 32));
-                const int nrec = __builtin_amdgcn_readfirstlane(((rows_valid - 1) * sCm + cols_valid) * ESZ);
+                const int nrec = __builtin_amdgcn_readfirstlane(
+                    rows_valid > 0 && cols_valid > 0 ? ((rows_valid - 1) * sCm + cols_valid) * ESZ : 0);
                 const __amdgpu_buffer_rsrc_t rsC = __builtin_amdgcn_make_buffer_rsrc(
                     (void*)(((uint64_t)chi << 32) | clo), (short)0, nrec, 0x00020000);
-                // The lane's bias values, read before any staging write.
-                float brv[IM];
-                f32x4_t bcv[4 * IN];
-#pragma unroll
-                for (int im = 0; im < IM; ++im) brv[im] = brow_w[im * 32 + lrow];
-#pragma unroll
-                for (int q = 0; q < 4 * IN; ++q) bcv[q] = *(const f32x4_t*)(bcol_w + (q / 4) * 32 + 8 * (q % 4) + lcol);
-                // Block (im, in), group g with bias added, in binary32.
+                // Block (im, in), group g with its bias added once, in
+                // binary32: four consecutive bias values from LDS, the
+                // columns' own (column bias) or the row's value repeated
+                // (row bias), or -0.0 (no bias: x + -0.0 is x exactly).
+                const int bsel = p.bias_rows;
+                // The bias vectors of one 32-row block, read from LDS together
+                // (one wait) before the block's staging writes.
+                f32x4_t bq[4 * IN];
+                auto load_bias = [&](auto imc) {
+                    constexpr int im = decltype(imc)::value;
+                    g16_static_for<0, 4 * IN>([&](auto qc) {
+                        constexpr int q = decltype(qc)::value, in = q / 4, g = q % 4;
+                        const int bidx = bsel ? 4 * (wm * C::WROWS + im * 32 + lrow)
+                                              : wn * C::WCOLS + in * 32 + 8 * g + lcol;
+                        bq[q] = *(const f32x4_t*)(bias_lds + bidx);
+                    });
+                };
                 auto value = [&](auto imc, auto qc) {
                     constexpr int im = decltype(imc)::value;
                     constexpr int q = decltype(qc)::value, in = q / 4, g = q % 4;
                     f32x4_t v = {acc[im][in][4 * g], acc[im][in][4 * g + 1],
                                  acc[im][in][4 * g + 2], acc[im][in][4 * g + 3]};
-                    v += brv[im];
-                    v += bcv[q];
+                    v += bq[q];
                     return v;
                 };
                 if constexpr (CVEC) {
@@ -531,6 +565,7 @@ gemm_bf16_persistent(GemmParams p) {
                         g16_static_for<0, IM / PASSES>([&](auto ic) {
                             constexpr int im = ps * (IM / PASSES) + decltype(ic)::value;
                             const int r = (im % (IM / PASSES)) * 32 + lrow;
+                            load_bias(std::integral_constant<int, im>{});
                             g16_static_for<0, 4 * IN>([&](auto qc) {
                                 constexpr int in = decltype(qc)::value / 4, g = decltype(qc)::value % 4;
                                 const f32x4_t v = value(std::integral_constant<int, im>{}, qc);
@@ -543,6 +578,7 @@ gemm_bf16_persistent(GemmParams p) {
                                     *(f32x4_t*)(stg + r * ROWB + ((c ^ (r & (NCH - 1))) << 4)) = v;
                                 }
                             });
+                            __builtin_amdgcn_sched_barrier(0);
                         });
                         g16_static_for<0, RPP / RPI>([&](auto jc) {
                             constexpr int i = decltype(jc)::value;
@@ -556,6 +592,7 @@ gemm_bf16_persistent(GemmParams p) {
                     g16_static_for<0, IM>([&](auto imc) {
                         constexpr int im = decltype(imc)::value;
                         const int vrow = ((im * 32 + lrow) * sCm) * ESZ;
+                        load_bias(imc);
                         g16_static_for<0, 4 * IN>([&](auto qc) {
                             constexpr int in = decltype(qc)::value / 4, g = decltype(qc)::value % 4;
                             const f32x4_t v = value(imc, qc);
