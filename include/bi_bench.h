@@ -42,8 +42,14 @@ int bi_bench_gemm_grid(int64_t G, int64_t M, int64_t N, int64_t K,
  * 1 = the persistent kernel with 128x256 tiles, 2 = with 256x128 tiles,
  * 3 = with 128x128 tiles, 4 = with 192x256 tiles, 32 / 64 / 128 = the
  * small-tile kernel with (tile_rows x 64) blocks, one wave each.
- * Binary32 operands: 0 = 64x64 tiles, 32 = 32x32 tiles (others:
- * BI_ERR_UNSUPPORTED).  bias (or NULL) is indexed by column (bias_rows 0, as
+ * Binary32 operands: 0 = 64x64 tiles, 32 = 32x32 tiles, 16 = one
+ * workgroup per 16x16 block with its four K chains on four waves, each
+ * operand staged through LDS where its layout allows (A k-contiguous with
+ * 16-byte aligned rows and K % 4 == 0; B column-contiguous with 16-byte
+ * aligned k rows and N % 4 == 0), else loaded directly; 17 = the same with
+ * both operands loaded directly, 18 = only B staged (where it can be), 19 =
+ * only A staged (others: BI_ERR_UNSUPPORTED; 16 to 19 BI_ERR_UNSUPPORTED
+ * where a 16x16 block's operands span 2^31 bytes or more).  bias (or NULL) is indexed by column (bias_rows 0, as
  * bi_addmm) or by row (1, as the convolution's output channels).  Every
  * tile_rows gives the same bits as bi_bmm / bi_addmm, which choose the kernel
  * from the shape (the choice is reported by bi_bench_gemm_tile_rows).
@@ -74,8 +80,8 @@ int bi_bench_gemm_shared_cu(int64_t G, int64_t M, int64_t N, int64_t K,
 /*
  * bi_bench_gemm_tile_rows — the tile_rows that bi_bmm (G slices) or
  * bi_addmm / bi_mm (G = 1) pick for an M x N x K product on the current
- * device: 0, 1, 2, 3, 4, 32, 64 or 128 for 16-bit operands, 0 or 32 for
- * binary32.  Negative bi_status on a bad shape or without a gfx950 device.
+ * device: 0, 1, 2, 3, 4, 32, 64 or 128 for 16-bit operands, 0, 32 or 16
+ * for binary32.  Negative bi_status on a bad shape or without a gfx950 device.
  */
 int bi_bench_gemm_tile_rows(int64_t G, int64_t M, int64_t N, int64_t K, int in_dtype);
 

@@ -94,7 +94,8 @@ def gemm_shared_cu(A, B, grid, bias=None, out=None, out_dtype=None, stream=None)
 def gemm_tile(A, B, tile_rows, bias=None, bias_rows=False, out=None, out_dtype=None, stream=None):
     """The invariant 16-bit batched GEMM (A [G,M,K] or [M,K]) with the kernel
     forced: tile_rows 0 / 1 / 2 / 3 / 4 = persistent 256x256 / 128x256 / 256x128 /
-    128x128 / 192x256, 32 / 64 / 128 = small tile."""
+    128x128 / 192x256, 32 / 64 / 128 = small tile (binary32: 0 = 64x64 tiles,
+    32 = 32x32 tiles, 16 = 16x16 blocks with one K chain per wave)."""
     squeeze = A.dim() == 2
     if squeeze:
         A, B = A.unsqueeze(0), B.unsqueeze(0)

@@ -123,11 +123,39 @@ int gemm_check(const GemmDesc& d) {
 // 64, 128 rows) for each block per compute unit, plus 2 us, when latency
 // bound.  Only products with at most two rounds of 256x256 tiles are
 // considered for the others (larger ones keep the 256x256 tile).
+// The binary32 split-chain kernels address a 16x16 block's operands with
+// 32-bit byte offsets from the block's first row / column: 15 rows (columns)
+// plus K + 512 steps of the K stride (the loads run up to two stages of 256
+// past K, clamped) must stay below 2^31 bytes.
+static bool split32_fits(const GemmDesc& d) {
+    const int64_t lim = 1ll << 31;
+    return (15 * d.sAm + (d.K + 512) * d.sAk) * 4 < lim && (15 * d.sBn + (d.K + 512) * d.sBk) * 4 < lim;
+}
+
+// Operand layouts the split kernel stages in 16-byte pieces.  A: k
+// contiguous, every row and slice start 16-byte aligned, K a multiple of 4
+// (a piece never straddles K).  B: columns contiguous, every k row and slice
+// start 16-byte aligned, N a multiple of 4 (a piece never straddles N).
+static bool split32_stage_a(const GemmDesc& d) {
+    return d.sAk == 1 && (d.M == 1 || d.sAm % 4 == 0) && d.K % 4 == 0 && aligned(d.A, 16) &&
+           d.sA1 % 4 == 0 && d.sA2 % 4 == 0;
+}
+static bool split32_stage_b(const GemmDesc& d) {
+    return d.sBn == 1 && d.sBk % 4 == 0 && d.N % 4 == 0 && aligned(d.B, 16) && d.sB1 % 4 == 0 &&
+           d.sB2 % 4 == 0;
+}
+
 int gemm_tile_rows(const GemmDesc& d, int cus) {
     const int64_t slices = d.G1 * d.G2;
-    // Binary32: 32x32 tiles (one 16x16 MFMA chain per wave) where the 64x64
-    // tiles do not fill the compute units.
-    if (d.in_dtype == BI_F32) return slices * cdiv(d.M, G32_BM) * cdiv(d.N, G32_BN) < cus ? 32 : 0;
+    // Binary32: 64x64 tiles; 32x32 tiles where those do not fill the compute
+    // units; 16x16 blocks with the K chains on separate waves (returned as
+    // 16) where even the 32x32 tiles would occupy fewer than half of them and
+    // the blocks' byte offsets fit the split kernel's 32-bit buffer offsets.
+    if (d.in_dtype == BI_F32) {
+        if (slices * cdiv(d.M, G32_BM) * cdiv(d.N, G32_BN) >= cus) return 0;
+        if (2 * slices * cdiv(d.M, 32) * cdiv(d.N, 32) >= cus || !split32_fits(d)) return 32;
+        return 16;
+    }
     const int64_t tiles = slices * cdiv(d.M, G16_BM) * cdiv(d.N, G16_BN);
     // N <= 128 fills half of a 256-wide tile: the 256x128 tile (returned as 2)
     // does the same rows with half the MFMA work and B traffic.
@@ -268,8 +296,27 @@ int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override, int tile_r
         // 64x64 tiles, or 32x32 tiles where the 64x64 ones do not fill the
         // compute units (same per-element arithmetic, same bits).
         const int rows = tile_rows >= 0 ? tile_rows : grid_override > 0 ? 0 : gemm_tile_rows(d, cus);
-        if (rows != 0 && rows != 32) return BI_ERR_UNSUPPORTED;
-        const int bt = rows == 32 ? 32 : G32_BM;
+        if (rows != 0 && rows != 32 && (rows < 16 || rows > 19)) return BI_ERR_UNSUPPORTED;
+        if (rows >= 16 && rows <= 19 && d.K > 0) {
+            if (!split32_fits(d)) return BI_ERR_UNSUPPORTED;
+            // one workgroup per 16x16 block (and slice); K = 0 (a bias or
+            // zero fill) takes the 32x32 tiles below
+            const int64_t blocks = d.G1 * d.G2 * cdiv(d.M, 16) * cdiv(d.N, 16);
+            if (blocks > (1ll << 30)) return BI_ERR_UNSUPPORTED;
+            typedef void (*KernS)(GemmF32Params);
+            static const KernS kerns[2][2][2] = {
+                {{gemm_f32_split_chains<0, false, false>, gemm_f32_split_chains<1, false, false>},
+                 {gemm_f32_split_chains<0, false, true>, gemm_f32_split_chains<1, false, true>}},
+                {{gemm_f32_split_chains<0, true, false>, gemm_f32_split_chains<1, true, false>},
+                 {gemm_f32_split_chains<0, true, true>, gemm_f32_split_chains<1, true, true>}}};
+            // 16: each operand staged where its layout allows; 17: neither;
+            // 18: B only; 19: A only
+            const bool sa = (rows == 16 || rows == 19) && split32_stage_a(d);
+            const bool sb = (rows == 16 || rows == 18) && split32_stage_b(d);
+            hipLaunchKernelGGL(kerns[sa][sb][out_bf16], dim3((unsigned)blocks), dim3(256), 0, st, p);
+            return launch_status();
+        }
+        const int bt = rows == 0 ? G32_BM : 32;
         p.tiles_m = (int)cdiv(d.M, bt);
         p.tiles_n = (int)cdiv(d.N, bt);
         p.tiles_per_slice = p.tiles_m * p.tiles_n;
@@ -287,7 +334,7 @@ int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override, int tile_r
              {gemm_f32_persistent<1, false, 32>, gemm_f32_persistent<1, true, 32>}},
             {{gemm_f32_persistent<0, false, 16>, gemm_f32_persistent<0, true, 16>},
              {gemm_f32_persistent<1, false, 16>, gemm_f32_persistent<1, true, 16>}}};
-        hipLaunchKernelGGL(kerns32[rows == 32][out_bf16][ktail], dim3(grid), dim3(G32_THREADS), 0, st, p);
+        hipLaunchKernelGGL(kerns32[rows != 0][out_bf16][ktail], dim3(grid), dim3(G32_THREADS), 0, st, p);
     }
     return launch_status();
 }

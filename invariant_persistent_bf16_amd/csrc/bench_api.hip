@@ -104,10 +104,11 @@ int bi_bench_gemm_tile(int64_t G, int64_t M, int64_t N, int64_t K, const void* A
                        int64_t sBn, const void* bias, int bias_rows, void* C, int64_t sCg, int64_t sCm,
                        int64_t sCn, int in_dtype, int out_dtype, int tile_rows, void* stream) {
     if (tile_rows != 0 && tile_rows != 1 && tile_rows != 2 && tile_rows != 3 && tile_rows != 4 &&
-        tile_rows != 32 && tile_rows != 64 && tile_rows != 128)
+        (tile_rows < 16 || tile_rows > 19) && tile_rows != 32 && tile_rows != 64 && tile_rows != 128)
         return BI_ERR_UNSUPPORTED;
     if (in_dtype == BI_F32 && ((tile_rows >= 1 && tile_rows <= 4) || tile_rows > 32))
         return BI_ERR_UNSUPPORTED;
+    if (in_dtype != BI_F32 && tile_rows >= 16 && tile_rows <= 19) return BI_ERR_UNSUPPORTED;
     if (bias_rows != 0 && bias_rows != 1) return BI_ERR_UNSUPPORTED;
     GemmDesc d;
     std::memset(&d, 0, sizeof(d));

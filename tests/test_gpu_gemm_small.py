@@ -11,9 +11,9 @@ convolution's output channels), binary32 and 16-bit outputs, bfloat16 and
 binary16 operands, batched slices and padded output rows; the small-tile
 results are also checked against the fp64 oracle.  The automatic choice is
 checked on the shapes it is for: the batch-1 linear of the addmm workload and
-the batch-1 SigLIP patch convolution.  Binary32 products have two tile sizes
-of their own (64x64 and 32x32, the same 16x16x4 MFMA chain per element),
-compared the same way.
+the batch-1 SigLIP patch convolution.  Binary32 products have kernels of
+their own (64x64 and 32x32 tiles, 16x16 blocks with one K chain per wave; the
+same 16x16x4 MFMA chains per element), compared the same way.
 """
 import pytest
 import torch
@@ -147,11 +147,16 @@ def test_auto_choice_on_batch1_linear_and_conv():
     assert bitwise_equal(one[0], forced[0]), "row 0 alone differs from row 0 in the batch"
 
 
-@pytest.mark.parametrize("G,M,N,K", [(1, 1, 40, 4), (1, 37, 100, 130), (2, 70, 33, 512), (1, 200, 256, 4096)])
+@pytest.mark.parametrize("G,M,N,K", [(1, 1, 40, 4), (1, 37, 100, 130), (2, 70, 33, 512), (1, 200, 256, 4096),
+                                     (1, 512, 512, 66), (2, 21, 47, 772), (1, 5, 30, 1284)])
 @pytest.mark.parametrize("layout", ["plain", "transposed"])
 def test_f32_tiles_same_bits(G, M, N, K, layout):
-    # Binary32: 32x32 tiles (one 16x16 MFMA chain per wave) against 64x64
-    # tiles, with the K tail (K % 32 != 0), ragged M and N, transposed views,
+    # Binary32: 32x32 tiles (16x16 MFMA blocks, four K chains per wave) and
+    # 16x16 blocks with the four chains on four waves (each operand staged
+    # through LDS in stages of 256 k where its layout allows -- 1 to 16
+    # stages here, ragged last stage -- or loaded directly, in all four
+    # combinations), against 64x64 tiles, with the K
+    # tail (K % 32 != 0, K % 4 != 0), ragged M and N, transposed views,
     # column and row bias, binary32 and bfloat16 outputs.
     A = synth.randn((G, M, K), seed=M + K, dtype=torch.float32)
     if layout == "plain":
@@ -168,8 +173,14 @@ def test_f32_tiles_same_bits(G, M, N, K, layout):
             small = bi_bench.gemm_tile(Ad, Bd, 32, bias=bias, bias_rows=rows, out_dtype=od)
             torch.cuda.synchronize()
             assert bitwise_equal(small, big), f"fp32 32x32 tiles differ (bias_rows={rows}, out {od})"
-    small = bi_bench.gemm_tile(Ad, Bd, 32, bias=cbd, out_dtype=bi.BI_F32)
-    torch.cuda.synchronize()
-    for g in range(G):
-        assert_parity(to64(small[g]), oracle.mm(A[g], B[g], cb), f"fp32 small tile slice {g}")
-    assert bi_bench.gemm_tile_rows(G, M, N, K, bi.BI_F32) == 32
+            for t in (16, 17, 18, 19):
+                split = bi_bench.gemm_tile(Ad, Bd, t, bias=bias, bias_rows=rows, out_dtype=od)
+                torch.cuda.synchronize()
+                assert bitwise_equal(split, big), f"fp32 split chains {t} differ (bias_rows={rows}, out {od})"
+    for t in (32, 16, 17, 18, 19):
+        out = bi_bench.gemm_tile(Ad, Bd, t, bias=cbd, out_dtype=bi.BI_F32)
+        torch.cuda.synchronize()
+        for g in range(G):
+            assert_parity(to64(out[g]), oracle.mm(A[g], B[g], cb), f"fp32 kernel {t} slice {g}")
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert bi_bench.gemm_tile_rows(G, M, N, K, bi.BI_F32) == (32 if M == 512 else 16)

@@ -33,7 +33,8 @@ def choose():
 
 
 # 0 = 256x256, 1 = 128x256, 2 = 256x128, 3 = 128x128, 4 = 192x256 persistent
-# tiles; 32 / 64 / 128 = one-wave small tiles of that many rows.  Each entry
+# tiles; 32 / 64 / 128 = one-wave small tiles of that many rows (binary32:
+# 32 = 32x32 tiles, 16 = 16x16 blocks with one K chain per wave).  Each entry
 # is the fastest kernel measured for the shape (graph replay, same box).
 ADDMM = {1: 32, 16: 32, 32: 32, 64: 64, 96: 3, 128: 3, 200: 3, 256: 3, 384: 1, 512: 1,
          576: 4, 768: 4, 1024: 0, 1152: 1, 1536: 1, 2048: 0, 8192: 0}
@@ -54,12 +55,13 @@ def test_patch_conv_gemm(choose, B, want):
 def test_attention_products_and_binary32(choose):
     assert choose(256, 1024, 1024, 128) == 0     # Q K^T
     assert choose(256, 1024, 128, 1024) == 2     # P V: N = 128 fills half of a 256-wide tile
-    assert choose(1, 200, 256, 4096, F32) == 32  # binary32 products that leave CUs idle
+    assert choose(1, 200, 256, 4096, F32) == 16  # binary32: one chain per wave on 16x16 blocks
+    assert choose(1, 512, 512, 66, F32) == 32    # binary32: 32x32 tiles, four chains per wave
     assert choose(1, 4096, 4096, 1024, F32) == 0
 
 
 def test_only_existing_kernels(choose):
-    allowed16, allowed32 = {0, 1, 2, 3, 4, 32, 64, 128}, {0, 32}
+    allowed16, allowed32 = {0, 1, 2, 3, 4, 32, 64, 128}, {0, 16, 32}
     for cus in (80, 256, 304):
         for G in (1, 3, 64):
             for M in (1, 7, 100, 1000, 5000):
