@@ -62,6 +62,21 @@ int bi_bench_gemm_tile(int64_t G, int64_t M, int64_t N, int64_t K,
                        int in_dtype, int out_dtype, int tile_rows, void* stream);
 
 /*
+ * bi_bench_addmm_events — bi_addmm (same arguments, checks, kernel choice
+ * and bits) with the GEMM kernel launched through hipExtLaunchKernelGGL, so
+ * that the runtime records start_event / stop_event (hipEvent_t, created
+ * with timing enabled, owned by the caller) when the kernel itself starts
+ * and ends: hipEventElapsedTime between them is the kernel's execution time
+ * without the launch gap that events recorded around the call include.
+ * M or N = 0 launches nothing and records nothing.  BI_ERR_NULL if an
+ * event is NULL; otherwise bi_addmm's status.
+ */
+int bi_bench_addmm_events(int64_t M, int64_t N, int64_t K, const void* A, int64_t sAm, int64_t sAk,
+                          const void* B, int64_t sBk, int64_t sBn, const void* bias, void* C,
+                          int64_t sCm, int64_t sCn, int in_dtype, int out_dtype,
+                          void* start_event, void* stop_event, void* stream);
+
+/*
  * bi_bench_gemm_shared_cu — the invariant GEMM of bi_bmm (bfloat16 operands,
  * optional column bias as bi_addmm) on the persistent kernel with 128x128
  * tiles compiled without its LDS reservation (66 KiB per workgroup instead of

@@ -33,6 +33,8 @@ _SIGS = {
     "bi_bench_decode_attn_splits": (_int, [_i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _f32, _vp, _sz,
                                            _int, _int, _int, _vp]),
     "bi_bench_read_probe": (_int, [_vp, _sz, _vp, _vp]),
+    "bi_bench_addmm_events": (_int, [_i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i64,
+                                     _i64, _int, _int, _vp, _vp, _vp]),
 }
 _lib = None
 
@@ -170,3 +172,21 @@ def decode_attn_splits(q, k, v, scale, splits, out=None, out_dtype=_bi.BI_F32, w
 def read_probe(buf, sink, stream=None):
     _check("bi_bench_read_probe", lib().bi_bench_read_probe(
         _p(buf), buf.numel() * buf.element_size(), _p(sink), _stream(stream)))
+
+
+def addmm_events(bias, A, B, start, stop, out=None, out_dtype=None, stream=None):
+    """bi_addmm's product with the GEMM kernel launched so that the runtime
+    records `start` / `stop` (torch.cuda.Event, enable_timing=True, each
+    recorded once before so that it exists) at the start and the end of the
+    kernel's own execution."""
+    M, K = A.shape
+    N = B.shape[1]
+    od = _dt(A) if out_dtype is None else out_dtype
+    C = out if out is not None else _empty((M, N), _bi._tdt(od), A.device, stream)
+    if not start.cuda_event or not stop.cuda_event:
+        raise ValueError("record both events once before timing with them")
+    _check("bi_bench_addmm_events", lib().bi_bench_addmm_events(
+        M, N, K, _p(A), A.stride(0), A.stride(1), _p(B), B.stride(0), B.stride(1), _p(bias), _p(C),
+        C.stride(0), C.stride(1), _dt(A), _dt(C), ctypes.c_void_p(start.cuda_event),
+        ctypes.c_void_p(stop.cuda_event), _stream(stream)))
+    return C

@@ -3,6 +3,7 @@
 // so a rejected call touches neither the device nor the stream; accepted
 // calls enqueue kernels on the caller's stream and return without waiting.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <algorithm>
 #include <atomic>
@@ -199,20 +200,29 @@ int gemm_tile_rows(const GemmDesc& d, int cus) {
     return best_rows;
 }
 
+// One kernel launch of the GEMM, with the dispatch's own start / end events
+// when ev is given.
+template <typename Kern, typename... Args>
+static void launch_gemm_kernel(Kern kern, dim3 grid, dim3 block, hipStream_t st, const LaunchEvents* ev,
+                               Args... args) {
+    if (ev) hipExtLaunchKernelGGL(kern, grid, block, 0, st, ev->start, ev->stop, 0, args...);
+    else    hipLaunchKernelGGL(kern, grid, block, 0, st, args...);
+}
+
 template <bool KC, int O16, bool F16>
-static void gemm_small_launch(const GemmParams& p, int rows, int cvec4, hipStream_t st) {
+static void gemm_small_launch(const GemmParams& p, int rows, int cvec4, hipStream_t st, const LaunchEvents* ev) {
     typedef void (*KernS)(GemmParams, int);
     const KernS k = rows == 128 ? gemm_bf16_small<KC, O16, F16, 4>
                   : rows == 64  ? gemm_bf16_small<KC, O16, F16, 2>
                                 : gemm_bf16_small<KC, O16, F16, 1>;
     const int grid = (int)(cdiv(p.total_tiles, 8) * 8);
-    hipLaunchKernelGGL(k, dim3(grid), dim3(GS_THREADS), 0, st, p, cvec4);
+    launch_gemm_kernel(k, dim3(grid), dim3(GS_THREADS), st, ev, p, cvec4);
 }
 
 // Launch an already checked GEMM.  grid_override > 0 forces the persistent
 // grid size and tile_rows >= 0 the kernel (both used only to show that the
 // result does not depend on them).
-int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override, int tile_rows) {
+int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override, int tile_rows, const LaunchEvents* ev) {
     if (d.G1 == 0 || d.M == 0 || d.N == 0) return BI_OK;
     int cus = 0;
     int rc = device_cu_count(&cus);
@@ -245,15 +255,15 @@ int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override, int tile_r
                               d.sC2 % 4 == 0;
             const bool f16 = d.in_dtype == BI_F16;
             if (f16) {
-                if (kc) { if (out16) gemm_small_launch<true, 1, true>(p, rows, cvec4, st);
-                          else       gemm_small_launch<true, 0, true>(p, rows, cvec4, st); }
-                else    { if (out16) gemm_small_launch<false, 1, true>(p, rows, cvec4, st);
-                          else       gemm_small_launch<false, 0, true>(p, rows, cvec4, st); }
+                if (kc) { if (out16) gemm_small_launch<true, 1, true>(p, rows, cvec4, st, ev);
+                          else       gemm_small_launch<true, 0, true>(p, rows, cvec4, st, ev); }
+                else    { if (out16) gemm_small_launch<false, 1, true>(p, rows, cvec4, st, ev);
+                          else       gemm_small_launch<false, 0, true>(p, rows, cvec4, st, ev); }
             } else {
-                if (kc) { if (out16) gemm_small_launch<true, 1, false>(p, rows, cvec4, st);
-                          else       gemm_small_launch<true, 0, false>(p, rows, cvec4, st); }
-                else    { if (out16) gemm_small_launch<false, 1, false>(p, rows, cvec4, st);
-                          else       gemm_small_launch<false, 0, false>(p, rows, cvec4, st); }
+                if (kc) { if (out16) gemm_small_launch<true, 1, false>(p, rows, cvec4, st, ev);
+                          else       gemm_small_launch<true, 0, false>(p, rows, cvec4, st, ev); }
+                else    { if (out16) gemm_small_launch<false, 1, false>(p, rows, cvec4, st, ev);
+                          else       gemm_small_launch<false, 0, false>(p, rows, cvec4, st, ev); }
             }
             return launch_status();
         }
@@ -284,7 +294,7 @@ int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override, int tile_r
                               : rows == 3 ? gemm16_kernel_128x128(f16, kc, out16, cvec)
                               : rows == 4 ? gemm16_kernel_192x256(f16, kc, out16, cvec)
                                           : gemm16_kernel_256x256(f16, kc, out16, cvec);
-        hipLaunchKernelGGL(kern, dim3(grid), dim3(G16_THREADS), 0, st, p);
+        launch_gemm_kernel(kern, dim3(grid), dim3(G16_THREADS), st, ev, p);
     } else {
         GemmF32Params p;
         p.A = (const float*)d.A; p.B = (const float*)d.B; p.bias = (const float*)d.bias; p.C = d.C;
@@ -313,7 +323,7 @@ int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override, int tile_r
             // 18: B only; 19: A only
             const bool sa = (rows == 16 || rows == 19) && split32_stage_a(d);
             const bool sb = (rows == 16 || rows == 18) && split32_stage_b(d);
-            hipLaunchKernelGGL(kerns[sa][sb][out_bf16], dim3((unsigned)blocks), dim3(256), 0, st, p);
+            launch_gemm_kernel(kerns[sa][sb][out_bf16], dim3((unsigned)blocks), dim3(256), st, ev, p);
             return launch_status();
         }
         const int bt = rows == 0 ? G32_BM : 32;
@@ -334,7 +344,7 @@ int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override, int tile_r
              {gemm_f32_persistent<1, false, 32>, gemm_f32_persistent<1, true, 32>}},
             {{gemm_f32_persistent<0, false, 16>, gemm_f32_persistent<0, true, 16>},
              {gemm_f32_persistent<1, false, 16>, gemm_f32_persistent<1, true, 16>}}};
-        hipLaunchKernelGGL(kerns32[rows != 0][out_bf16][ktail], dim3(grid), dim3(G32_THREADS), 0, st, p);
+        launch_gemm_kernel(kerns32[rows != 0][out_bf16][ktail], dim3(grid), dim3(G32_THREADS), st, ev, p);
     }
     return launch_status();
 }

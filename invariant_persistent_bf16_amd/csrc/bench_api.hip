@@ -123,6 +123,18 @@ int bi_bench_gemm_tile(int64_t G, int64_t M, int64_t N, int64_t K, const void* A
     return gemm_launch(d, (hipStream_t)stream, 0, tile_rows);
 }
 
+int bi_bench_addmm_events(int64_t M, int64_t N, int64_t K, const void* A, int64_t sAm, int64_t sAk,
+                          const void* B, int64_t sBk, int64_t sBn, const void* bias, void* C, int64_t sCm,
+                          int64_t sCn, int in_dtype, int out_dtype, void* start_event, void* stop_event,
+                          void* stream) {
+    if (!start_event || !stop_event) return BI_ERR_NULL;
+    GemmDesc d = mm_desc(M, N, K, A, sAm, sAk, B, sBk, sBn, bias, C, sCm, sCn, in_dtype, out_dtype);
+    int rc = gemm_check(d);
+    if (rc != BI_OK) return rc;
+    const LaunchEvents ev = {(hipEvent_t)start_event, (hipEvent_t)stop_event};
+    return gemm_launch(d, (hipStream_t)stream, 0, -1, &ev);
+}
+
 int bi_bench_gemm_shared_cu(int64_t G, int64_t M, int64_t N, int64_t K, const void* A, int64_t sAg,
                             int64_t sAm, int64_t sAk, const void* B, int64_t sBg, int64_t sBk,
                             int64_t sBn, const void* bias, void* C, int64_t sCg, int64_t sCm,

@@ -28,6 +28,15 @@ int gemm_tile_rows(const GemmDesc& d, int cus);
 // 256x256 kernel (on grid_override workgroups if > 0); 32, 64 or 128 force
 // the small-tile kernel with blocks of that many rows.  Every choice gives the
 // same bits.
-int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override, int tile_rows = -1);
+// ev (optional): events that the runtime records at the start and the end
+// of the GEMM kernel's own execution (hipExtLaunchKernelGGL), for timing.
+struct LaunchEvents {
+    hipEvent_t start, stop;
+};
+int gemm_launch(const GemmDesc& d, hipStream_t st, int grid_override, int tile_rows = -1,
+                const LaunchEvents* ev = nullptr);
+GemmDesc mm_desc(int64_t M, int64_t N, int64_t K, const void* A, int64_t sAm, int64_t sAk,
+                 const void* B, int64_t sBk, int64_t sBn, const void* bias, void* C,
+                 int64_t sCm, int64_t sCn, int in_dtype, int out_dtype);
 
 }  // namespace bi

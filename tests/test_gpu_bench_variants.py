@@ -9,6 +9,8 @@
   gives row 0 equal to "alone" for M = 8, 63 and different for M = 64, 200;
   splits by load (132 units) give request 0 equal to batch 1 only at B = 1.
   This shows the invariance tests can see a changed reduction order.
+* The addmm with dispatch-attached events (the benchmark's timing of its
+  headline kernel) gives bi_addmm's bits.
 """
 import json
 import os
@@ -117,3 +119,30 @@ def test_read_probe_runs():
     sink = torch.empty(65536, dtype=torch.int32, device=DEV)
     bi_bench.read_probe(buf, sink)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M", [1, 200, 2048])
+def test_addmm_events_same_bits_and_kernel_time(M):
+    # bi_bench_addmm_events is bi_addmm with events attached to the GEMM
+    # dispatch: the same bits, and a kernel time no longer than events
+    # recorded around the call.
+    N, K = 1024, 512
+    A = synth.randn((M, K), seed=41, dtype=torch.bfloat16).to(DEV)
+    B = synth.randn((K, N), seed=42, dtype=torch.bfloat16, scale=0.05).to(DEV)
+    bias = synth.randn((N,), seed=43, dtype=torch.bfloat16).to(DEV)
+    ref = bi.bi_addmm(bias, A, B)
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    o0, o1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for e in (k0, k1):
+        e.record()
+    torch.cuda.synchronize()
+    o0.record()
+    got = bi_bench.addmm_events(bias, A, B, k0, k1)
+    o1.record()
+    torch.cuda.synchronize()
+    assert bitwise_equal(got, ref), f"addmm_events differs from bi_addmm at M={M}"
+    t_kernel, t_call = k0.elapsed_time(k1), o0.elapsed_time(o1)
+    print(f"M={M}: kernel {t_kernel * 1e3:.1f} us, around the call {t_call * 1e3:.1f} us", flush=True)
+    assert 0.0 < t_kernel <= t_call
+    with pytest.raises(ValueError):
+        bi_bench.addmm_events(bias, A, B, torch.cuda.Event(enable_timing=True), k1)
