@@ -92,8 +92,11 @@ int gemm_check(const GemmDesc& d) {
         if (d.bias && !aligned(d.bias, 2)) return BI_ERR_LAYOUT;
     } else {
         if (d.K > 0 && (!aligned(d.A, 4) || !aligned(d.B, 4))) return BI_ERR_LAYOUT;
-        // k times the K stride is a 32-bit element offset.
-        if (d.K > 0 && (d.K * d.sAk >= (1ll << 31) || d.K * d.sBk >= (1ll << 31))) return BI_ERR_UNSUPPORTED;
+        // The tiled kernels address a step's operands with 32-bit byte offsets
+        // from the tile's first row (column) and the step's first k.
+        const int64_t lim = 1ll << 31;
+        if (d.K > 0 && ((63 * d.sAm + 31 * d.sAk) * 4 + 4 >= lim || (63 * d.sBn + 31 * d.sBk) * 4 + 4 >= lim))
+            return BI_ERR_UNSUPPORTED;
         if (d.bias && !aligned(d.bias, 4)) return BI_ERR_LAYOUT;
     }
     const int64_t bm = d.in_dtype != BI_F32 ? G16_BM : G32_BM;

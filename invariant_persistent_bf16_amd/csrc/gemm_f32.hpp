@@ -10,24 +10,24 @@
 // is a function of K alone (never of M, the tile or the grid).  Rows/columns
 // past M/N read from clamped addresses and are never stored, the K tail is
 // zero-filled (a zero slice leaves a chain unchanged).  Operands keep their
-// binary32 precision: nothing is rounded to a narrower type.  Two tile sizes
-// run this same per-element arithmetic and
-// give the same bits: 64x64 outputs per workgroup (each of 4 waves a 32x32
-// block as 2x2 MFMA blocks of 16x16), and 32x32 (each wave one 16x16 block)
-// for products whose 64x64 tiles would leave most compute units idle; the
-// host picks by shape.  A small product's time is the length of its
-// dependent MFMA chain (one 16x16x4 step every ~45 ns); the four
-// interleaved chains are independent, so the chain is K/16 steps long
-// instead of K/4.
+// binary32 precision: nothing is rounded to a narrower type.  Three kernels
+// run this same per-element arithmetic and give the same bits; the host
+// picks by shape: 64x64 outputs per workgroup (each of 4 waves a 32x32 block
+// as 2x2 MFMA blocks of 16x16, its four chains interleaved), 32x32 (each wave
+// one 16x16 block) where the 64x64 tiles would leave most compute units idle,
+// and gemm_f32_split_chains below (one 16x16 block per workgroup, one chain
+// per wave) where even the 32x32 tiles would.  Four chains make an
+// element's dependent MFMA sequence K/16 steps long instead of K/4.
 //
-// Operands may have any element strides (the loads are scalar and coalesced
-// along whichever stride is 1), so transposed views need no copy.  Loads run
-// three K steps ahead of their LDS store in four register sets, issued
-// unconditionally (past the last step they re-read it), so the compiler's
-// waits cover exactly the set being stored; the address of each element is
-// fixed per tile and a step adds a uniform offset.  Per step that leaves one
-// address add per load beside the MFMAs (the K-tail variant, used only when
-// K is not a multiple of the step, clamps k per element and zeroes the tail).
+// Operands may have any element strides (the loads are 4-byte buffer loads
+// coalesced along whichever stride is 1), so transposed views need no copy.
+// Loads run three K steps ahead of their LDS store in four register sets,
+// issued unconditionally (past the last step they re-read it), so the
+// compiler's waits cover exactly the set being stored; each element's byte
+// offset from the tile's first row (column) is fixed per tile and a step
+// moves the wave-uniform base.  The 64x64 tile without a K tail fits 256
+// registers per lane, so two of its workgroups share a compute unit (the
+// grid is up to four workgroups per CU).
 #pragma once
 
 #include <type_traits>
@@ -54,6 +54,18 @@ struct GemmF32Params {
     int tiles_m, tiles_n, tiles_per_slice, total_tiles;
     int bias_rows;      // 1: bias indexed by row (conv output channel), 0: by column
 };
+
+// Buffer loads: a wave-uniform base in the descriptor, 32-bit byte offsets
+// per lane; an offset of GS32_OOB (past the 2^31 - 1 byte record count)
+// reads zero.
+constexpr uint32_t GS32_OOB = 0x80000000u;  // buffer offset that reads as zero
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gs32_rsrc(const float* base) {
+    const uint64_t v = (uint64_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, 0x7fffffff, 0x00020000);
+}
 
 // WT: rows (and columns) of one wave's block, 32 (2x2 MFMA blocks, 64x64
 // tile) or 16 (one MFMA block, 32x32 tile); p.tiles_* count tiles of 2 WT.
@@ -103,67 +115,71 @@ gemm_f32_persistent(GemmF32Params p) {
 
         // Loads run three K steps ahead of their LDS store: step j's operands
         // go to register set j % 4, issued at the start of step j - 3.  Every
-        // step issues its loads (past the last step it re-reads the last one,
-        // unused), so the code is straight-line and each store waits only for
-        // its own set.  The K tail (k >= K, read from a clamped address)
-        // becomes zero at the store.
+        // step issues its loads (past the last step they re-read it, unused),
+        // so the code is straight-line and each store waits only for its own
+        // set.
         float ra[4][NE], rb[4][NE];
-        // Per element of the thread's share of a step: its address at k = 0 of
-        // the tile, fixed for the tile; a step adds the uniform k0 times the K
-        // stride.  KTAIL (K not a multiple of the step): the element's k is
-        // clamped to K - 1 (32-bit: the host bounds K times the strides below
-        // 2^31) and the tail becomes zero at the store.
-        const float* pa[NE];
-        const float* pb[NE];
-        int ka[NE], kb_[NE];
+        // Per element of the thread's share of a step: its byte offset from
+        // the tile's first row (column) at the step's first k, fixed for the
+        // tile (32-bit: the host bounds 64 rows and 32 k of the strides below
+        // 2^31 bytes); a step moves the wave-uniform base by k0 times the K
+        // stride.  Rows and columns past M / N read clamped addresses (never
+        // stored); KTAIL (K not a multiple of the step): k >= K gets the
+        // out-of-range offset and reads zero.
+        const float* At = Ab + m0 * p.sAm;
+        const float* Bt = Bb + n0 * p.sBn;
+        uint32_t oa[NE], ob[NE];
 #pragma unroll
         for (int i = 0; i < NE; ++i) {
             const int idx = tid + G32_THREADS * i;
             const int mm = a_kfast ? idx / G32_BK : idx % BM;
-            ka[i] = a_kfast ? idx % G32_BK : idx / BM;
-            const int64_t r = min(m0 + mm, p.M - 1);
+            const int ka = a_kfast ? idx % G32_BK : idx / BM;
             const int nn = b_kfast ? idx / G32_BK : idx % BN;
-            kb_[i] = b_kfast ? idx % G32_BK : idx / BN;
-            const int64_t c = min(n0 + nn, p.N - 1);
-            if constexpr (KTAIL) {
-                pa[i] = Ab + r * p.sAm;
-                pb[i] = Bb + c * p.sBn;
-            } else {
-                pa[i] = Ab + r * p.sAm + ka[i] * p.sAk;
-                pb[i] = Bb + c * p.sBn + kb_[i] * p.sBk;
-            }
+            const int kb = b_kfast ? idx % G32_BK : idx / BN;
+            oa[i] = (uint32_t)((min(m0 + mm, p.M - 1) - m0) * p.sAm + (int64_t)ka * p.sAk) * 4u;
+            ob[i] = (uint32_t)((min(n0 + nn, p.N - 1) - n0) * p.sBn + (int64_t)kb * p.sBk) * 4u;
         }
-        const int K1 = (int)p.K - 1, sAk = (int)p.sAk, sBk = (int)p.sBk;
         auto load_tile = [&](int kt, auto uc) {
             constexpr int u = decltype(uc)::value;
             const int k0 = min(kt, nk - 1) * G32_BK;
-            if constexpr (KTAIL) {
+            const __amdgpu_buffer_rsrc_t rA = gs32_rsrc(At + (int64_t)k0 * p.sAk);
+            const __amdgpu_buffer_rsrc_t rB = gs32_rsrc(Bt + (int64_t)k0 * p.sBk);
+            // only the last step has a K tail; the others load unchecked (the
+            // branch is uniform and both sides issue the same loads in order)
+            const int kl = KTAIL && k0 + G32_BK > p.K ? (int)p.K - k0 : G32_BK;
 #pragma unroll
-                for (int i = 0; i < NE; ++i) ra[u][i] = pa[i][min(k0 + ka[i], K1) * sAk];
+            for (int i = 0; i < NE; ++i) {
+                const int idx = tid + G32_THREADS * i;
+                const int ka = a_kfast ? idx % G32_BK : idx / BM;
+                ra[u][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                    rA, !KTAIL || ka < kl ? oa[i] : GS32_OOB, 0, 0));
+            }
 #pragma unroll
-                for (int i = 0; i < NE; ++i) rb[u][i] = pb[i][min(k0 + kb_[i], K1) * sBk];
-            } else {
-                const int64_t oa = (int64_t)k0 * p.sAk, ob = (int64_t)k0 * p.sBk;
-#pragma unroll
-                for (int i = 0; i < NE; ++i) ra[u][i] = pa[i][oa];
-#pragma unroll
-                for (int i = 0; i < NE; ++i) rb[u][i] = pb[i][ob];
+            for (int i = 0; i < NE; ++i) {
+                const int idx = tid + G32_THREADS * i;
+                const int kb = b_kfast ? idx % G32_BK : idx / BN;
+                rb[u][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                    rB, !KTAIL || kb < kl ? ob[i] : GS32_OOB, 0, 0));
             }
         };
         auto store_tile = [&](int kt, auto uc) {
             constexpr int u = decltype(uc)::value, st = u & 1;
-            const int kl = (int)p.K - kt * G32_BK;   // valid k within this step
+            // past the last step the stored values belong to a stage that is
+            // never read again; the K tail already reads zero
+            (void)kt;
 #pragma unroll
             for (int i = 0; i < NE; ++i) {
                 const int idx = tid + G32_THREADS * i;
                 const int mm = a_kfast ? idx / G32_BK : idx % BM;
-                sA[st][ka[i]][mm] = !KTAIL || ka[i] < kl ? ra[u][i] : 0.0f;
+                const int ka = a_kfast ? idx % G32_BK : idx / BM;
+                sA[st][ka][mm] = ra[u][i];
             }
 #pragma unroll
             for (int i = 0; i < NE; ++i) {
                 const int idx = tid + G32_THREADS * i;
                 const int nn = b_kfast ? idx / G32_BK : idx % BN;
-                sB[st][kb_[i]][nn] = !KTAIL || kb_[i] < kl ? rb[u][i] : 0.0f;
+                const int kb = b_kfast ? idx % G32_BK : idx / BN;
+                sB[st][kb][nn] = rb[u][i];
             }
         };
         // Block (bi, bj) of the wave: rows wm WT + 16 bi .., columns wn WT + 16 bj ..;
@@ -252,15 +268,6 @@ __device__ __forceinline__ void gs32_static_for(F&& f) {
         f(std::integral_constant<int, I>{});
         gs32_static_for<N, I + 1>(f);
     }
-}
-
-constexpr uint32_t GS32_OOB = 0x80000000u;  // buffer offset that reads as zero
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t gs32_rsrc(const float* base) {
-    const uint64_t v = (uint64_t)base;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, 0x7fffffff, 0x00020000);
 }
 
 // The same per-element arithmetic for products too small to fill the

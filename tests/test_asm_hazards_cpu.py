@@ -12,7 +12,9 @@ LDS) replaced accumulators with the zero-filled stage it was reading.
 
 The check runs on the assembly that the library's code objects were
 assembled from (kept by the build), or on a fresh compile when the build is
-missing or older than the sources.
+missing or older than the sources.  The same assembly's kernel metadata pins
+the register budgets: no kernel spills, and the binary32 64x64-tile GEMM fits
+two workgroups per compute unit.
 """
 import glob
 import os
@@ -134,3 +136,33 @@ def test_library_kernels_have_no_pending_register_hazard(texts):
     assert checked > 100, checked
     assert n_asm_reads > 1000, n_asm_reads
     assert not found, "\n".join(f"{k}: {v}" for k, v in list(found.items())[:10])
+
+
+def _kernel_metadata(text):
+    """(name, vgpr_count, vgpr_spill_count) of each kernel in an assembly file."""
+    import re
+    meta = text[text.find("amdhsa.kernels"):]
+    out = []
+    for block in meta.split("\n  - ")[1:]:
+        name = re.search(r"\.name:\s+(\S+)", block)
+        vg = re.search(r"\.vgpr_count:\s+(\d+)", block)
+        sp = re.search(r"\.vgpr_spill_count:\s+(\d+)", block)
+        if name and vg and sp:
+            out.append((name.group(1), int(vg.group(1)), int(sp.group(1))))
+    return out
+
+
+def test_register_budgets():
+    # No kernel of the library spills registers, and the binary32 64x64-tile
+    # GEMM without a K tail fits 256 registers per lane, so that two of its
+    # workgroups share a compute unit (its grid is four workgroups per CU;
+    # at 332 registers it ran 24% slower at 4096 x 4096 x 1024).
+    texts = _asm_texts()
+    seen = 0
+    for src, text in texts.items():
+        for name, vgprs, spills in _kernel_metadata(text):
+            seen += 1
+            assert spills == 0, f"{name} spills {spills} registers"
+            if name.startswith("_ZN2bi19gemm_f32_persistentIL") and "Lb0ELi32E" in name:
+                assert vgprs <= 256, f"{name}: {vgprs} registers leave one workgroup per CU"
+    assert seen > 50
