@@ -93,6 +93,64 @@ __global__ void __launch_bounds__(256) conv_prepare32(const T* __restrict__ w, T
     }
 }
 
+// The same weight pack and unfold for the common patch geometry (16-bit
+// data, no padding, no dilation, one group, Kw, the column stride and W
+// even): every pair of consecutive k lies in one kernel row and starts at an
+// even input column, so a 16-byte piece of U (8 consecutive k) is four
+// aligned 32-bit loads.  Where each k of a piece lies relative to the
+// location's first input element is a function of the piece index alone: the
+// workgroup tabulates it in LDS once (koff, -1 for k >= Kg), so a piece costs
+// three divisions by constants (as multiply-high by host-computed magic
+// numbers, exact for the numerators the host admits), four loads and one
+// 16-byte store.  Same values as conv_prepare32.
+struct ConvPatch16 {
+    int Cin, H, W, L, OW, sh, sw, Kh, Kw, Kg, Kp;
+    int nchunk;           // Kp / 8 pieces per row
+    int wchunks, total;   // weight pieces (first), all pieces
+    uint64_t m_nchunk, m_L, m_OW;   // ceil(2^32 / d): floor(x / d) = (x * m) >> 32
+};
+
+__device__ __forceinline__ uint32_t conv_mdiv(uint32_t x, uint64_t m) {
+    return (uint32_t)(((uint64_t)x * m) >> 32);
+}
+
+__global__ void __launch_bounds__(256) conv_prepare_patch16(const uint16_t* __restrict__ w, uint16_t* __restrict__ wp,
+                                                            const uint16_t* __restrict__ x, uint16_t* __restrict__ u,
+                                                            ConvPatch16 g) {
+    extern __shared__ __attribute__((aligned(16))) int koff[];   // [nchunk * 4]
+    const int khw = g.Kh * g.Kw;
+    for (int j = threadIdx.x; j < g.nchunk * 4; j += blockDim.x) {
+        const int k = 2 * j;                 // piece j / 4, 32-bit word j % 4
+        const int ci = k / khw, rem = k - ci * khw, kh = rem / g.Kw, kw = rem - kh * g.Kw;
+        koff[j] = k < g.Kg ? (ci * g.H + kh) * g.W + kw : -1;
+    }
+    __syncthreads();
+    const uint32_t* x32 = (const uint32_t*)x;
+    const uint32_t* w32 = (const uint32_t*)w;
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < g.total; i += gridDim.x * blockDim.x) {
+        u32x4_t v;
+        if (i < g.wchunks) {
+            const int co = (int)conv_mdiv((uint32_t)i, g.m_nchunk), c = i - co * g.nchunk;
+            const int k0 = 8 * c;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = k0 + 2 * e < g.Kg ? w32[(co * g.Kg + k0) / 2 + e] : 0u;
+            *(u32x4_t*)(wp + co * g.Kp + k0) = v;
+            continue;
+        }
+        const int r = i - g.wchunks;
+        const int row = (int)conv_mdiv((uint32_t)r, g.m_nchunk), c = r - row * g.nchunk;
+        const int n = (int)conv_mdiv((uint32_t)row, g.m_L), l = row - n * g.L;
+        const int oh = (int)conv_mdiv((uint32_t)l, g.m_OW), ow = l - oh * g.OW;
+        const int base = (n * g.Cin * g.H + oh * g.sh) * g.W + ow * g.sw;   // even
+        const int4 ko = *(const int4*)&koff[4 * c];
+        v[0] = ko.x >= 0 ? x32[(base + ko.x) / 2] : 0u;
+        v[1] = ko.y >= 0 ? x32[(base + ko.y) / 2] : 0u;
+        v[2] = ko.z >= 0 ? x32[(base + ko.z) / 2] : 0u;
+        v[3] = ko.w >= 0 ? x32[(base + ko.w) / 2] : 0u;
+        *(u32x4_t*)(u + row * g.Kp + 8 * c) = v;
+    }
+}
+
 // One thread per 8 consecutive k of one (co) row.
 template <typename T>
 __global__ void conv_pack_weight(const T* __restrict__ w, T* __restrict__ wp, ConvGeom g) {

@@ -4,7 +4,9 @@ The SigLIP patch embedding (3 -> 1152 channels, 14x14 kernel, stride 14, 224x224
 images): sample 0 bit for bit the same at B in {1, 2, 4, 8, 16, 32} (the
 batch sweep of the VLA page), sampled outputs against the direct seven-loop
 oracle; general stride / padding / dilation / groups cases against the
-oracle; the all-ones closed form exactly.
+oracle (16-bit cases with no padding, one group and even kernel width,
+column stride and width take the specialised unfold, the SigLIP shape
+among them); the all-ones closed form and integer inputs exactly.
 """
 import numpy as np
 import pytest
@@ -79,6 +81,12 @@ CASES = [
     (2, 4, 35, 48, 20, 4, 8, (4, 8), (0, 0), (1, 1), 2),
     (1, 3, 20, 20, 8, 5, 5, (5, 5), (0, 0), (1, 1), 1),
     (2, 5, 27, 24, 16, 4, 6, (4, 6), (0, 0), (1, 1), 1),
+    # The specialised unfold for 16-bit data with even Kw, column stride and
+    # W, no padding, one group: overlapping windows, a zero-padded K
+    # (Kg = 12 -> 16) and locations per row that are not a power of two.
+    (2, 3, 11, 14, 24, 3, 4, (1, 2), (0, 0), (1, 1), 1),
+    (3, 3, 16, 18, 10, 2, 2, (2, 2), (0, 0), (1, 1), 1),
+    (2, 2, 13, 22, 9, 3, 4, (2, 4), (0, 0), (1, 1), 1),
 ]
 
 
