@@ -5,8 +5,8 @@ One step runs every operation of the path once, on inputs already resident
 in HBM (seeded synthetic data of the pages' workload shapes):
   * addmm   bf16  X [8192, 4096] @ W [4096, 14336] + bias -> bf16   (the large GEMM)
   * conv2d  bf16  SigLIP patch embedding, 32 images 3x224x224 -> [32, 1152, 16, 16]
-  * attention bf16, B=32, H=8, T=1024, D=128: S = Q K^T (fp32), softmax -> P (bf16),
-                O = P V (fp32)
+  * attention bf16, B=32, H=8, T=1024, D=128: P = softmax(scale Q K^T) (bf16; the
+                scores in binary32 on chip, the bits of bmm + softmax), O = P V (fp32)
   * decode  bf16  q [256, 32, 64], K, V [256, 32, 8192, 64], 2048-token chunks -> fp32
   * mm      fp32  X [200, 4096] @ W [4096, 256]
 The headline `value` is the addmm GEMM throughput in TFLOP/s (algorithmic
@@ -100,10 +100,9 @@ def main():
 
     G = ATT["B"] * ATT["H"]
     att_scale = float(torch.tensor(1 / math.sqrt(ATT["D"]), dtype=torch.float32))
-    Q = Kt = V = Sb = Pb = Ob = None
+    Q = Kt = V = Pb = Ob = None
     if want("attention"):
         Q, Kt, V = synth.attn_batch(synth.attn_shared(), ATT["B"], device=dev)
-        Sb = torch.empty(G, ATT["T"], ATT["T"], dtype=torch.float32, device=dev)
         Pb = torch.empty(G, ATT["T"], ATT["T"], dtype=torch.bfloat16, device=dev)
         Ob = torch.empty(G, ATT["T"], ATT["D"], dtype=torch.float32, device=dev)
 
@@ -132,10 +131,9 @@ def main():
     ops = {
         "addmm": lambda ev: bi_bench.addmm_events(bd, X, Wd, ev[0], ev[1], out=Y),
         "conv2d": lambda: bi.bi_conv2d(cx, cwd, cbd, stride=(14, 14), out=cy, workspace=cws),
-        "attention": lambda: (bi.bi_bmm(Q, Kt.transpose(1, 2), out=Sb),
-                              bi.bi_softmax_rows(Sb.view(G * ATT["T"], ATT["T"]), att_scale,
-                                                 out=Pb.view(G * ATT["T"], ATT["T"])),
-                              bi.bi_bmm(Pb, V, out=Ob)),
+        # P = softmax(scale Q K^T) in one kernel (the bits of bmm + softmax, S
+        # never written), then O = P V
+        "attention": lambda: (bi.bi_attention_probs(Q, Kt, att_scale, out=Pb), bi.bi_bmm(Pb, V, out=Ob)),
         "decode": lambda: bi.bi_decode_attn(dq, dk, dv, 0.125, out=dout, workspace=dws),
         "mm_fp32": lambda: bi.bi_mm(mXd, mWd, out=mY),
     }
@@ -187,7 +185,8 @@ def main():
         "addmm": 2.0 * (ADDMM["M"] * ADDMM["K"] + ADDMM["K"] * ADDMM["N"] + ADDMM["N"] +
                         ADDMM["M"] * ADDMM["N"]),
         "conv2d": 2.0 * (CONV_B * 3 * 224 * 224 + 1152 * 588 + 1152 + CONV_B * 1152 * 256),
-        "attention": G * (3 * ATT["T"] * ATT["D"] * 2 + ATT["T"] * ATT["T"] * (4 + 4 + 2 + 2) +
+        # Q, K, V read, P written and read back (bf16), O written (fp32)
+        "attention": G * (3 * ATT["T"] * ATT["D"] * 2 + ATT["T"] * ATT["T"] * (2 + 2) +
                           ATT["T"] * ATT["D"] * 4),
         "decode": DEC["B"] * DEC["H"] * (2 * DEC["S"] * DEC["D"] * 2 + DEC["D"] * 2 + DEC["D"] * 4),
         "mm_fp32": 4.0 * (MM32["M"] * MM32["K"] + MM32["K"] * MM32["N"] + MM32["M"] * MM32["N"]),
@@ -269,7 +268,7 @@ def main():
                                    dict(q=dq, k=dk, v=dv, out=dout), dict(W=mW, X=mX[MM32["M"]], Y=mY))
         out["cpu_baseline"] = cpu
         out["comparison"]["oracle_parity_sample"] = parity
-    del X, Y, Q, Kt, V, Sb, Pb, Ob, dq, dk, dv
+    del X, Y, Q, Kt, V, Pb, Ob, dq, dk, dv
     torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
 

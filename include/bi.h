@@ -313,6 +313,27 @@ int bi_softmax_rows(int64_t rows, int64_t cols, const void* S, int64_t ldS, floa
                     void* P, int64_t ldP, int out_dtype, void* stream);
 
 /*
+ * bi_attention_probs — P[g, t, :] = softmax(scale * Q[g, t, :] @ K[g]^T) in
+ * bfloat16, for g < G, t < T, over Tk keys, with the bits of the two-stage
+ * path: bi_bmm(Q, K^T) into binary32 S, then bi_softmax_rows(S, scale) to
+ * bfloat16 P ("Batch-Invariant Kernel Design: Conv2d and Attention BMM",
+ * section "Kernel 2: Attention BMM"; the softmax of "Unmasking the True
+ * Culprit ...", section "Beyond Matrix Multiplication").  S is not written
+ * to memory: a workgroup keeps a slice's keys in registers and a block of 32
+ * query rows' scores in LDS.  Q: bfloat16 (g, t, d) at Q[g*sQg + t*sQt + d];
+ * K: (g, j, d) at K[g*sKg + j*sKt + d] (d contiguous, rows 16-byte aligned:
+ * Q, K 16-byte aligned and their strides multiples of 8); P: bfloat16 (g, t,
+ * j) at P[g*sPg + t*sPt + j], 8-byte aligned, strides multiples of 4.
+ * D in {64, 128}, Tk in {256, 512, 768, 1024} (else BI_ERR_UNSUPPORTED).
+ * G == 0 or T == 0: nothing.  Errors before any launch: BI_ERR_SHAPE
+ * (negative sizes), BI_ERR_NULL, BI_ERR_LAYOUT, BI_ERR_UNSUPPORTED,
+ * BI_ERR_DEVICE.
+ */
+int bi_attention_probs(int64_t G, int64_t T, int64_t Tk, int64_t D, const void* Q, int64_t sQg,
+                       int64_t sQt, const void* K, int64_t sKg, int64_t sKt, float scale, void* P,
+                       int64_t sPg, int64_t sPt, void* stream);
+
+/*
  * Row operations beside the matmul, each row reduced by one wave (one
  * workgroup for rows longer than 4096) in an order fixed by `cols` alone, never
  * by the number of rows ("Unmasking the True Culprit ...", section "Beyond

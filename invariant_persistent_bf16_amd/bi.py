@@ -37,6 +37,8 @@ _SIGS = {
     "bi_prefill_attn_paged": (_int, [_i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _vp, _i64,
                                      _i64, _vp, _f32, _vp, _sz, _int, _int, _vp]),
     "bi_softmax_rows": (_int, [_i64, _i64, _vp, _i64, _f32, _vp, _i64, _int, _vp]),
+    "bi_attention_probs": (_int, [_i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _f32, _vp,
+                                  _i64, _i64, _vp]),
     "bi_rms_norm": (_int, [_i64, _i64, _vp, _i64, _vp, _f32, _vp, _i64, _int, _int, _vp]),
     "bi_log_softmax_rows": (_int, [_i64, _i64, _vp, _i64, _vp, _i64, _int, _int, _vp]),
     "bi_mean_rows": (_int, [_i64, _i64, _vp, _i64, _vp, _int, _int, _vp]),
@@ -312,10 +314,27 @@ def bi_mean_rows(x, out=None, out_dtype=BI_F32, stream=None):
     return y
 
 
-def attention(Q, K, V, scale, S_buf=None, P_buf=None, out=None, stream=None):
-    """Attention of flattened [G, T, D] operands in three launches:
-    S = bi_bmm(Q, K^T) (fp32), P = bi_softmax_rows(S, scale) (bf16), O = bi_bmm(P, V) (fp32)."""
+def bi_attention_probs(Q, K, scale, out=None, stream=None):
+    """P = softmax(scale * Q @ K^T) in bfloat16 (Q [G, T, D], K [G, Tk, D]),
+    with the bits of bi_bmm + bi_softmax_rows, without writing S."""
     G, T, D = Q.shape
+    Tk = K.shape[1]
+    P = _out((G, T, Tk), BI_BF16, Q.device, out, stream)
+    _check("bi_attention_probs", lib().bi_attention_probs(
+        G, T, Tk, D, _p(Q), Q.stride(0), Q.stride(1), _p(K), K.stride(0), K.stride(1), float(scale),
+        _p(P), P.stride(0), P.stride(1), _stream(stream)))
+    return P
+
+
+def attention(Q, K, V, scale, S_buf=None, P_buf=None, out=None, stream=None):
+    """Attention of flattened [G, T, D] operands.  With S_buf, three launches:
+    S = bi_bmm(Q, K^T) (fp32, into S_buf), P = bi_softmax_rows(S, scale)
+    (bf16), O = bi_bmm(P, V) (fp32).  Without: P = bi_attention_probs(Q, K,
+    scale) (the same P bits, S never written), then O = bi_bmm(P, V)."""
+    G, T, D = Q.shape
+    if S_buf is None and Q.dtype == torch.bfloat16:
+        P = bi_attention_probs(Q, K, scale, out=P_buf, stream=stream)
+        return bi_bmm(P, V, out=out, out_dtype=BI_F32, stream=stream)
     S = bi_bmm(Q, K.transpose(1, 2), out=S_buf, out_dtype=BI_F32, stream=stream)
     P = bi_softmax_rows(S.view(G * T, T), scale, out=None if P_buf is None else P_buf.view(G * T, T),
                         out_dtype=_dt(Q), stream=stream)

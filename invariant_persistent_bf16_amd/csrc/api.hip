@@ -11,6 +11,7 @@
 
 #include "../../include/bi.h"
 #include "conv_pack.hpp"
+#include "attn_probs.hpp"
 #include "decode.hpp"
 #include "prefill.hpp"
 #include "gemm_bf16.hpp"
@@ -868,6 +869,40 @@ int bi_softmax_rows(int64_t rows, int64_t cols, const void* S, int64_t ldS, floa
          {softmax_rows_kernel<0, true, 0>, softmax_rows_kernel<0, true, 1>}}};
     const Kern k = kerns[nch == 4 ? 0 : nch == 16 ? 1 : 2][vec ? 1 : 0][ob ? 1 : 0];
     hipLaunchKernelGGL(k, grid, dim3(SM_THREADS), 0, st, s, ldS, scale, P, ldP, rows, (int)cols);
+    return launch_status();
+}
+
+int bi_attention_probs(int64_t G, int64_t T, int64_t Tk, int64_t D, const void* Q, int64_t sQg,
+                       int64_t sQt, const void* K, int64_t sKg, int64_t sKt, float scale, void* P,
+                       int64_t sPg, int64_t sPt, void* stream) {
+    if (G < 0 || T < 0 || Tk < 0 || D < 0) return BI_ERR_SHAPE;
+    if ((D != 64 && D != 128) || (Tk != 256 && Tk != 512 && Tk != 768 && Tk != 1024)) return BI_ERR_UNSUPPORTED;
+    if (G == 0 || T == 0) return BI_OK;
+    if (!Q || !K || !P) return BI_ERR_NULL;
+    if (sQg < 0 || sQt < 0 || sKg < 0 || sKt < 0 || sPg < 0 || sPt < 0) return BI_ERR_LAYOUT;
+    // 16-byte fragments of Q and K rows, 8-byte chunks of P rows
+    if (!aligned(Q, 16) || !aligned(K, 16) || sQg % 8 || sQt % 8 || sKg % 8 || sKt % 8) return BI_ERR_LAYOUT;
+    if (!aligned(P, 8) || sPg % 4 || sPt % 4) return BI_ERR_LAYOUT;
+    if ((T > 1 && (sQt < D || sPt < Tk)) || sKt < D) return BI_ERR_LAYOUT;
+    if (G > (1ll << 24) || T > (1ll << 30)) return BI_ERR_UNSUPPORTED;
+    int cus = 0;
+    int rc = device_cu_count(&cus);
+    if (rc != BI_OK) return rc;
+    AttnProbsParams a;
+    a.Q = (const uint16_t*)Q; a.K = (const uint16_t*)K; a.P = (uint16_t*)P;
+    a.sQg = sQg; a.sQt = sQt; a.sKg = sKg; a.sKt = sKt; a.sPg = sPg; a.sPt = sPt;
+    a.G = (int)G; a.T = (int)T; a.scale = scale;
+    // one workgroup per CU: split a slice's query blocks when there are fewer slices than CUs
+    const int64_t nblocks = cdiv(T, AP_ROWS);
+    a.splits = (int)std::max<int64_t>(1, std::min<int64_t>(nblocks, cdiv(cus, G)));
+    const int64_t grid = G * a.splits;
+    if (grid > (1ll << 30)) return BI_ERR_UNSUPPORTED;
+    typedef void (*Kern)(AttnProbsParams);
+    static const Kern kerns[2][4] = {
+        {attn_probs_kernel<64, 256>, attn_probs_kernel<64, 512>, attn_probs_kernel<64, 768>, attn_probs_kernel<64, 1024>},
+        {attn_probs_kernel<128, 256>, attn_probs_kernel<128, 512>, attn_probs_kernel<128, 768>,
+         attn_probs_kernel<128, 1024>}};
+    hipLaunchKernelGGL(kerns[D == 128][Tk / 256 - 1], dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, a);
     return launch_status();
 }
 

@@ -69,6 +69,8 @@ def bi():
     L.bi_prefill_attn_paged.argtypes = [i64, i64, i64, vp, i64, vp, vp, i64, vp, vp, i64, i64, vp, i64, i64, vp,
                                         ctypes.c_float, vp, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, vp]
     L.bi_softmax_rows.argtypes = [i64, i64, vp, i64, ctypes.c_float, vp, i64, ctypes.c_int, vp]
+    L.bi_attention_probs.argtypes = [i64, i64, i64, i64, vp, i64, i64, vp, i64, i64, ctypes.c_float, vp,
+                                     i64, i64, vp]
     L.bi_rms_norm.argtypes = [i64, i64, vp, i64, vp, ctypes.c_float, vp, i64, ctypes.c_int, ctypes.c_int, vp]
     L.bi_log_softmax_rows.argtypes = [i64, i64, vp, i64, vp, i64, ctypes.c_int, ctypes.c_int, vp]
     L.bi_mean_rows.argtypes = [i64, i64, vp, i64, vp, ctypes.c_int, ctypes.c_int, vp]
@@ -212,6 +214,20 @@ def test_softmax_validation(bi):
     assert bi.bi_softmax_rows(4, 8, None, 8, 1.0, P, 8, BF16, None) == NULL
     assert bi.bi_softmax_rows(4, 8, P, 4, 1.0, P, 8, BF16, None) == LAYOUT
     assert bi.bi_softmax_rows(0, 8, P, 8, 1.0, P, 8, BF16, None) == OK
+
+
+def test_attention_probs_validation(bi):
+    def ap(G=2, T=64, Tk=1024, D=128, Q=P, sQg=64 * 128, sQt=128, K=P, sKg=1024 * 128, sKt=128,
+           Pp=P, sPg=64 * 1024, sPt=1024):
+        return bi.bi_attention_probs(G, T, Tk, D, Q, sQg, sQt, K, sKg, sKt, 0.125, Pp, sPg, sPt, None)
+    assert ap(T=-1) == SHAPE
+    assert ap(D=96) == UNSUP and ap(Tk=1000) == UNSUP and ap(Tk=2048) == UNSUP
+    assert ap(G=0) == OK and ap(T=0) == OK
+    assert ap(Q=None) == NULL and ap(Pp=None) == NULL
+    assert ap(Q=P + 8) == LAYOUT            # Q rows not 16-byte aligned
+    assert ap(sKt=132) == LAYOUT            # K row stride not a multiple of 8 elements
+    assert ap(sPt=1022) == LAYOUT           # P row stride not a multiple of 4
+    assert ap(sQt=64) == LAYOUT             # rows overlap: stride below D
 
 
 def test_row_ops_validation(bi):

@@ -8,6 +8,9 @@ rounding of its fp64 P into its second product; the GPU rounds its binary32
 P, so elements that sit within binary32 error of a bfloat16 rounding boundary
 may round the other way: that stage is gated by a bound derived from one
 bfloat16 unit in the last place of P (see DESIGN), the stages by 1e-5.
+The one-kernel probabilities (bi_attention_probs: scores in LDS, never in
+memory) must give the two-stage P bit for bit, on ragged and strided shapes
+and on the whole B = 32 workload, and then the same O.
 """
 import math
 
@@ -119,3 +122,56 @@ def test_slice0_invariant_B1_vs_B32_and_end_to_end():
     # worst case; observed flips are rare, so the error sits far below it.
     assert e <= 2.0 ** -8, f"end-to-end rel-L2 {e}"
     assert_parity(got, ref, "attention end-to-end", rel=1e-3, row=1e-2)
+
+
+def _two_stage_probs(Q, K, scale):
+    G, T, D = Q.shape
+    S = bi.bi_bmm(Q, K.transpose(1, 2), out_dtype=bi.BI_F32)
+    return bi.bi_softmax_rows(S.view(G * T, -1), scale, out_dtype=bi.BI_BF16).view(G, T, -1)
+
+
+@pytest.mark.parametrize("G,T,Tk,D", [(4, 1024, 1024, 128), (3, 100, 256, 64), (2, 33, 512, 128),
+                                      (5, 1, 768, 64), (300, 64, 256, 128), (1, 1000, 1024, 128)])
+def test_fused_probs_same_bits_as_two_stages(G, T, Tk, D):
+    # bi_attention_probs runs the bmm's MFMA chain and the softmax's reduction
+    # tree without writing S: P must equal bi_bmm -> bi_softmax_rows bit for
+    # bit; ragged query blocks (T % 32), one query row, more slices than CUs,
+    # and one slice split over many workgroups.
+    Q = synth.randn((G, T, D), seed=G + T, dtype=torch.bfloat16).to(DEV)
+    K = synth.randn((G, Tk, D), seed=Tk + D, dtype=torch.bfloat16).to(DEV)
+    for scale in (float(torch.tensor(1 / math.sqrt(D), dtype=torch.float32)), 0.37):
+        P = bi.bi_attention_probs(Q, K, scale)
+        ref = _two_stage_probs(Q, K, scale)
+        torch.cuda.synchronize()
+        assert bitwise_equal(P, ref), f"fused P differs (scale {scale})"
+
+
+def test_fused_probs_strided_views_and_errors():
+    G, T, Tk, D = 3, 70, 512, 64
+    Qw = synth.randn((G, T, 2 * D), seed=51, dtype=torch.bfloat16).to(DEV)
+    Kw = synth.randn((G, Tk, 3 * D), seed=52, dtype=torch.bfloat16).to(DEV)
+    Q, K = Qw[:, :, D:], Kw[:, :, :D]           # row strides 2D and 3D
+    Pw = torch.empty(G, T, Tk + 64, dtype=torch.bfloat16, device=DEV)
+    P = bi.bi_attention_probs(Q, K, 0.125, out=Pw[:, :, :Tk])
+    ref = _two_stage_probs(Q.contiguous(), K.contiguous(), 0.125)
+    torch.cuda.synchronize()
+    assert bitwise_equal(P, ref)
+    with pytest.raises(RuntimeError, match="BI_ERR_UNSUPPORTED"):
+        bi.bi_attention_probs(Q[:, :, :32], K[:, :, :32], 0.125)          # D = 32
+    with pytest.raises(RuntimeError, match="BI_ERR_UNSUPPORTED"):
+        bi.bi_attention_probs(Q, K[:, :300], 0.125)                        # Tk = 300
+
+
+def test_fused_attention_bench_config_same_bits():
+    # The B = 32 workload (256 slices of 1024 x 1024 x 128): every P and O bit
+    # equal to the three-launch path's.
+    Q, K, V = synth.attn_batch(synth.attn_shared(), 32, device=DEV)
+    S_buf = torch.empty(256, 1024, 1024, dtype=torch.float32, device=DEV)
+    P_ref = torch.empty(256, 1024, 1024, dtype=torch.bfloat16, device=DEV)
+    O_ref = bi.attention(Q, K, V, SCALE, S_buf=S_buf, P_buf=P_ref)
+    del S_buf
+    P = torch.empty_like(P_ref)
+    O = bi.attention(Q, K, V, SCALE, P_buf=P)
+    torch.cuda.synchronize()
+    assert bitwise_equal(P, P_ref), "fused P differs at the bench config"
+    assert bitwise_equal(O, O_ref), "O differs at the bench config"
