@@ -428,9 +428,10 @@ def small_batch(Wd, bd, x0, cwd, cbd, cx0):
 
 def invariance_cost(Wd, bd, x0, dq, dk, dv, Y):
     """Untimed extra: the invariant kernels against batch-size-tuned variants
-    (split-K for the GEMM filling the CUs, split-KV by load for decode) at the
-    batch sizes where they differ (GPU time from graph replay), plus an HBM
-    read-rate probe."""
+    (split-K for the GEMM filling the CUs; for decode the handbook's split-KV
+    by load and a fair split-KV whose parts fill the CUs and are merged in the
+    same launch) at the batch sizes where they differ (GPU time from graph
+    replay), plus an HBM read-rate probe."""
     import torch
 
     import synth
@@ -460,10 +461,17 @@ def invariance_cost(Wd, bd, x0, dq, dk, dv, Y):
                           device=dev)
         tf = _graph_us(lambda: bi.bi_decode_attn(q, k, v, 0.125, out=o, workspace=wsf)) * 1e-3
         tl = _graph_us(lambda: bi_bench.decode_attn_splits(q, k, v, 0.125, s, out=o, workspace=ws)) * 1e-3
+        # the fair competitor: parts sized to fill the CUs, waves sized to the
+        # parts, merged in the same launch
+        sk = bi_bench.decode_splitkv_policy(B, H, S, cus)
+        wsk = bi_bench.decode_splitkv_workspace(B, H, D, sk, dev)
+        tk = _graph_us(lambda: bi_bench.decode_attn_splitkv(q, k, v, 0.125, sk, wsk, out=o)) * 1e-3
         gbs = B * H * 2 * S * D * 2 / 1e9
         res["decode"][str(B)] = {"fixed_chunk_us": round(tf * 1e3, 2), "by_load_us": round(tl * 1e3, 2),
                                  "splits_by_load": s, "fixed_GBps": round(gbs / (tf * 1e-3), 1),
-                                 "fixed_over_by_load": round(tf / tl, 3)}
+                                 "fixed_over_by_load": round(tf / tl, 3),
+                                 "splitkv_fair_us": round(tk * 1e3, 2), "splitkv_fair_splits": sk,
+                                 "fixed_over_splitkv_fair": round(tf / tk, 3)}
     sink = torch.empty(65536, dtype=torch.int32, device=dev)
     tp = _time_ms(lambda: bi_bench.read_probe(dk, sink), iters=5)
     res["hbm_read_probe_GBps"] = round(dk.numel() * 2 / (tp * 1e-3) / 1e9, 1)

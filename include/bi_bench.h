@@ -155,6 +155,29 @@ int bi_bench_decode_attn_splits(int64_t B, int64_t H, int64_t S, int64_t D,
                                 int in_dtype, int out_dtype, int splits, void* stream);
 
 /*
+ * bi_bench_decode_attn_splitkv — decode attention (bfloat16 q, K, V as in
+ * bi_decode_attn, contiguous) split by load, as a fair batch-size-tuned
+ * competitor of the fixed 2048-token chunks: each (b, h) is cut into
+ * `splits` parts of L = S / splits tokens (L in {256, 512, 1024, 2048}, else
+ * BI_ERR_UNSUPPORTED), one workgroup per part with its 8 waves taking L / 8
+ * tokens each, and the parts' triples are merged in part order in the same
+ * launch by the workgroup that finishes a (b, h) last.  NOT batch
+ * invariant when the split count follows B (bi_bench_decode_splitkv_policy).
+ * ws: bi_bench_decode_splitkv_workspace_bytes(B, H, D, splits) bytes,
+ * 16-byte aligned, ZEROED by the caller before its first use (the last
+ * B * H words are counters that every call leaves at zero again).  Calls
+ * that share a workspace must not overlap.  bi_bench_decode_splitkv_policy
+ * gives the split count S / L for the longest L in {2048, 1024, 512, 256}
+ * dividing S whose grid of B * H * S / L workgroups fills `cus` compute units
+ * (L = 256 if none does; BI_ERR_UNSUPPORTED if 256 does not divide S).
+ */
+int bi_bench_decode_splitkv_policy(int64_t B, int64_t H, int64_t S, int cus);
+size_t bi_bench_decode_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t D, int splits);
+int bi_bench_decode_attn_splitkv(int64_t B, int64_t H, int64_t S, int64_t D, const void* q, const void* k,
+                                 const void* v, void* out, float scale, void* ws, size_t ws_bytes, int out_dtype,
+                                 int splits, void* stream);
+
+/*
  * bi_bench_read_probe — streams `bytes` (a multiple of 16) from `p` with
  * 16-byte loads and writes one reduction word per workgroup to `sink`
  * (at least 4 * 65536 bytes), to measure the achievable HBM read rate.

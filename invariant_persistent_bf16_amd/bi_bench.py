@@ -33,6 +33,10 @@ _SIGS = {
     "bi_bench_decode_attn_splits": (_int, [_i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _f32, _vp, _sz,
                                            _int, _int, _int, _vp]),
     "bi_bench_read_probe": (_int, [_vp, _sz, _vp, _vp]),
+    "bi_bench_decode_splitkv_policy": (_int, [_i64, _i64, _i64, _int]),
+    "bi_bench_decode_splitkv_workspace_bytes": (_sz, [_i64, _i64, _i64, _int]),
+    "bi_bench_decode_attn_splitkv": (_int, [_i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _f32, _vp, _sz, _int,
+                                            _int, _vp]),
     "bi_bench_addmm_events": (_int, [_i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i64,
                                      _i64, _int, _int, _vp, _vp, _vp]),
 }
@@ -190,3 +194,25 @@ def addmm_events(bias, A, B, start, stop, out=None, out_dtype=None, stream=None)
         C.stride(0), C.stride(1), _dt(A), _dt(C), ctypes.c_void_p(start.cuda_event),
         ctypes.c_void_p(stop.cuda_event), _stream(stream)))
     return C
+
+
+def decode_splitkv_policy(B, H, S, cus):
+    return lib().bi_bench_decode_splitkv_policy(B, H, S, cus)
+
+
+def decode_splitkv_workspace(B, H, D, splits, device):
+    """A zeroed workspace for decode_attn_splitkv (its counters start at zero)."""
+    n = lib().bi_bench_decode_splitkv_workspace_bytes(B, H, D, splits)
+    return torch.zeros((n + 3) // 4, dtype=torch.float32, device=device)
+
+
+def decode_attn_splitkv(q, k, v, scale, splits, workspace, out=None, out_dtype=_bi.BI_F32, stream=None):
+    """Decode split by load into `splits` parts, merged in the same launch
+    (q [B, H, D], K, V [B, H, S, D] contiguous bfloat16)."""
+    B, H, D = q.shape
+    S = k.shape[2]
+    o = out if out is not None else _empty((B, H, D), _bi._tdt(out_dtype), q.device, stream)
+    _check("bi_bench_decode_attn_splitkv", lib().bi_bench_decode_attn_splitkv(
+        B, H, S, D, _p(q), _p(k), _p(v), _p(o), float(scale), _p(workspace), workspace.numel() * 4,
+        _dt(o), splits, _stream(stream)))
+    return o

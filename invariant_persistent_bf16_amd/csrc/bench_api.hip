@@ -63,6 +63,64 @@ __global__ void decode_merge_parts_kernel(const float* __restrict__ ws, void* __
     store_out<OUT_BF16>(out, i, num / den);
 }
 
+// Split-KV decode sized by load, for the cost-of-invariance comparison: the
+// KV sequence of each (b, h) is cut into `splits` parts of L = 8 TW tokens
+// (the split count chosen from the batch so that the grid fills the compute
+// units), each part one workgroup whose 8 waves take TW tokens each (no
+// loads for tokens outside the part), and the merge runs in the same launch:
+// the workgroup that finishes a (b, h) last merges its parts' triples in part
+// order.  The compute units' L2 caches are not coherent with each other, so
+// the triples are written and read at system scope (through to memory,
+// GS_SYS = sc0 | sc1) and counted with a system-scope atomic, after the
+// stores have completed; a device-scope fence would instead write back the
+// whole L2 of every workgroup's XCD.  The last workgroup resets its counter
+// for the next call.  Not batch invariant (the split count follows B), and
+// run to run deterministic (the merge order is the part order, not the
+// arrival order).
+constexpr int DEC_SYS = 17;   // buffer cache policy: sc0 | sc1, system scope
+
+template <int D, int TW, int OUT_BF16>
+__global__ void __launch_bounds__(DEC_THREADS)
+decode_splitkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                      const uint16_t* __restrict__ v, float* __restrict__ ws, unsigned* __restrict__ cnt,
+                      void* __restrict__ out, int64_t S, int splits, float scale) {
+    constexpr int L = TW * DEC_WAVES;
+    const int64_t bh = blockIdx.x / splits;
+    const int c = blockIdx.x - (int)(bh * splits);
+    const int64_t w0 = (int64_t)c * L + (int64_t)(threadIdx.x >> 6) * TW;
+    DecContigKV<D> kv;
+    kv.rk = row_rsrc(k + (bh * S) * D, S * D * 2);
+    kv.rv = row_rsrc(v + (bh * S) * D, S * D * 2);
+    kv.lane_off = (threadIdx.x & 63) % (D / 8) * 16;
+    float* tp = ws + bh * splits * (int64_t)(2 + D);
+    decode_chunk_body<D, 32, DecContigKV<D>, TW, DEC_SYS>(kv, q + bh * D, tp + c * (int64_t)(2 + D), w0,
+                                                          min(S, w0 + TW), scale);
+    // Count this part once its triple's stores have completed; the last part merges.
+    __builtin_amdgcn_s_waitcnt(0);   // vmcnt, expcnt and lgkmcnt all zero
+    __syncthreads();
+    __shared__ unsigned last;
+    if (threadIdx.x == 0)
+        last = __hip_atomic_fetch_add(&cnt[bh], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) ==
+               (unsigned)(splits - 1);
+    __syncthreads();
+    if (!last) return;
+    const __amdgpu_buffer_rsrc_t rt = row_rsrc(tp, (int64_t)splits * (2 + D) * 4);
+    auto get = [&](int i) { return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rt, 4 * i, 0, DEC_SYS)); };
+    if (threadIdx.x < D) {
+        const int d = threadIdx.x;
+        float M = -INFINITY;
+        for (int p = 0; p < splits; ++p) M = fmaxf(M, get(p * (2 + D)));
+        float num = 0.0f, den = 0.0f;
+        for (int p = 0; p < splits; ++p) {
+            const float w = expf(get(p * (2 + D)) - M);
+            num = fmaf(w, get(p * (2 + D) + 2 + d), num);
+            den = fmaf(w, get(p * (2 + D) + 1), den);
+        }
+        store_out<OUT_BF16>(out, bh * D + d, num / den);
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(&cnt[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 __global__ void read_probe_kernel(const u32x4_t* __restrict__ p, int64_t n16, uint32_t* __restrict__ sink) {
     uint32_t acc = 0;
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n16;
@@ -293,6 +351,56 @@ int bi_bench_decode_attn_splits(int64_t B, int64_t H, int64_t S, int64_t D, cons
         if (out_dtype == BI_BF16) hipLaunchKernelGGL((decode_merge_parts_kernel<128, 1>), g2, dim3(256), 0, st, wsf, out, BH, splits, nsub);
         else                      hipLaunchKernelGGL((decode_merge_parts_kernel<128, 0>), g2, dim3(256), 0, st, wsf, out, BH, splits, nsub);
     }
+    return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_LAUNCH;
+}
+
+int bi_bench_decode_splitkv_policy(int64_t B, int64_t H, int64_t S, int cus) {
+    if (B < 1 || H < 1 || S < 1 || cus < 1) return BI_ERR_SHAPE;
+    // the longest part (2048 down to 256 tokens, dividing S) whose grid fills the CUs
+    for (int64_t L = DEC_CHUNK; L >= 256; L /= 2)
+        if (S % L == 0 && (B * H * (S / L) >= cus || L == 256)) return (int)(S / L);
+    return BI_ERR_UNSUPPORTED;
+}
+
+size_t bi_bench_decode_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t D, int splits) {
+    if (B < 0 || H < 0 || D < 1 || splits < 1) return 0;
+    // triples, then one counter per (b, h)
+    return (size_t)(B * H * splits * (2 + D) * 4 + B * H * 4);
+}
+
+int bi_bench_decode_attn_splitkv(int64_t B, int64_t H, int64_t S, int64_t D, const void* q, const void* k,
+                                 const void* v, void* out, float scale, void* ws, size_t ws_bytes, int out_dtype,
+                                 int splits, void* stream) {
+    if (out_dtype != BI_F32 && out_dtype != BI_BF16) return BI_ERR_DTYPE;
+    if (B < 0 || H < 0 || S < 1) return BI_ERR_SHAPE;
+    if (D != 64 && D != 128) return BI_ERR_UNSUPPORTED;
+    if (splits < 1 || S % splits) return BI_ERR_UNSUPPORTED;
+    const int64_t L = S / splits;
+    if (L != 256 && L != 512 && L != 1024 && L != 2048) return BI_ERR_UNSUPPORTED;
+    if ((S + DEC_CHUNK) * D * 2 >= (1ll << 31)) return BI_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0) return BI_OK;
+    if (!q || !k || !v || !out) return BI_ERR_NULL;
+    if (!ws || ws_bytes < bi_bench_decode_splitkv_workspace_bytes(B, H, D, splits) || ((uintptr_t)ws % 16))
+        return BI_ERR_WORKSPACE;
+    if (B * H * splits > (1ll << 30)) return BI_ERR_UNSUPPORTED;
+    float* wsf = (float*)ws;
+    unsigned* cnt = (unsigned*)(wsf + B * H * splits * (2 + D));
+    typedef void (*Kern)(const uint16_t*, const uint16_t*, const uint16_t*, float*, unsigned*, void*, int64_t, int,
+                         float);
+    // [D 64/128][L 256/512/1024/2048][out bf16]
+    static const Kern kerns[2][4][2] = {
+        {{decode_splitkv_kernel<64, 32, 0>, decode_splitkv_kernel<64, 32, 1>},
+         {decode_splitkv_kernel<64, 64, 0>, decode_splitkv_kernel<64, 64, 1>},
+         {decode_splitkv_kernel<64, 128, 0>, decode_splitkv_kernel<64, 128, 1>},
+         {decode_splitkv_kernel<64, 256, 0>, decode_splitkv_kernel<64, 256, 1>}},
+        {{decode_splitkv_kernel<128, 32, 0>, decode_splitkv_kernel<128, 32, 1>},
+         {decode_splitkv_kernel<128, 64, 0>, decode_splitkv_kernel<128, 64, 1>},
+         {decode_splitkv_kernel<128, 128, 0>, decode_splitkv_kernel<128, 128, 1>},
+         {decode_splitkv_kernel<128, 256, 0>, decode_splitkv_kernel<128, 256, 1>}}};
+    const int li = L == 256 ? 0 : L == 512 ? 1 : L == 1024 ? 2 : 3;
+    hipLaunchKernelGGL(kerns[D == 128][li][out_dtype == BI_BF16], dim3((unsigned)(B * H * splits)), dim3(DEC_THREADS),
+                       0, (hipStream_t)stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, wsf, cnt,
+                       out, S, splits, scale);
     return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_LAUNCH;
 }
 

@@ -141,13 +141,18 @@ struct DecPagedKV {
 // [w0, w0 + tw) with w0 = c*chunk + w*tw, tw = chunk/8; tokens at or past
 // t_end are masked.  The arithmetic does not depend on how K and V are stored,
 // so a paged request and the same values stored contiguously give the same bits.
-template <int D, int BATCH_MAX, class KV>
+// TW: tokens per wave (DEC_TOK_PER_WAVE for every product kernel; a smaller
+// TW only serves the benchmark's split-KV comparison, whose parts are shorter).
+// STORE_AUX: cache policy of the triple's stores (0 for every product kernel;
+// the comparison writes its triples through to memory for another workgroup).
+template <int D, int BATCH_MAX, class KV, int TW = DEC_TOK_PER_WAVE, int STORE_AUX = 0>
 __device__ __forceinline__ void decode_chunk_body(const KV& kv, const uint16_t* __restrict__ qrow,
                                                   float* __restrict__ trip, int64_t w0, int64_t t_end,
                                                   float scale) {
     constexpr int LPT = D / 8;               // lanes per token
     constexpr int TPI = 64 / LPT;            // tokens per wave-wide load
-    constexpr int NI = DEC_TOK_PER_WAVE / TPI;
+    constexpr int NI = TW / TPI;
+    static_assert(TW % TPI == 0 && TW <= DEC_TOK_PER_WAVE, "tokens per wave");
     // Loads in flight per lane (BATCH_MAX = 32: all of the wave's K (or V)
     // loads for D = 64, half for D = 128, as the register budget allows); one
     // workgroup per CU then keeps 256 KiB of K or V in flight, which hides HBM
@@ -267,18 +272,26 @@ __device__ __forceinline__ void decode_chunk_body(const KV& kv, const uint16_t* 
     }
     __syncthreads();
     // Wave partials in wave order; thread d < D finishes dimension d.
+    auto put = [&](int i, float x) {
+        if constexpr (STORE_AUX == 0) {
+            trip[i] = x;
+        } else {
+            const __amdgpu_buffer_rsrc_t rt = row_rsrc(trip, (2 + D) * 4);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rt, 4 * i, 0, STORE_AUX);
+        }
+    };
     if (tid < D) {
         float od = red_o[0][tid];
 #pragma unroll
         for (int w = 1; w < DEC_WAVES; ++w) od += red_o[w][tid];
-        trip[2 + tid] = od;
+        put(2 + tid, od);
     }
     if (tid == 0) {
         float lt = red_l[0];
 #pragma unroll
         for (int w = 1; w < DEC_WAVES; ++w) lt += red_l[w];
-        trip[0] = m;
-        trip[1] = lt;
+        put(0, m);
+        put(1, lt);
     }
 }
 

@@ -146,3 +146,29 @@ def test_addmm_events_same_bits_and_kernel_time(M):
     assert 0.0 < t_kernel <= t_call
     with pytest.raises(ValueError):
         bi_bench.addmm_events(bias, A, B, torch.cuda.Event(enable_timing=True), k1)
+
+
+@pytest.mark.parametrize("B,D", [(1, 64), (2, 128), (5, 64)])
+def test_splitkv_decode_correct_and_fixed_chunks_reproduce_the_product(B, D):
+    # The load-split decode (parts merged in the same launch) is correct for
+    # every split count, deterministic across calls (its counters reset
+    # themselves), and with 2048-token parts it is the product's arithmetic:
+    # bi_decode_attn's bits.
+    H, S = 4, 8192
+    q = synth.randn((B, H, D), seed=61, dtype=torch.bfloat16).to(DEV)
+    k = synth.randn((B, H, S, D), seed=62, dtype=torch.bfloat16).to(DEV)
+    v = synth.randn((B, H, S, D), seed=63, dtype=torch.bfloat16).to(DEV)
+    ref = oracle.decode(q.cpu(), k.cpu(), v.cpu(), 0.125)
+    prod = bi.bi_decode_attn(q, k, v, 0.125)
+    for splits in (4, 8, 16, 32):
+        ws = bi_bench.decode_splitkv_workspace(B, H, D, splits, DEV)
+        o1 = bi_bench.decode_attn_splitkv(q, k, v, 0.125, splits, ws)
+        o2 = bi_bench.decode_attn_splitkv(q, k, v, 0.125, splits, ws)
+        torch.cuda.synchronize()
+        assert bitwise_equal(o1, o2), f"splits={splits}: two calls differ"
+        assert_parity(to64(o1), ref, f"split-KV decode splits={splits}")
+        if splits == S // 2048:
+            assert bitwise_equal(o1, prod), "2048-token parts differ from bi_decode_attn"
+        assert torch.count_nonzero(ws[-(B * H):]) == 0, "counters not reset"
+    assert bi_bench.decode_splitkv_policy(1, 32, 8192, 256) == 8      # 32 x 8 parts of 1024 fill 256 CUs
+    assert bi_bench.decode_splitkv_policy(16, 32, 8192, 256) == 4     # 2048-token parts already fill them
