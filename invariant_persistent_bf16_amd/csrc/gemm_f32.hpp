@@ -307,7 +307,7 @@ template <int OUT_BF16, bool ASTAGE, bool BSTAGE, int KS = GS32_KS, int R = GS32
 __global__ void __launch_bounds__(256)
 gemm_f32_split_chains(GemmF32Params p) {
     static_assert(R % 2 == 0 && R >= 4, "the LDS slot of stage t is t % 2 = (t % R) % 2; stores run 2 stages ahead");
-    static_assert(GS32_MIX <= KS / 16, "memory shares follow MFMAs of the stage");
+    constexpr int MIX = GS32_MIX < KS / 16 ? GS32_MIX : KS / 16;   // MFMAs followed by a memory share
     constexpr int AP = KS + 4;            // A's LDS row pitch in words (row m starts at bank 4m)
     constexpr int NJ = KS / 16;           // MFMAs per wave and stage
     constexpr int APR = KS / 4;           // 16-byte pieces of A per row and stage
@@ -445,15 +445,15 @@ gemm_f32_split_chains(GemmF32Params p) {
         constexpr int u = decltype(uc)::value, g = decltype(gc)::value;
         gs32_static_for<NRD>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
-            if constexpr (i * GS32_MIX / NRD == g) read_item((u + 1) & 1, std::integral_constant<int, (u + 1) & 1>{}, ic);
+            if constexpr (i * MIX / NRD == g) read_item((u + 1) & 1, std::integral_constant<int, (u + 1) & 1>{}, ic);
         });
         gs32_static_for<NST>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
-            if constexpr (i * GS32_MIX / NST == g) store_item(u & 1, std::integral_constant<int, (u + 2) % R>{}, ic);
+            if constexpr (i * MIX / NST == g) store_item(u & 1, std::integral_constant<int, (u + 2) % R>{}, ic);
         });
         gs32_static_for<NLD>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
-            if constexpr (i * GS32_MIX / NLD == g) load_item(t + R - 1, std::integral_constant<int, (u + R - 1) % R>{}, ic);
+            if constexpr (i * MIX / NLD == g) load_item(t + R - 1, std::integral_constant<int, (u + R - 1) % R>{}, ic);
         });
     };
     auto step = [&](int t, auto uc) {
@@ -462,13 +462,13 @@ gemm_f32_split_chains(GemmF32Params p) {
                 constexpr int jj = decltype(jc)::value;
                 mfma(uc, jc);
                 __builtin_amdgcn_sched_barrier(0);
-                if constexpr (jj < GS32_MIX) {
+                if constexpr (jj < MIX) {
                     memory_share(t, uc, jc);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             });
         } else {
-            gs32_static_for<GS32_MIX>([&](auto gc) { memory_share(t, uc, gc); });
+            gs32_static_for<MIX>([&](auto gc) { memory_share(t, uc, gc); });
         }
         __syncthreads();
     };
