@@ -26,7 +26,8 @@
  *     library never synchronises.
  *   - Ownership: the caller owns every buffer, outputs and workspaces
  *     included.  The library allocates no device memory and keeps no mutable
- *     global state (it caches the read-only compute-unit count per device).
+ *     global state (it caches the read-only compute-unit count per device),
+ *     apart from the per-thread timing events of bi_set_launch_events.
  *   - Dtypes: BI_F32 = IEEE binary32, BI_BF16 = bfloat16, BI_F16 = IEEE
  *     binary16 (the matmul family and the convolution only).  Accumulation is
  *     always binary32.  16-bit outputs are the binary32 result rounded to
@@ -375,6 +376,23 @@ int bi_log_softmax_rows(int64_t rows, int64_t cols, const void* x, int64_t ldx, 
  */
 int bi_mean_rows(int64_t rows, int64_t cols, const void* x, int64_t ldx, void* y, int in_dtype,
                  int out_dtype, void* stream);
+
+/*
+ * bi_set_launch_events — attach timing events to the library's own kernels.
+ * For callers that time the entry points' kernels without a profiler (events
+ * recorded around a call also time the event packets and the launch gaps).
+ *
+ * start, stop: hipEvent_t values passed as void*, created with timing
+ * enabled and recorded at least once; the caller owns them.  After the call,
+ * the first kernel that any entry point launches from this host thread
+ * records start when it begins, and every kernel launched from this thread
+ * records stop when it ends, so once the calls complete, the elapsed time
+ * between the events is the time from the first kernel's start to the last
+ * one's end.  stop == NULL clears the setting (start is then ignored); a new
+ * call restarts it.  Entry points that launch no kernel (empty shapes,
+ * argument errors) leave the events untouched.  Returns BI_OK.
+ */
+int bi_set_launch_events(void* start, void* stop);
 
 #ifdef __cplusplus
 }

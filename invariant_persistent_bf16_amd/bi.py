@@ -18,6 +18,7 @@ _i64, _vp, _int, _f32, _sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctyp
 
 _SIGS = {
     "bi_status_string": (ctypes.c_char_p, [_int]),
+    "bi_set_launch_events": (_int, [_vp, _vp]),
     "bi_mm": (_int, [_i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _int, _int, _vp]),
     "bi_addmm": (_int, [_i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i64, _i64,
                         _int, _int, _vp]),
@@ -339,3 +340,15 @@ def attention(Q, K, V, scale, S_buf=None, P_buf=None, out=None, stream=None):
     P = bi_softmax_rows(S.view(G * T, T), scale, out=None if P_buf is None else P_buf.view(G * T, T),
                         out_dtype=_dt(Q), stream=stream)
     return bi_bmm(P.view(G, T, T), V, out=out, out_dtype=BI_F32, stream=stream)
+
+
+def bi_set_launch_events(start, stop):
+    """Attach torch.cuda.Event objects (enable_timing=True, each recorded once
+    before) to the library's kernels launched from this thread: start at the
+    first kernel's start, stop at the last kernel's end.  (None, None) clears."""
+    if stop is None:
+        lib().bi_set_launch_events(None, None)
+        return
+    if not start.cuda_event or not stop.cuda_event:
+        raise ValueError("record both events once before timing with them")
+    lib().bi_set_launch_events(ctypes.c_void_p(start.cuda_event), ctypes.c_void_p(stop.cuda_event))

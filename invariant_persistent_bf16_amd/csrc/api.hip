@@ -204,13 +204,32 @@ int gemm_tile_rows(const GemmDesc& d, int cus) {
     return best_rows;
 }
 
+// Events that the caller asked every kernel of the library to carry
+// (bi_set_launch_events): the first kernel launched after the request records
+// start when it begins, every kernel records stop when it ends, so stop ends
+// up at the end of the last one.  Per host thread; empty in normal use.
+static thread_local LaunchEvents t_events = {nullptr, nullptr};
+static thread_local bool t_events_first = false;
+
+// Every kernel launch of the entry points goes through here.
+template <typename Kern, typename... Args>
+static void launch_kernel(Kern kern, dim3 grid, dim3 block, size_t lds, hipStream_t st, Args... args) {
+    if (t_events.stop) {
+        hipExtLaunchKernelGGL(kern, grid, block, (uint32_t)lds, st, t_events_first ? t_events.start : nullptr,
+                              t_events.stop, 0, args...);
+        t_events_first = false;
+    } else {
+        hipLaunchKernelGGL(kern, grid, block, lds, st, args...);
+    }
+}
+
 // One kernel launch of the GEMM, with the dispatch's own start / end events
 // when ev is given.
 template <typename Kern, typename... Args>
 static void launch_gemm_kernel(Kern kern, dim3 grid, dim3 block, hipStream_t st, const LaunchEvents* ev,
                                Args... args) {
     if (ev) hipExtLaunchKernelGGL(kern, grid, block, 0, st, ev->start, ev->stop, 0, args...);
-    else    hipLaunchKernelGGL(kern, grid, block, 0, st, args...);
+    else    launch_kernel(kern, grid, block, 0, st, args...);
 }
 
 template <bool KC, int O16, bool F16>
@@ -426,7 +445,7 @@ int row_op_launch(int64_t rows, int64_t cols, const void* x, int64_t ldx, const 
     const int regime = cols <= 1024 ? 0 : cols <= 4096 ? 1 : cols <= 16384 ? 2 : 3;
     const int64_t rpb = regime < 2 ? 4 : 1;
     const dim3 grid((unsigned)std::min<int64_t>((rows + rpb - 1) / rpb, 1ll << 30));
-    hipLaunchKernelGGL(kerns[regime][ib ? 1 : 0][vec ? 1 : 0], grid, dim3(256), 0, st, x, ldx, w, eps, y, ldy, rows,
+    launch_kernel(kerns[regime][ib ? 1 : 0][vec ? 1 : 0], grid, dim3(256), 0, st, x, ldx, w, eps, y, ldy, rows,
                        (int)cols, ob ? 1 : 0);
     return launch_status();
 }
@@ -454,11 +473,11 @@ static void decode_paged_launch(dim3 g1, dim3 g2, hipStream_t st, bool uni, cons
                                 int H, int log2p, int num_pages, int max_seq, int maxchunks, float* wsf,
                                 float scale, void* out, int64_t BH, int out_dtype) {
     auto kern = uni ? decode_chunk_paged_kernel<D, true> : decode_chunk_paged_kernel<D, false>;
-    hipLaunchKernelGGL(kern, g1, dim3(DEC_THREADS), 0, st, (const uint16_t*)q, (const uint16_t*)kc,
+    launch_kernel(kern, g1, dim3(DEC_THREADS), 0, st, (const uint16_t*)q, (const uint16_t*)kc,
                        (const uint16_t*)vc, bt, max_pages, sl, H, log2p, num_pages, max_seq, maxchunks, (int)BH, wsf,
                        scale);
     auto merge = out_dtype == BI_BF16 ? decode_merge_kernel<D, 1> : decode_merge_kernel<D, 0>;
-    hipLaunchKernelGGL(merge, g2, dim3(256), 0, st, (const float*)wsf, out, BH, maxchunks, sl, H, max_seq);
+    launch_kernel(merge, g2, dim3(256), 0, st, (const float*)wsf, out, BH, maxchunks, sl, H, max_seq);
 }
 
 }  // namespace bi
@@ -585,7 +604,7 @@ int bi_conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, const void* x, int64
         // 2701 workgroups: 6.7 us, against 6.8-7.1 us with 2-16 per CU and
         // each workgroup's offset table spread over more pieces)
         const int pgrid = (int)std::min<int64_t>(cdiv(wchunks + uchunks, 256), 16 * cus);
-        hipLaunchKernelGGL(conv_prepare_patch16, dim3(pgrid), dim3(256), (size_t)(nchunk * 16), st,
+        launch_kernel(conv_prepare_patch16, dim3(pgrid), dim3(256), (size_t)(nchunk * 16), st,
                            (const uint16_t*)w, (uint16_t*)wp, (const uint16_t*)x, (uint16_t*)u, gp);
     } else if (idx32) {
         ConvGeom32 g32;
@@ -595,20 +614,20 @@ int bi_conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, const void* x, int64
         g32.cig = (int)g.cig; g32.Kg = (int)g.Kg; g32.Kp = (int)g.Kp;
         const int pgrid = (int)std::min<int64_t>(cdiv(wchunks + uchunks, 256), 64 * cus);
         if (in_dtype != BI_F32)
-            hipLaunchKernelGGL((conv_prepare32<uint16_t>), dim3(pgrid), dim3(256), 0, st,
+            launch_kernel((conv_prepare32<uint16_t>), dim3(pgrid), dim3(256), 0, st,
                                (const uint16_t*)w, (uint16_t*)wp, (const uint16_t*)x, (uint16_t*)u, g32);
         else
-            hipLaunchKernelGGL((conv_prepare32<float>), dim3(pgrid), dim3(256), 0, st,
+            launch_kernel((conv_prepare32<float>), dim3(pgrid), dim3(256), 0, st,
                                (const float*)w, (float*)wp, (const float*)x, (float*)u, g32);
     } else if (in_dtype != BI_F32) {
-        hipLaunchKernelGGL((conv_pack_weight<uint16_t>), dim3(wgrid), dim3(256), 0, st,
+        launch_kernel((conv_pack_weight<uint16_t>), dim3(wgrid), dim3(256), 0, st,
                            (const uint16_t*)w, (uint16_t*)wp, g);
-        hipLaunchKernelGGL((conv_unfold<uint16_t>), dim3(ugrid), dim3(256), 0, st,
+        launch_kernel((conv_unfold<uint16_t>), dim3(ugrid), dim3(256), 0, st,
                            (const uint16_t*)x, (uint16_t*)u, g);
     } else {
-        hipLaunchKernelGGL((conv_pack_weight<float>), dim3(wgrid), dim3(256), 0, st,
+        launch_kernel((conv_pack_weight<float>), dim3(wgrid), dim3(256), 0, st,
                            (const float*)w, (float*)wp, g);
-        hipLaunchKernelGGL((conv_unfold<float>), dim3(ugrid), dim3(256), 0, st,
+        launch_kernel((conv_unfold<float>), dim3(ugrid), dim3(256), 0, st,
                            (const float*)x, (float*)u, g);
     }
     rc = launch_status();
@@ -660,15 +679,15 @@ static int decode_launch(int64_t B, int64_t H, int64_t S, int64_t D, const void*
     const dim3 g2((unsigned)cdiv(BH * D, 256));
     const int sn = (int)nchunk;
     if (D == 64) {
-        hipLaunchKernelGGL((decode_chunk_kernel<64>), g1, dim3(DEC_THREADS), 0, st,
+        launch_kernel((decode_chunk_kernel<64>), g1, dim3(DEC_THREADS), 0, st,
                            (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, wsf, S, sn, DEC_CHUNK, scale);
-        if (out_dtype == BI_BF16) hipLaunchKernelGGL((decode_merge_kernel<64, 1>), g2, dim3(256), 0, st, wsf, out, BH, sn, nullptr, 1, 0);
-        else                      hipLaunchKernelGGL((decode_merge_kernel<64, 0>), g2, dim3(256), 0, st, wsf, out, BH, sn, nullptr, 1, 0);
+        if (out_dtype == BI_BF16) launch_kernel((decode_merge_kernel<64, 1>), g2, dim3(256), 0, st, wsf, out, BH, sn, nullptr, 1, 0);
+        else                      launch_kernel((decode_merge_kernel<64, 0>), g2, dim3(256), 0, st, wsf, out, BH, sn, nullptr, 1, 0);
     } else {
-        hipLaunchKernelGGL((decode_chunk_kernel<128>), g1, dim3(DEC_THREADS), 0, st,
+        launch_kernel((decode_chunk_kernel<128>), g1, dim3(DEC_THREADS), 0, st,
                            (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, wsf, S, sn, DEC_CHUNK, scale);
-        if (out_dtype == BI_BF16) hipLaunchKernelGGL((decode_merge_kernel<128, 1>), g2, dim3(256), 0, st, wsf, out, BH, sn, nullptr, 1, 0);
-        else                      hipLaunchKernelGGL((decode_merge_kernel<128, 0>), g2, dim3(256), 0, st, wsf, out, BH, sn, nullptr, 1, 0);
+        if (out_dtype == BI_BF16) launch_kernel((decode_merge_kernel<128, 1>), g2, dim3(256), 0, st, wsf, out, BH, sn, nullptr, 1, 0);
+        else                      launch_kernel((decode_merge_kernel<128, 0>), g2, dim3(256), 0, st, wsf, out, BH, sn, nullptr, 1, 0);
     }
     return launch_status();
 }
@@ -829,12 +848,12 @@ int bi_prefill_attn_paged(int64_t B, int64_t H, int64_t D, const void* q, int64_
     a.cscale = (float)((double)scale * 1.4426950408889634);
     hipStream_t st = (hipStream_t)stream;
     const dim3 g1((unsigned)(maxchunks * B * ntiles * H));
-    if (out_dtype == BI_BF16) hipLaunchKernelGGL((prefill_chunk_kernel<128, 1>), g1, dim3(PF_THREADS), 0, st, a);
-    else                      hipLaunchKernelGGL((prefill_chunk_kernel<128, 0>), g1, dim3(PF_THREADS), 0, st, a);
+    if (out_dtype == BI_BF16) launch_kernel((prefill_chunk_kernel<128, 1>), g1, dim3(PF_THREADS), 0, st, a);
+    else                      launch_kernel((prefill_chunk_kernel<128, 0>), g1, dim3(PF_THREADS), 0, st, a);
     if (maxchunks > 1) {
         const dim3 g2((unsigned)cdiv(total_q * H * (D / 4), 256));
-        if (out_dtype == BI_BF16) hipLaunchKernelGGL((prefill_merge_kernel<128, 1>), g2, dim3(256), 0, st, a);
-        else                      hipLaunchKernelGGL((prefill_merge_kernel<128, 0>), g2, dim3(256), 0, st, a);
+        if (out_dtype == BI_BF16) launch_kernel((prefill_merge_kernel<128, 1>), g2, dim3(256), 0, st, a);
+        else                      launch_kernel((prefill_merge_kernel<128, 0>), g2, dim3(256), 0, st, a);
     }
     return launch_status();
 }
@@ -868,7 +887,7 @@ int bi_softmax_rows(int64_t rows, int64_t cols, const void* S, int64_t ldS, floa
         {{softmax_rows_kernel<0, false, 0>, softmax_rows_kernel<0, false, 1>},
          {softmax_rows_kernel<0, true, 0>, softmax_rows_kernel<0, true, 1>}}};
     const Kern k = kerns[nch == 4 ? 0 : nch == 16 ? 1 : 2][vec ? 1 : 0][ob ? 1 : 0];
-    hipLaunchKernelGGL(k, grid, dim3(SM_THREADS), 0, st, s, ldS, scale, P, ldP, rows, (int)cols);
+    launch_kernel(k, grid, dim3(SM_THREADS), 0, st, s, ldS, scale, P, ldP, rows, (int)cols);
     return launch_status();
 }
 
@@ -902,7 +921,7 @@ int bi_attention_probs(int64_t G, int64_t T, int64_t Tk, int64_t D, const void* 
         {attn_probs_kernel<64, 256>, attn_probs_kernel<64, 512>, attn_probs_kernel<64, 768>, attn_probs_kernel<64, 1024>},
         {attn_probs_kernel<128, 256>, attn_probs_kernel<128, 512>, attn_probs_kernel<128, 768>,
          attn_probs_kernel<128, 1024>}};
-    hipLaunchKernelGGL(kerns[D == 128][Tk / 256 - 1], dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, a);
+    launch_kernel(kerns[D == 128][Tk / 256 - 1], dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, a);
     return launch_status();
 }
 
@@ -939,6 +958,12 @@ int bi_mean_rows(int64_t rows, int64_t cols, const void* x, int64_t ldx, void* y
     rc = device_cu_count(&cus);
     if (rc != BI_OK) return rc;
     return row_op_launch<RO_MEAN>(rows, cols, x, ldx, nullptr, 0.0f, y, 1, in_dtype, out_dtype, (hipStream_t)stream);
+}
+
+int bi_set_launch_events(void* start, void* stop) {
+    t_events = stop ? LaunchEvents{(hipEvent_t)start, (hipEvent_t)stop} : LaunchEvents{nullptr, nullptr};
+    t_events_first = stop != nullptr;
+    return BI_OK;
 }
 
 }  // extern "C"
