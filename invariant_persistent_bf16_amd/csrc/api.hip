@@ -593,7 +593,26 @@ int bi_conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, const void* x, int64
                        Kw % 2 == 0 && sw % 2 == 0 && W % 2 == 0 && aligned(x, 4) && aligned(w, 4) && idx32 &&
                        (wchunks + uchunks) * nchunk < (1ll << 32) && N * g.L * g.L < (1ll << 32) &&
                        g.L * g.OW < (1ll << 32) && nchunk * 16 <= 32 * 1024;
-    if (patch) {
+    // Row blocks (one workgroup per output row of locations): the input rows
+    // and U's rows in whole 16-byte pieces, the blocks within 48 KiB of LDS.
+    const int64_t blk = Kh * W;
+    const int64_t rows_lds = nchunk * 16 + Cin * blk * 2;
+    const int64_t rowblocks = N * g.OH;
+    const bool patch_rows = patch && aligned(x, 16) && (blk * 2) % 16 == 0 && (H * W * 2) % 16 == 0 &&
+                            (sh * W * 2) % 16 == 0 && rows_lds <= 48 * 1024 && rowblocks <= lim32 / 256 &&
+                            Cin * (blk / 8) * (blk / 8) < (1ll << 32) && g.OW * nchunk * nchunk < (1ll << 32);
+    if (patch_rows) {
+        ConvPatchRows gr;
+        gr.Cin = (int)Cin; gr.H = (int)H; gr.W = (int)W; gr.OH = (int)g.OH; gr.OW = (int)g.OW;
+        gr.sh = (int)sh; gr.sw = (int)sw; gr.Kh = (int)Kh; gr.Kw = (int)Kw; gr.Kg = (int)g.Kg; gr.Kp = (int)g.Kp;
+        gr.nchunk = (int)nchunk; gr.blk = (int)blk; gr.pieces = (int)(blk / 8); gr.wchunks = (int)wchunks;
+        gr.rowblocks = (int)rowblocks;
+        auto magic = [](int64_t d) { return (uint64_t)(((1ull << 32) + (uint64_t)d - 1) / (uint64_t)d); };
+        gr.m_nchunk = magic(nchunk); gr.m_pieces = magic(blk / 8);
+        const int grid = (int)std::max<int64_t>(rowblocks, cdiv(wchunks, 256));
+        launch_kernel(conv_prepare_patch_rows, dim3(grid), dim3(256), (size_t)rows_lds, st,
+                      (const uint16_t*)w, (uint16_t*)wp, (const uint16_t*)x, (uint16_t*)u, gr);
+    } else if (patch) {
         ConvPatch16 gp;
         gp.Cin = (int)Cin; gp.H = (int)H; gp.W = (int)W; gp.L = (int)g.L; gp.OW = (int)g.OW;
         gp.sh = (int)sh; gp.sw = (int)sw; gp.Kh = (int)Kh; gp.Kw = (int)Kw; gp.Kg = (int)g.Kg; gp.Kp = (int)g.Kp;

@@ -151,6 +151,94 @@ __global__ void __launch_bounds__(256) conv_prepare_patch16(const uint16_t* __re
     }
 }
 
+// The patch geometry again, one workgroup per output row (n, oh): the input
+// rows oh*sh .. oh*sh + Kh - 1 of every channel are Kh*W consecutive elements
+// of x, and U's rows (n, oh*OW .. oh*OW + OW - 1) are OW*Kp consecutive
+// elements, so the workgroup reads Cin such blocks with 16-byte loads into
+// LDS and writes its OW rows of U with 16-byte stores, each piece gathered
+// from LDS as four aligned 32-bit words (offsets tabulated per piece as in
+// conv_prepare_patch16).  Each thread of the grid also packs one piece of the
+// weight (the grid holds at least as many threads as pieces).  Needs, besides the patch
+// geometry, 16-byte aligned x and channel / row-block / row-stride sizes in
+// whole 16-byte pieces (checked on the host).  Same values as conv_prepare32.
+struct ConvPatchRows {
+    int Cin, H, W, OH, OW, sh, sw, Kh, Kw, Kg, Kp;
+    int nchunk;           // Kp / 8 pieces per row of U
+    int blk;              // Kh * W: elements of one channel's input rows
+    int pieces;           // blk / 8
+    int wchunks;          // Cout * nchunk weight pieces
+    int rowblocks;        // N * OH workgroups unfold; the grid may hold more, which only pack weight
+    uint64_t m_nchunk, m_pieces;   // ceil(2^32 / d): floor(x / d) = (x * m) >> 32
+};
+
+__global__ void __launch_bounds__(256) conv_prepare_patch_rows(const uint16_t* __restrict__ w, uint16_t* __restrict__ wp,
+                                                               const uint16_t* __restrict__ x, uint16_t* __restrict__ u,
+                                                               ConvPatchRows g) {
+    extern __shared__ __attribute__((aligned(16))) int smem[];
+    int* koff = smem;                                    // [nchunk * 4]: word offset of k pair inside the blocks, -1 past Kg
+    uint32_t* xs = (uint32_t*)(smem + g.nchunk * 4);     // [Cin][Kh][W] bf16 as words
+    const int tid = threadIdx.x;
+
+    // this thread's weight piece (one per thread of the grid): loads issued with the input's
+    const uint32_t* w32 = (const uint32_t*)w;
+    const int wi = blockIdx.x * 256 + tid;
+    u32x4_t wv = {0u, 0u, 0u, 0u};
+    int wco = 0, wk0 = 0;
+    if (wi < g.wchunks) {
+        wco = (int)conv_mdiv((uint32_t)wi, g.m_nchunk);
+        wk0 = 8 * (wi - wco * g.nchunk);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wv[e] = wk0 + 2 * e < g.Kg ? w32[(wco * g.Kg + wk0) / 2 + e] : 0u;
+    }
+    if ((int)blockIdx.x >= g.rowblocks) {   // uniform over the workgroup
+        if (wi < g.wchunks) *(u32x4_t*)(wp + wco * g.Kp + wk0) = wv;
+        return;
+    }
+    const int n = blockIdx.x / g.OH, oh = blockIdx.x - n * g.OH;
+
+    // the Cin row blocks, 16-byte pieces, up to 6 per thread in flight
+    const int nl = g.Cin * g.pieces;
+    const uint16_t* xb = x + ((int64_t)n * g.Cin * g.H + (int64_t)oh * g.sh) * g.W;
+    for (int j0 = tid; j0 < nl; j0 += 6 * 256) {
+        u32x4_t v[6];
+#pragma unroll
+        for (int r = 0; r < 6; ++r) {
+            const int j = j0 + 256 * r;
+            if (j < nl) {
+                const int ci = (int)conv_mdiv((uint32_t)j, g.m_pieces), q = j - ci * g.pieces;
+                v[r] = *(const u32x4_t*)(xb + (int64_t)ci * g.H * g.W + 8 * q);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 6; ++r) {
+            const int j = j0 + 256 * r;
+            if (j < nl) *(u32x4_t*)(xs + 4 * j) = v[r];   // channel blocks back to back: ci * blk + 8 q
+        }
+    }
+    const int khw = g.Kh * g.Kw;
+    for (int j = tid; j < g.nchunk * 4; j += 256) {
+        const int k = 2 * j;
+        const int ci = k / khw, rem = k - ci * khw, kh = rem / g.Kw, kw = rem - kh * g.Kw;
+        koff[j] = k < g.Kg ? (ci * g.blk + kh * g.W + kw) / 2 : -1;
+    }
+    if (wi < g.wchunks) *(u32x4_t*)(wp + wco * g.Kp + wk0) = wv;
+    __syncthreads();
+
+    // OW rows of U, consecutive: piece j is row ow = j / nchunk, k = 8 (j mod nchunk)
+    uint16_t* dst = u + ((int64_t)n * g.OH + oh) * g.OW * g.Kp;
+    for (int j = tid; j < g.OW * g.nchunk; j += 256) {
+        const int ow = (int)conv_mdiv((uint32_t)j, g.m_nchunk), c = j - ow * g.nchunk;
+        const int col = ow * g.sw / 2;
+        const int4 ko = *(const int4*)&koff[4 * c];
+        u32x4_t v;
+        v[0] = ko.x >= 0 ? xs[ko.x + col] : 0u;
+        v[1] = ko.y >= 0 ? xs[ko.y + col] : 0u;
+        v[2] = ko.z >= 0 ? xs[ko.z + col] : 0u;
+        v[3] = ko.w >= 0 ? xs[ko.w + col] : 0u;
+        *(u32x4_t*)(dst + 8 * j) = v;
+    }
+}
+
 // One thread per 8 consecutive k of one (co) row.
 template <typename T>
 __global__ void conv_pack_weight(const T* __restrict__ w, T* __restrict__ wp, ConvGeom g) {

@@ -5,8 +5,9 @@ images): sample 0 bit for bit the same at B in {1, 2, 4, 8, 16, 32} (the
 batch sweep of the VLA page), sampled outputs against the direct seven-loop
 oracle; general stride / padding / dilation / groups cases against the
 oracle (16-bit cases with no padding, one group and even kernel width,
-column stride and width take the specialised unfold, the SigLIP shape
-among them); the all-ones closed form and integer inputs exactly.
+column stride and width take the specialised unfolds, by 16-byte pieces or,
+where input rows come in whole pieces, by rows of locations, the SigLIP
+shape among them); the all-ones closed form and integer inputs exactly.
 """
 import numpy as np
 import pytest
@@ -87,6 +88,13 @@ CASES = [
     (2, 3, 11, 14, 24, 3, 4, (1, 2), (0, 0), (1, 1), 1),
     (3, 3, 16, 18, 10, 2, 2, (2, 2), (0, 0), (1, 1), 1),
     (2, 2, 13, 22, 9, 3, 4, (2, 4), (0, 0), (1, 1), 1),
+    # Row blocks in whole 16-byte pieces (W = 16, 40): one workgroup per row
+    # of locations; overlapping rows with unused input rows and a padded K,
+    # then non-overlapping patches; then blocks too large for its LDS budget
+    # (48 channels x 4 rows x 136), which fall back to the piecewise unfold.
+    (2, 3, 20, 16, 12, 3, 4, (2, 2), (0, 0), (1, 1), 1),
+    (3, 5, 24, 40, 16, 6, 8, (6, 8), (0, 0), (1, 1), 1),
+    (1, 48, 8, 136, 8, 4, 4, (4, 4), (0, 0), (1, 1), 1),
 ]
 
 
