@@ -26,10 +26,13 @@
 //     ascending d): lane l then holds query l % 32 and 32 of the 64 keys, so a
 //     query's maximum and sum are a lane's own values plus one exchange with
 //     lane l ^ 32;
-//   * online softmax within the chunk: m' = max(m, block max),
-//     l' = l * 2^(m - m') + sum 2^(x - m'), o' = o * 2^(m - m') + P V, keys of
-//     the block in a fixed order, 2^(x - m') evaluated as 2^fma(q.k, c, -m');
-//     masked keys (t > pos) give exactly 0;
+//   * online softmax within the chunk with a reference m that moves only when
+//     the block maximum exceeds it by more than 8 (m' = block max then, else
+//     m' = m, so every 2^(x - m') < 2^8): l' = l * 2^(m - m') + sum 2^(x - m'),
+//     o' = o * 2^(m - m') + P V, keys of the block in a fixed order,
+//     2^(x - m') evaluated as 2^fma(q.k, c, -m'); masked keys (t > pos) give
+//     exactly 0.  The chunk triple is then (m, l, o) for a reference m at most
+//     the chunk maximum, which the merge takes as it takes the maximum;
 //   * O^T += V^T P^T on the MFMA, P^T straight from the score registers as
 //     two bfloat16 terms (hi = bf16(p), lo = bf16(p - hi); two MFMAs, so p
 //     enters the binary32 sums to about 2^-17), V^T read with
@@ -126,6 +129,17 @@ __device__ __forceinline__ void pf_static_for(F&& f) {
     }
 }
 
+// The value of lane l and of lane l ^ 32, as a pair in either order
+// (v_permlane32_swap, one instruction; max and sum of the pair are symmetric).
+__device__ __forceinline__ float pf_max_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pf_sum_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ int pf_swap23(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
 template <int D, int OUT_BF16>
@@ -206,10 +220,32 @@ prefill_chunk_kernel(PfArgs a) {
         uint8_t* kdst = smem + st * STAGE;
         int ln = lane;
         asm volatile("" : "+v"(ln));
+        const int p = ln & 15;
+        const int g16 = 16 * (wave >> 1);   // the 16-row group holding the wave's K and V rows
+        if (a.log2p >= 4 && kbase + g16 + 15 < kend) {
+            // Pages of 16 or more tokens start at multiples of 16, so the
+            // group's 16 keys lie in one page: the page and the group's first
+            // row are wave-uniform, and a lane adds only its row within the
+            // group and its 16-byte chunk (32-bit offsets from a scalar base).
+            const int key0 = kbase + g16;
+            const int pg = __builtin_amdgcn_readfirstlane(pids[(key0 >> a.log2p) - pfirst]);
+            const int64_t row0 = (((int64_t)pg * a.H + h) << a.log2p) + (key0 & pmask);
+            const uint8_t* kb = a.kc + row0 * ROWB;
+            const uint8_t* vb = a.vc + row0 * ROWB;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int rho = 8 * wave + 4 * i + (ln >> 4);
+                const uint32_t rk = rho & 15, rv = pf_swap23(rho) & 15;
+                __builtin_amdgcn_global_load_lds((const void*)(kb + (rk * ROWB + ((p ^ rk) << 4))),
+                                                 (pf_lds_t*)(kdst + (8 * wave + 4 * i) * ROWB), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((const void*)(vb + (rv * ROWB + ((p ^ (4 * (rho & 3))) << 4))),
+                                                 (pf_lds_t*)(kdst + BLK + (8 * wave + 4 * i) * ROWB), 16, 0, 0);
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int rho = 8 * wave + 4 * i + (ln >> 4);
-            const int p = ln & 15;
             {
                 const int key = min(kbase + rho, kend - 1);
                 const int pg = pids[(key >> a.log2p) - pfirst];
@@ -343,22 +379,36 @@ prefill_chunk_kernel(PfArgs a) {
     // rounding is monotonic).  o holds blocks 0 .. i - 1 here.
     auto softmax = [&](int i) {
         const int kbase = kc0 + i * PF_KB;
-        const bool need_mask = kbase + PF_KB - 1 > wpos_lo;
+        // Keys past the query's position: -inf.  Only the blocks that reach
+        // past the wave's first position need it; the volatile statement keeps
+        // this a branch (selected on every block it would cost ~100
+        // instructions).  Key kbase + 4 hl + kr, kr = 32 kb + 8 (r >> 2) + (r & 3).
+        if (kbase + PF_KB - 1 > wpos_lo) {
+            int lim = pos - kbase - 4 * hl;
+            asm volatile("" : "+v"(lim));
+            // (lim - kr) < 0 selects -inf through a sign mask and a bitfield
+            // insert; the opaque mask keeps the compiler from turning this
+            // into 32 compares held in scalar register pairs at once.
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    uint32_t m = (uint32_t)((lim - (32 * kb + 8 * (r >> 2) + (r & 3))) >> 31);
+                    asm volatile("" : "+v"(m));
+                    sacc[kb][r] = __uint_as_float((m & 0xff800000u) | (~m & __float_as_uint(sacc[kb][r])));
+                }
+        }
         float mb = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float x = sacc[kb][r];
-                if (need_mask) {
-                    const int key = kbase + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-                    x = key <= pos ? x : -INFINITY;
-                }
-                sacc[kb][r] = x;
-                mb = fmaxf(mb, x);
-            }
-        mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-        const float m_new = fmaxf(m_run, mb * a.cscale);
+            for (int r = 0; r < 16; ++r) mb = fmaxf(mb, sacc[kb][r]);
+        mb = pf_max_xor32(mb);
+        // The reference m moves only when the block's maximum exceeds it by
+        // more than 8 (so every 2^(x - m) stays below 2^8): per query, from its
+        // own scores, so the order stays a function of the query alone.
+        const float m_blk = mb * a.cscale;
+        const float m_new = m_blk > m_run + 8.0f ? m_blk : m_run;
         // No key of the chunk yet (m_new = -inf): subtract 0 instead, so that
         // every 2^(x - m) is 2^-inf = 0 and alpha = 0 (o and l are still 0).
         const float m_use = m_new == -INFINITY ? 0.0f : m_new;
@@ -382,7 +432,7 @@ prefill_chunk_kernel(PfArgs a) {
                 pl[2 * kb + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0 - bf16lo_to_f32(hi), p1 - bf16hi_to_f32(hi));
             }
         l_run = l_run * alpha + ps;
-        // o * 1 = o: skip the rescale when no query of the wave raised its maximum.
+        // o * 1 = o: skip the rescale when no query of the wave moved its reference.
         if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
@@ -436,16 +486,21 @@ prefill_chunk_kernel(PfArgs a) {
 
     // ---- results of this chunk for the queries that have keys in it
     if (!wave_on) return;
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float l_tot = pf_sum_xor32(l_run);
     if (!q_ok || pos < kc0) return;
     const int nch = pos / PF_CHUNK + 1;
+    // The query's row again, from an opaque lane id, so that the 64-bit row
+    // is not kept live across the block loop.
+    int ln_o = lane;
+    asm volatile("" : "+v"(ln_o));
+    const int64_t row_o = rq.r0 + min(wq0 + (ln_o & 31), rq.n - 1);
     if (nch == 1) {
         // out[row][h][d], d = 32 db + 8 (r >> 2) + 4 hl + (r & 3).
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int64_t e = (row * a.H + h) * D + 32 * db + 8 * g + 4 * hl;
+                const int64_t e = (row_o * a.H + h) * D + 32 * db + 8 * g + 4 * hl;
                 f32x4_t v;
 #pragma unroll
                 for (int k = 0; k < 4; ++k) v[k] = o[db][4 * g + k] / l_tot;
@@ -458,7 +513,7 @@ prefill_chunk_kernel(PfArgs a) {
             }
     } else {
         // Triple row [m, l, -, -, o[0 .. D)] of this (chunk, head, query).
-        float* w = a.ws + (((int64_t)c * a.H + h) * a.total_q + row) * (4 + D);
+        float* w = a.ws + (((int64_t)c * a.H + h) * a.total_q + row_o) * (4 + D);
         if (hl == 0) *(f32x4_t*)w = f32x4_t{m_run, l_tot, 0.0f, 0.0f};
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
