@@ -184,6 +184,15 @@ int bi_bench_decode_attn_splitkv(int64_t B, int64_t H, int64_t S, int64_t D, con
  */
 int bi_bench_read_probe(const void* p, size_t bytes, void* sink, void* stream);
 
+/*
+ * bi_bench_wave_reduce — one wave of 64 lanes: lane l holds in[l] (binary32,
+ * 64 values) and writes the library's wave-wide xor-butterfly sum to out[l]
+ * and maximum to out[64 + l] (out: 128 values).  Exposes the reduction the
+ * softmax, row operations and attention probabilities share, so that a test
+ * can pin its order (offsets 32, 16, ..., 1) bit for bit.
+ */
+int bi_bench_wave_reduce(const float* in, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

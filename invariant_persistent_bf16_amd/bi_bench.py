@@ -33,6 +33,7 @@ _SIGS = {
     "bi_bench_decode_attn_splits": (_int, [_i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _f32, _vp, _sz,
                                            _int, _int, _int, _vp]),
     "bi_bench_read_probe": (_int, [_vp, _sz, _vp, _vp]),
+    "bi_bench_wave_reduce": (_int, [_vp, _vp, _vp]),
     "bi_bench_decode_splitkv_policy": (_int, [_i64, _i64, _i64, _int]),
     "bi_bench_decode_splitkv_workspace_bytes": (_sz, [_i64, _i64, _i64, _int]),
     "bi_bench_decode_attn_splitkv": (_int, [_i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _f32, _vp, _sz, _int,
@@ -216,3 +217,12 @@ def decode_attn_splitkv(q, k, v, scale, splits, workspace, out=None, out_dtype=_
         B, H, S, D, _p(q), _p(k), _p(v), _p(o), float(scale), _p(workspace), workspace.numel() * 4,
         _dt(o), splits, _stream(stream)))
     return o
+
+
+def wave_reduce(x, stream=None):
+    """The library's wave-wide xor-butterfly sum and maximum of x (64 binary32
+    values on the device): returns (sum per lane, max per lane)."""
+    assert x.dtype == torch.float32 and x.numel() == 64 and x.is_contiguous()
+    out = _empty((128,), torch.float32, x.device, stream)
+    _check("bi_bench_wave_reduce", lib().bi_bench_wave_reduce(_p(x), _p(out), _stream(stream)))
+    return out[:64], out[64:]

@@ -16,8 +16,8 @@
 //   * the softmax of row i is the one of softmax_rows_kernel: x = S * scale
 //     (binary32), lane l of the row's wave owns the 4-key chunks l, l + 64,
 //     l + 128, l + 192 and folds them in ascending order, then the same xor
-//     butterflies, exponential, reciprocal and Markstein-corrected quotient,
-//     and the same rounding to bfloat16.
+//     butterflies (wave_max / wave_sum), exponential, reciprocal and
+//     Markstein-corrected quotient, and the same rounding to bfloat16.
 //
 // One workgroup (4 waves) per (slice, range of 32-row query blocks), one per
 // compute unit.  Wave w keeps its quarter of the slice's keys (Tk / 4 keys,
@@ -121,15 +121,19 @@ attn_probs_kernel(AttnProbsParams p) {
         for (int r0 = 0; r0 < 8; r0 += AP_RG) {
             f32x4_t x[AP_RG][NCH];
             float m[AP_RG], sum[AP_RG], rsum[AP_RG];
+            // every score of the AP_RG rows read before the first is used, so
+            // the LDS reads overlap instead of each waiting for the last
+#pragma unroll
+            for (int q = 0; q < AP_RG; ++q)
+#pragma unroll
+                for (int v = 0; v < NCH; ++v)
+                    x[q][v] = *(const f32x4_t*)&sS[(8 * wave + r0 + q) * AP_PITCH + 4 * (lane + 64 * v)];
 #pragma unroll
             for (int q = 0; q < AP_RG; ++q) {
-                const float* srow = &sS[(8 * wave + r0 + q) * AP_PITCH];
 #pragma unroll
-                for (int v = 0; v < NCH; ++v) {
-                    const f32x4_t s4 = *(const f32x4_t*)&srow[4 * (lane + 64 * v)];
+                for (int v = 0; v < NCH; ++v)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) x[q][v][e] = s4[e] * p.scale;
-                }
+                    for (int e = 0; e < 4; ++e) x[q][v][e] *= p.scale;
                 m[q] = -INFINITY;
 #pragma unroll
                 for (int v = 0; v < NCH; ++v)
@@ -137,9 +141,7 @@ attn_probs_kernel(AttnProbsParams p) {
                     for (int e = 0; e < 4; ++e) m[q] = fmaxf(m[q], x[q][v][e]);
             }
 #pragma unroll
-            for (int o = 32; o >= 1; o >>= 1)
-#pragma unroll
-                for (int q = 0; q < AP_RG; ++q) m[q] = fmaxf(m[q], __shfl_xor(m[q], o, 64));
+            for (int q = 0; q < AP_RG; ++q) m[q] = wave_max(m[q]);
 #pragma unroll
             for (int q = 0; q < AP_RG; ++q) {
                 sum[q] = 0.0f;
@@ -152,9 +154,7 @@ attn_probs_kernel(AttnProbsParams p) {
                     }
             }
 #pragma unroll
-            for (int o = 32; o >= 1; o >>= 1)
-#pragma unroll
-                for (int q = 0; q < AP_RG; ++q) sum[q] += __shfl_xor(sum[q], o, 64);
+            for (int q = 0; q < AP_RG; ++q) sum[q] = wave_sum(sum[q]);
 #pragma unroll
             for (int q = 0; q < AP_RG; ++q) {
                 rsum[q] = 1.0f / sum[q];

@@ -11,6 +11,7 @@
 #include "gemm_bf16.hpp"
 #include "gemm_f32.hpp"
 #include "internal.hpp"
+#include "softmax.hpp"
 
 namespace bi {
 
@@ -130,6 +131,14 @@ __global__ void read_probe_kernel(const u32x4_t* __restrict__ p, int64_t n16, ui
     }
     for (int o = 32; o >= 1; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o, 64);
     if (threadIdx.x == 0) sink[blockIdx.x] = acc;
+}
+
+// One wave: the shared xor-butterfly sum and maximum of in[0 .. 63].
+__global__ void __launch_bounds__(64) wave_reduce_kernel(const float* __restrict__ in, float* __restrict__ out) {
+    const int l = threadIdx.x;
+    const float v = in[l];
+    out[l] = wave_sum(v);
+    out[64 + l] = wave_max(v);
 }
 
 static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -401,6 +410,12 @@ int bi_bench_decode_attn_splitkv(int64_t B, int64_t H, int64_t S, int64_t D, con
     hipLaunchKernelGGL(kerns[D == 128][li][out_dtype == BI_BF16], dim3((unsigned)(B * H * splits)), dim3(DEC_THREADS),
                        0, (hipStream_t)stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, wsf, cnt,
                        out, S, splits, scale);
+    return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_LAUNCH;
+}
+
+int bi_bench_wave_reduce(const float* in, float* out, void* stream) {
+    if (!in || !out) return BI_ERR_NULL;
+    hipLaunchKernelGGL(wave_reduce_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, in, out);
     return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_LAUNCH;
 }
 

@@ -11,10 +11,13 @@
   This shows the invariance tests can see a changed reduction order.
 * The addmm with dispatch-attached events (the benchmark's timing of its
   headline kernel) gives bi_addmm's bits.
+* The wave-wide reduction shared by the softmax, the row operations and the
+  attention probabilities adds in the xor-butterfly order, bit for bit.
 """
 import json
 import os
 
+import numpy as np
 import pytest
 import torch
 
@@ -172,3 +175,27 @@ def test_splitkv_decode_correct_and_fixed_chunks_reproduce_the_product(B, D):
         assert torch.count_nonzero(ws[-(B * H):]) == 0, "counters not reset"
     assert bi_bench.decode_splitkv_policy(1, 32, 8192, 256) == 8      # 32 x 8 parts of 1024 fill 256 CUs
     assert bi_bench.decode_splitkv_policy(16, 32, 8192, 256) == 4     # 2048-token parts already fill them
+
+
+def test_wave_reduction_order_is_the_xor_butterfly():
+    # The cross-lane sum shared by the softmax, the row operations and the
+    # attention probabilities: at offsets 32, 16, 8, 4, 2, 1 each lane adds
+    # the value of lane l ^ o.  Values spread over many binades so that another
+    # order of the same additions rounds differently; the binary32 emulation
+    # below follows the butterfly step by step (every lane ends equal).
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal(64) * 2.0 ** rng.integers(-20, 20, 64)).astype(np.float32)
+    s = x.copy()
+    lanes = np.arange(64)
+    for o in (32, 16, 8, 4, 2, 1):
+        s = (s + s[lanes ^ o]).astype(np.float32)
+    got_s, got_m = bi_bench.wave_reduce(torch.from_numpy(x).to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(got_s.cpu().numpy().view(np.uint32), s.view(np.uint32))
+    assert np.all(got_m.cpu().numpy() == x.max())
+    # a plain left-to-right sum rounds differently on these values, so the
+    # check above does see the order
+    seq = np.float32(0.0)
+    for v in x:
+        seq = np.float32(seq + v)
+    assert seq != s[0]
