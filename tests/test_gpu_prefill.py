@@ -127,3 +127,42 @@ def test_prefill_long_prompt_sampled():
     bt_s = bt.cpu().expand(len(rows), -1).contiguous()
     ref = oracle.prefill_paged(qs, cu_s, p0_s, kc.cpu(), vc.cpu(), bt_s, SCALE)
     assert_parity(to64(o[rows]), ref, "prefill 8192 sampled rows")
+
+
+def _repage(kc, vc, bt, lens, P, seed):
+    """The same tokens of each request in pages of P tokens (a seeded permutation of pages)."""
+    P0, H, D = kc.shape[2], kc.shape[1], kc.shape[3]
+    npg = [(n + P - 1) // P for n in lens]
+    num_pages = sum(npg) + 3
+    g = torch.Generator().manual_seed(seed)
+    perm = torch.randperm(num_pages, generator=g)
+    kc2 = torch.zeros((num_pages, H, P, D), dtype=kc.dtype)
+    vc2 = torch.zeros_like(kc2)
+    bt2 = torch.full((len(lens), max(npg)), -1, dtype=torch.int32)
+    used = 0
+    for b, n in enumerate(lens):
+        t = torch.arange(n)
+        src_page, src_slot = bt[b, t // P0].long(), t % P0
+        pages = perm[used:used + npg[b]]
+        used += npg[b]
+        bt2[b, :npg[b]] = pages.to(torch.int32)
+        dst_page, dst_slot = pages[t // P], t % P
+        for c2, c in ((kc2, kc), (vc2, vc)):
+            c2[dst_page, :, dst_slot, :] = c[src_page, :, src_slot, :]
+    return kc2, vc2, bt2
+
+
+@pytest.mark.parametrize("P", [1, 4, 8, 32, 64, 128])
+def test_page_size_does_not_change_the_bits(P):
+    # Pages only place the tokens: every page size gives the bits of 16-token
+    # pages (the copies take a uniform page per 16 keys for pages of 16 or
+    # more tokens and per-lane pages below, and chunks start inside pages of
+    # 128); prefix hits, a chunk crossing 4096 and ragged lengths.
+    prefix, n = [37, 1000, 4000], [100, 17, 300]
+    lens = [a + b for a, b in zip(prefix, n)]
+    q, cu, p0, kc, vc, bt = synth.paged_prefill_inputs(prefix, n, H=2, D=128, P=16, seed=11)
+    ref = _run(*_dev(q, cu, p0, kc, vc, bt))
+    kc2, vc2, bt2 = _repage(kc, vc, bt, lens, P, seed=100 + P)
+    got = _run(*_dev(q, cu, p0, kc2, vc2, bt2))
+    torch.cuda.synchronize()
+    assert bitwise_equal(got, ref), f"pages of {P} tokens changed the bits"
