@@ -446,7 +446,7 @@ int row_op_launch(int64_t rows, int64_t cols, const void* x, int64_t ldx, const 
     const int64_t rpb = regime < 2 ? 4 : 1;
     const dim3 grid((unsigned)std::min<int64_t>((rows + rpb - 1) / rpb, 1ll << 30));
     launch_kernel(kerns[regime][ib ? 1 : 0][vec ? 1 : 0], grid, dim3(256), 0, st, x, ldx, w, eps, y, ldy, rows,
-                       (int)cols, ob ? 1 : 0);
+                  (int)cols, ob ? 1 : 0);
     return launch_status();
 }
 
@@ -474,8 +474,8 @@ static void decode_paged_launch(dim3 g1, dim3 g2, hipStream_t st, bool uni, cons
                                 float scale, void* out, int64_t BH, int out_dtype) {
     auto kern = uni ? decode_chunk_paged_kernel<D, true> : decode_chunk_paged_kernel<D, false>;
     launch_kernel(kern, g1, dim3(DEC_THREADS), 0, st, (const uint16_t*)q, (const uint16_t*)kc,
-                       (const uint16_t*)vc, bt, max_pages, sl, H, log2p, num_pages, max_seq, maxchunks, (int)BH, wsf,
-                       scale);
+                  (const uint16_t*)vc, bt, max_pages, sl, H, log2p, num_pages, max_seq, maxchunks, (int)BH, wsf,
+                  scale);
     auto merge = out_dtype == BI_BF16 ? decode_merge_kernel<D, 1> : decode_merge_kernel<D, 0>;
     launch_kernel(merge, g2, dim3(256), 0, st, (const float*)wsf, out, BH, maxchunks, sl, H, max_seq);
 }
@@ -624,7 +624,7 @@ int bi_conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, const void* x, int64
         // each workgroup's offset table spread over more pieces)
         const int pgrid = (int)std::min<int64_t>(cdiv(wchunks + uchunks, 256), 16 * cus);
         launch_kernel(conv_prepare_patch16, dim3(pgrid), dim3(256), (size_t)(nchunk * 16), st,
-                           (const uint16_t*)w, (uint16_t*)wp, (const uint16_t*)x, (uint16_t*)u, gp);
+                      (const uint16_t*)w, (uint16_t*)wp, (const uint16_t*)x, (uint16_t*)u, gp);
     } else if (idx32) {
         ConvGeom32 g32;
         g32.N = (int)N; g32.Cin = (int)Cin; g32.H = (int)H; g32.W = (int)W; g32.Cout = (int)Cout;
@@ -634,20 +634,20 @@ int bi_conv2d(int64_t N, int64_t Cin, int64_t H, int64_t W, const void* x, int64
         const int pgrid = (int)std::min<int64_t>(cdiv(wchunks + uchunks, 256), 64 * cus);
         if (in_dtype != BI_F32)
             launch_kernel((conv_prepare32<uint16_t>), dim3(pgrid), dim3(256), 0, st,
-                               (const uint16_t*)w, (uint16_t*)wp, (const uint16_t*)x, (uint16_t*)u, g32);
+                          (const uint16_t*)w, (uint16_t*)wp, (const uint16_t*)x, (uint16_t*)u, g32);
         else
             launch_kernel((conv_prepare32<float>), dim3(pgrid), dim3(256), 0, st,
-                               (const float*)w, (float*)wp, (const float*)x, (float*)u, g32);
+                          (const float*)w, (float*)wp, (const float*)x, (float*)u, g32);
     } else if (in_dtype != BI_F32) {
         launch_kernel((conv_pack_weight<uint16_t>), dim3(wgrid), dim3(256), 0, st,
-                           (const uint16_t*)w, (uint16_t*)wp, g);
+                      (const uint16_t*)w, (uint16_t*)wp, g);
         launch_kernel((conv_unfold<uint16_t>), dim3(ugrid), dim3(256), 0, st,
-                           (const uint16_t*)x, (uint16_t*)u, g);
+                      (const uint16_t*)x, (uint16_t*)u, g);
     } else {
         launch_kernel((conv_pack_weight<float>), dim3(wgrid), dim3(256), 0, st,
-                           (const float*)w, (float*)wp, g);
+                      (const float*)w, (float*)wp, g);
         launch_kernel((conv_unfold<float>), dim3(ugrid), dim3(256), 0, st,
-                           (const float*)x, (float*)u, g);
+                      (const float*)x, (float*)u, g);
     }
     rc = launch_status();
     if (rc != BI_OK) return rc;
@@ -699,12 +699,12 @@ static int decode_launch(int64_t B, int64_t H, int64_t S, int64_t D, const void*
     const int sn = (int)nchunk;
     if (D == 64) {
         launch_kernel((decode_chunk_kernel<64>), g1, dim3(DEC_THREADS), 0, st,
-                           (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, wsf, S, sn, DEC_CHUNK, scale);
+                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, wsf, S, sn, DEC_CHUNK, scale);
         if (out_dtype == BI_BF16) launch_kernel((decode_merge_kernel<64, 1>), g2, dim3(256), 0, st, wsf, out, BH, sn, nullptr, 1, 0);
         else                      launch_kernel((decode_merge_kernel<64, 0>), g2, dim3(256), 0, st, wsf, out, BH, sn, nullptr, 1, 0);
     } else {
         launch_kernel((decode_chunk_kernel<128>), g1, dim3(DEC_THREADS), 0, st,
-                           (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, wsf, S, sn, DEC_CHUNK, scale);
+                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, wsf, S, sn, DEC_CHUNK, scale);
         if (out_dtype == BI_BF16) launch_kernel((decode_merge_kernel<128, 1>), g2, dim3(256), 0, st, wsf, out, BH, sn, nullptr, 1, 0);
         else                      launch_kernel((decode_merge_kernel<128, 0>), g2, dim3(256), 0, st, wsf, out, BH, sn, nullptr, 1, 0);
     }
