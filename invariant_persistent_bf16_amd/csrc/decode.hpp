@@ -31,6 +31,7 @@
 
 #include "common.hpp"
 #include "rowio.hpp"
+#include "wave.hpp"
 
 namespace bi {
 
@@ -207,8 +208,7 @@ __device__ __forceinline__ void decode_chunk_body(const KV& kv, const uint16_t* 
                     acc = fmaf(qf[2 * e], bf16lo_to_f32(kr[b][e]), acc);
                     acc = fmaf(qf[2 * e + 1], bf16hi_to_f32(kr[b][e]), acc);
                 }
-#pragma unroll
-                for (int o = 1; o < LPT; o <<= 1) acc += __shfl_xor(acc, o, 64);
+                acc = xor_sum_steps<1, LPT>(acc);
                 sc[i0 + b] = tg < nv - (i0 + b) * TPI ? acc * scale : -INFINITY;
                 m = fmaxf(m, sc[i0 + b]);
             }
@@ -222,8 +222,7 @@ __device__ __forceinline__ void decode_chunk_body(const KV& kv, const uint16_t* 
 #pragma unroll
         for (int b = 0; b < BATCH; ++b) vr0[b] = kv.v((int)(t0 + (int64_t)b * TPI));
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    m = wave_max(m);
     if (lane == 0) red_m[wave] = m;
     __syncthreads();
     m = red_m[0];
@@ -259,12 +258,9 @@ __device__ __forceinline__ void decode_chunk_body(const KV& kv, const uint16_t* 
         }
     }
     // Fold the token groups of the wave (lane bits above the LPT lanes).
+    l = xor_sum_steps<LPT, 64>(l);
 #pragma unroll
-    for (int off = LPT; off < 64; off <<= 1) {
-        l += __shfl_xor(l, off, 64);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] += __shfl_xor(o[e], off, 64);
-    }
+    for (int e = 0; e < 8; ++e) o[e] = xor_sum_steps<LPT, 64>(o[e]);
     if (lane == 0) red_l[wave] = l;
     if (tg == 0) {
 #pragma unroll

@@ -34,6 +34,7 @@
 
 #include "common.hpp"
 #include "rowio.hpp"
+#include "wave.hpp"
 
 namespace bi {
 
@@ -46,57 +47,6 @@ __device__ __forceinline__ float sm_exp(float y) { return __builtin_amdgcn_exp2f
 __device__ __forceinline__ float sm_div(float x, float s, float y) {
     const float q = x * y;
     return __builtin_fmaf(__builtin_fmaf(-q, s, x), y, q);
-}
-
-// The value of lane l ^ O (O = 1, 2, 4, 8: within a row of 16 lanes) by DPP
-// moves: quad permutations for 1 and 2, a rotation of the row by 8 for 8, and
-// for 4 the half-row mirror (l ^ 7) followed by the quad reversal (l ^ 3).
-template <int O>
-__device__ __forceinline__ float lane_xor(float v) {
-    static_assert(O == 1 || O == 2 || O == 4 || O == 8, "within a row");
-    const int x = __float_as_int(v);
-    if constexpr (O == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));
-    if constexpr (O == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));
-    if constexpr (O == 8) return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false));
-    const int t = __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, t, 0x1B, 0xF, 0xF, false));
-}
-
-// Xor-butterfly over the 64 lanes, offsets 32, 16, ..., 1: at each step a
-// lane combines its value with that of lane l ^ o (every lane ends with the
-// same bits).  Offsets 32 and 16 use v_permlane32_swap / v_permlane16_swap,
-// which leave each lane the pair (own value, partner's value) in some order;
-// the sum and the maximum of a pair do not depend on that order.  The others
-// are DPP moves, so no step goes through the LDS crossbar.
-__device__ __forceinline__ float wave_sum(float x) {
-    {
-        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-        x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    }
-    {
-        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-        x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    }
-    x += lane_xor<8>(x);
-    x += lane_xor<4>(x);
-    x += lane_xor<2>(x);
-    x += lane_xor<1>(x);
-    return x;
-}
-__device__ __forceinline__ float wave_max(float x) {
-    {
-        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-        x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-    }
-    {
-        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-        x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-    }
-    x = fmaxf(x, lane_xor<8>(x));
-    x = fmaxf(x, lane_xor<4>(x));
-    x = fmaxf(x, lane_xor<2>(x));
-    x = fmaxf(x, lane_xor<1>(x));
-    return x;
 }
 
 // NCH > 0: the lane keeps its NCH chunks (4 * NCH values) in registers, so
