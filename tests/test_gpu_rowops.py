@@ -5,7 +5,9 @@ Each is compared with the fp64 oracle on the same seeded inputs across every
 regime of the row length (one wave per row up to 4096 columns, one workgroup
 per row up to 16384, re-reading beyond), with ragged column counts, both input
 dtypes, and at the LLM shapes the bench times on sampled rows.  Invariance:
-row 0 alone gives the same bits as row 0 of a large batch; aligned rows (vector
+row 0 alone gives the same bits as row 0 of a large batch, and with more rows
+than the resident workgroups hold (RMSNorm's waves then loop over rows) every
+sampled row, the last included, equals that row alone; aligned rows (vector
 loads) and the same rows one element off alignment (element loads) give the
 same bits; bfloat16 output is RNE of the binary32 output.  Closed forms:
 RMSNorm of rows of +-2^k with eps = 0 is +-w exactly; the mean of small
@@ -120,3 +122,21 @@ def test_llm_shapes_sampled():
     assert_parity(to64(y[rows]), oracle.rms_norm(x[rows], w, 1e-6), "rms_norm 8192x4096")
     assert_parity(to64(m[rows])[:, None], oracle.mean_rows(x[rows])[:, None], "mean 8192x4096")
     assert_parity(to64(ls[rows]), oracle.log_softmax_rows(lg[rows]), "log_softmax 8192x14336")
+
+
+@pytest.mark.parametrize("rows,cols", [(50001, 256), (9001, 4096), (3, 1000)])
+def test_rms_norm_rows_beyond_one_pass(rows, cols):
+    # More rows than one pass of the resident grid: each wave normalises
+    # several rows in turn.  Sampled rows equal the same row normalised alone,
+    # bit for bit, and match the oracle.
+    x = synth.randn((rows, cols), seed=rows + cols, dtype=torch.bfloat16).to(DEV)
+    w = synth.randn((cols,), seed=7, dtype=torch.bfloat16).to(DEV)
+    y = bi.bi_rms_norm(x, w, 1e-6, out_dtype=bi.BI_F32)
+    gen = np.random.default_rng(rows)
+    pick = sorted({0, rows - 1, *gen.integers(0, rows, 30).tolist()})
+    alone = [bi.bi_rms_norm(x[r:r + 1], w, 1e-6, out_dtype=bi.BI_F32) for r in pick]
+    _sync()
+    for r, a in zip(pick, alone):
+        assert bitwise_equal(y[r:r + 1], a), f"row {r} of {rows} differs from the row alone"
+    idx = torch.tensor(pick)
+    assert_parity(to64(y.cpu()[idx]), oracle.rms_norm(x.cpu()[idx], w.cpu(), 1e-6), f"rms_norm {rows}x{cols} sampled")
