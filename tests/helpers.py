@@ -70,9 +70,8 @@ def assert_bf16_is_rne_of(got_bf16, got_f32, what=""):
 def bitwise_equal(a, b):
     if a.dtype != b.dtype or a.shape != b.shape:
         return False
-    if a.dtype == torch.bfloat16:
-        return torch.equal(a.view(torch.int16), b.view(torch.int16))
-    return torch.equal(a.view(torch.int32), b.view(torch.int32))
+    iv = {2: torch.int16, 4: torch.int32, 8: torch.int64}[a.element_size()]
+    return torch.equal(a.view(iv), b.view(iv))
 
 
 def assert_within_dot_bound(got, ref, mag, K, what=""):

@@ -1,0 +1,115 @@
+"""Seeded random sweep of the 16-bit GEMM across every kernel the tile choice
+can return (through the C ABI).
+
+Batch invariance rests on every kernel giving an element the same bits: each
+kernel runs the same K-ascending chain of 32x32x16 MFMAs per output element
+and adds the bias once after it ("Unmasking the True Culprit ...", section "Why
+This Achieves Batch Invariance"; "Batch-Invariant Kernel Design: Conv2d and
+Attention BMM", section "The two correctness tests").  Each case draws a shape
+(G, M, N, K with K a multiple of 8), the B layout, bfloat16 or binary16
+operands, no bias / a column bias / a row bias, the output dtype and a padded
+output row stride from its seed, forces every kernel with bi_bench_gemm_tile,
+and requires identical bits from all of them; the binary32 output is checked
+against the fp64 oracle on sampled rows of every slice.  Binary32 operands get
+the same treatment over their own kernels, with any K and transposed views.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import assert_parity, bitwise_equal, to64
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from invariant_persistent_bf16_amd import bi, bi_bench
+DEV = "cuda"
+KERNELS = (0, 1, 2, 3, 4, 32, 64, 128)   # persistent 256x256 / 128x256 / 256x128 / 128x128 / 192x256, small tiles
+CASES = 40
+
+
+def _case(seed):
+    rng = np.random.default_rng(7000 + seed)
+    small = rng.integers(0, 4) == 0
+    c = dict(G=int(rng.choice([1, 1, 2, 3])), M=int(rng.integers(1, 12 if small else 700)),
+             K=8 * int(rng.integers(1, 160)), kcontig=bool(rng.integers(0, 2)), f16=bool(rng.integers(0, 4) == 0),
+             bias=str(rng.choice(["none", "col", "row"])), pad=int(rng.choice([0, 0, 8, 40])))
+    c["N"] = int(rng.integers(1, 700)) if c["kcontig"] else 8 * int(rng.integers(1, 88))
+    return c
+
+
+@pytest.mark.parametrize("seed", range(CASES))
+def test_random_shape_every_kernel_same_bits(seed):
+    c = _case(seed)
+    G, M, N, K = c["G"], c["M"], c["N"], c["K"]
+    dt = torch.float16 if c["f16"] else torch.bfloat16
+    od16 = bi.BI_F16 if c["f16"] else bi.BI_BF16
+    A = synth.randn((G, M, K), seed=seed, dtype=dt)
+    if c["kcontig"]:
+        B = synth.randn((G, N, K), seed=seed + 100, dtype=dt, scale=0.05).transpose(1, 2)
+    else:
+        B = synth.randn((G, K, N), seed=seed + 100, dtype=dt, scale=0.05)
+    bias = None if c["bias"] == "none" else synth.randn((M if c["bias"] == "row" else N,), seed=seed + 200,
+                                                        dtype=dt, scale=0.1)
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    bd = None if bias is None else bias.to(DEV)
+    rows = c["bias"] == "row"
+    name = f"seed {seed}: {c}"
+    print(name, flush=True)
+    results = {}
+    for od in (bi.BI_F32, od16):
+        tdt = torch.float32 if od == bi.BI_F32 else dt
+        outs = {}
+        for t in KERNELS:
+            # output rows padded by c["pad"] elements: every kernel writes only the N columns
+            store = torch.full((G, M, N + c["pad"]), -7.0, dtype=tdt, device=DEV)
+            bi_bench.gemm_tile(Ad, Bd, t, bias=bd, bias_rows=rows, out=store[:, :, :N], out_dtype=od)
+            outs[t] = store
+        torch.cuda.synchronize()
+        for t in KERNELS[1:]:
+            assert bitwise_equal(outs[t], outs[0]), f"{name}: kernel {t} differs from 256x256 (out {od})"
+        if c["pad"]:
+            assert torch.all(outs[0][:, :, N:] == -7.0), f"{name}: a write past N"
+        results[od] = outs[0][:, :, :N]
+    # the auto choice is one of the kernels above
+    assert bi_bench.gemm_tile_rows(G, M, N, K, bi.BI_F16 if c["f16"] else bi.BI_BF16) in KERNELS
+    rng = np.random.default_rng(seed)
+    pick = sorted({0, M - 1, *rng.integers(0, M, 6).tolist()})
+    got = results[bi.BI_F32].cpu()
+    for g in range(G):
+        want = oracle.mm(A[g], B[g], bias if c["bias"] == "col" else None, rows=pick)
+        if rows:
+            want = want + bias.double().numpy()[pick][:, None]
+        assert_parity(to64(got[g][pick]), want, f"{name} slice {g}")
+
+
+F32_KERNELS = (0, 32, 16, 17, 18, 19)   # 64x64 and 32x32 tiles; 16x16 blocks with the chains on four waves
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_shape_every_f32_kernel_same_bits(seed):
+    # Binary32 operands: any K, each operand plain or a transposed view, the
+    # same bits from every kernel (16 .. 19: the split-chain blocks with each
+    # operand staged through LDS or loaded directly).
+    rng = np.random.default_rng(9000 + seed)
+    G, M, N = int(rng.choice([1, 2])), int(rng.integers(1, 400)), int(rng.integers(1, 400))
+    K = int(rng.integers(1, 2100))
+    at, bt = bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
+    A = (synth.randn((G, K, M), seed=seed, dtype=torch.float32).transpose(1, 2) if at
+         else synth.randn((G, M, K), seed=seed, dtype=torch.float32))
+    B = (synth.randn((G, N, K), seed=seed + 50, dtype=torch.float32, scale=0.05).transpose(1, 2) if bt
+         else synth.randn((G, K, N), seed=seed + 50, dtype=torch.float32, scale=0.05))
+    bias = synth.randn((N,), seed=seed + 60, dtype=torch.float32, scale=0.02)
+    Ad, Bd, bd = A.to(DEV), B.to(DEV), bias.to(DEV)
+    name = f"seed {seed}: G={G} M={M} N={N} K={K} A^T={at} B^T={bt}"
+    print(name, flush=True)
+    outs = {t: bi_bench.gemm_tile(Ad, Bd, t, bias=bd, out_dtype=bi.BI_F32) for t in F32_KERNELS}
+    torch.cuda.synchronize()
+    for t in F32_KERNELS[1:]:
+        assert bitwise_equal(outs[t], outs[0]), f"{name}: kernel {t} differs from the 64x64 tiles"
+    pick = sorted({0, M - 1, *rng.integers(0, M, 6).tolist()})
+    got = outs[0].cpu()
+    for g in range(G):
+        assert_parity(to64(got[g][pick]), oracle.mm(A[g], B[g], bias, rows=pick), f"{name} slice {g}")
