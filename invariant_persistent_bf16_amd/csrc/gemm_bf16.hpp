@@ -28,20 +28,25 @@
 // 256x256 tiles would leave compute units idle, and 256x128 (each wave
 // 128x64) for N <= 128; the description
 // below is of the 256x256 tile, the others scale the copy counts, LDS rows
-// and fragment counts with the shape and spread their reads and copies evenly
-// over the step's MFMAs.  K advances in steps of 32 through a
+// and fragment counts with the shape.  K advances in steps of 32 through a
 // 4-stage LDS ring (4 x (16 + 16) KiB): operand tiles are copied HBM -> LDS by
 // buffer_load_dwordx4 ... lds (no staging registers; a lane whose 16 bytes
 // fall outside the operand gets an out-of-range offset and the hardware
-// writes zeros), three steps ahead of their use, so the copy latency is
-// covered by three steps of MFMA work.  The fragments of step k+1 are read
-// from LDS into a second register set while the 32 MFMAs of step k run
-// (explicit one-to-one interleave), so each step waits only for a copy issued
-// three steps earlier.
-//   * A, and a K-contiguous B: LDS rows of 64 bytes (32 K values of one M row
-//     or N column); the four 16-byte chunks of row r sit at chunk c ^ f(r),
-//     f(r) = (r >> 2) & 3, so 16 lanes reading 16 consecutive rows hit 16
-//     distinct 16-byte bank groups.  Fragments are ds_read_b128.
+// writes zeros) two to four steps ahead of their use, and the fragments of
+// step k+1 are read from LDS into a second register set while the 32 MFMAs
+// of step k run; the reads and copies of a step are spread evenly over its
+// MFMAs.
+//   * A: stages 0-1 and 2-3 form two double stages with LDS rows of 128
+//     bytes (64 K values: the pair's two steps), filled by copies of 8 rows x
+//     128 bytes issued at every other step, so each copy request covers whole
+//     128-byte lines of A (16 rows x 64 bytes per copy ran 3-8 % slower on
+//     MI355X, most where A streams from HBM).  The eight 16-byte chunks of
+//     row r sit at chunk c ^ f2(r), f2(r) = (r >> 1) & 7, so 16 lanes reading
+//     16 consecutive rows hit 16 distinct 16-byte bank groups.  Fragments
+//     are ds_read_b128.
+//   * a K-contiguous B: LDS rows of 64 bytes (32 K values of one N column)
+//     per stage; the four 16-byte chunks of row r sit at chunk c ^ f(r),
+//     f(r) = (r >> 2) & 3, for the same reason.  Fragments are ds_read_b128.
 //   * an N-contiguous B (a [K, N] weight): LDS rows of 512 bytes (256 N values
 //     of one K row), chunk c of row k at c ^ 4(k & 3).  Fragments are built by
 //     two ds_read_b64_tr_b16 (gfx950's transposing LDS read: within a group of
@@ -94,9 +99,8 @@ struct G16Cfg {
     // does not depend on it (ONE_PER_CU = false, a test-only variant, runs
     // two workgroups per unit and gives the same bits).
     static constexpr int LDS = (ONE_PER_CU && RING + BIAS < 81 * 1024) ? 81 * 1024 : RING + BIAS;
-    static constexpr int NA = BM / 64;                          // A copies per wave and step
+    static constexpr int NA = BM / 64;                          // A copies per wave and step (on average)
     static constexpr int NB = BN / 64;                          // B copies per wave and step
-    static constexpr int NDMA = NA + NB;
     static constexpr int NMF = 2 * IM * IN;                     // MFMAs per wave and step
     static constexpr int RB = BN * 2;                           // bytes of an N-contiguous B row in LDS
     static constexpr int LPR = RB / 16;                         // lanes per such row in one copy
@@ -154,25 +158,6 @@ template <int V>
 __device__ __forceinline__ void g16_wait_vm_lgkm0() {
     __builtin_amdgcn_s_waitcnt((V & 15) | (7 << 4) | ((V >> 4) << 14));
 }
-// The memory instruction issued after MFMA i of a step: r (0..31) = LDS
-// fragment read r, 32 + j = copy j, -1 = none.  The copies are spread over
-// the step (one after every fourth MFMA) so that the four waves' copies do
-// not reach the texture path in one burst.
-#ifndef G16_SLOT_PATTERN
-#define G16_SLOT_PATTERN 1
-#endif
-template <bool B_KCONTIG>
-constexpr int g16_slot(int i) {
-    const int nread = B_KCONTIG ? 16 : 24;
-    if (G16_SLOT_PATTERN == 0) return i < nread ? i : (i - nread < 8 ? 32 + i - nread : -1);
-    if (G16_SLOT_PATTERN == 1) {
-        if (!B_KCONTIG) return i % 4 == 3 ? 32 + i / 4 : i - i / 4;
-        return i % 4 == 2 ? 32 + i / 4 : (i % 4 < 2 ? 2 * (i / 4) + i % 4 : -1);
-    }
-    if (!B_KCONTIG) return i % 4 == 0 ? 32 + i / 4 : i - i / 4 - 1;
-    return i % 4 == 0 ? 32 + i / 4 : (i % 4 < 3 ? 2 * (i / 4) + i % 4 - 1 : -1);
-}
-
 template <int I, int N, typename F>
 __device__ __forceinline__ void g16_static_for(F&& f) {
     if constexpr (I < N) {
@@ -226,18 +211,24 @@ gemm_bf16_persistent(GemmParams p) {
         int lane_t = lane;
         asm volatile("" : "+v"(lane_t));
         const int tid_t = wave * 64 + lane_t;
-        // ---- per-lane LDS fragment addresses (stage 0; stages add 16 KiB each)
-        //  A row r = R0 + 32 im, R0 = 128 wm + lane%32: f(r) = f(R0), so chunk
-        //  (2kk + lane/32) ^ f(r) = x ^ 2kk with x = lane/32 ^ f(R0).
+        // ---- per-lane LDS fragment addresses
+        //  A (double stage 0; the second adds 2 A_STAGE): row r = R0 + 32 im,
+        //  R0 = WROWS wm + lane%32, f2(r) = f2(R0); the step's half h of the
+        //  row, chunk (4h + 2kk + lane/32) ^ f2(r) = x ^ 2kk ^ 4h with
+        //  x = lane/32 ^ f2(R0).
+        //  K-contiguous B (stage 0; stages add B_STAGE): the same with 64-byte
+        //  rows and f(r).
         //  N-contiguous B: K row kk*16 + 8(g/2) + 4hr + z (z = li/4, k&3 = z),
         //  chunk (16wn + 4in + y) ^ 4z = 16wn + 4(in ^ z) + y.
         const uint32_t lds0 = g16_lds_addr(smem);
-        uint32_t a_fb[2], b_fb[4];
+        uint32_t a_fb[2][2], b_fb[4];
         {
             const int R0 = wm * C::WROWS + (lane_t & 31);
-            const int x = (lane_t >> 5) ^ ((R0 >> 2) & 3);
+            const int x = (lane_t >> 5) ^ ((R0 >> 1) & 7);
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) a_fb[kk] = lds0 + R0 * 64 + ((x ^ (2 * kk)) << 4);
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) a_fb[h][kk] = lds0 + R0 * 128 + ((x ^ (2 * kk) ^ (4 * h)) << 4);
             if constexpr (B_KCONTIG) {
                 const int N0 = wn * C::WCOLS + (lane_t & 31);
                 const int xb = (lane_t >> 5) ^ ((N0 >> 2) & 3);
@@ -273,21 +264,20 @@ gemm_bf16_persistent(GemmParams p) {
         // base, fixed for the tile (out-of-range rows already turned into the
         // zero-reading offset); each K step adds a uniform byte offset through
         // the instruction's scalar offset.  The host bounds every offset below 2^31.
-        // A (and K-contiguous B): wave w, copy j covers LDS rows 64w + 16j + lane/4;
-        // the lane writes physical chunk lane&3, i.e. logical chunk
+        // A: wave w, copy j (0 .. 2NA-1) of a pair covers double-stage rows
+        // (BM/4) w + 8j + lane/8; the lane writes physical chunk lane&7, i.e.
+        // logical chunk (lane&7) ^ f2(row) = (lane&7) ^ (lane>>4) ^ 4(j&1)
+        // (BM/4 is a multiple of 16).
+        // K-contiguous B: copy j covers LDS rows (BN/4) w + 16j + lane/4; the
+        // lane writes physical chunk lane&3, i.e. logical chunk
         // (lane&3) ^ f(row) = (lane&3) ^ ((lane>>4)&3).
         // N-contiguous B: copy j covers K rows 8w + 2j + lane/32; the lane writes
         // physical chunk lane&31 of that row, i.e. logical chunk
         // (lane&31) ^ 4(krow&3), columns clamped to the last valid 8.
         const int a_u = (lane_t & 3) ^ ((lane_t >> 4) & 3);
-        const int a_row0 = (BM / 4) * wave + (lane_t >> 2);
         const int b_row0 = (BN / 4) * wave + (lane_t >> 2);
-        uint32_t a_off[C::NA], b_off[C::NB];
+        uint32_t a_off[2 * C::NA], b_off[C::NB];
         {
-            const int64_t a_rows_left = p.M - m0 - a_row0;
-#pragma unroll
-            for (int j = 0; j < C::NA; ++j)
-                a_off[j] = a_rows_left > 16 * j ? (uint32_t)(((a_row0 + 16 * j) * (int)p.sAm + a_u * 8) * 2) : G16_OOB;
             if constexpr (B_KCONTIG) {
                 const int64_t b_rows_left = p.N - n0 - b_row0;
 #pragma unroll
@@ -303,25 +293,38 @@ gemm_bf16_persistent(GemmParams p) {
                 }
             }
         }
-        const int a_u8 = a_u * 8;
+        const int b_u8 = a_u * 8;
+        const int a_row0 = (BM / 4) * wave + (lane_t >> 3);
+        const int a_u8 = ((lane_t & 7) ^ (lane_t >> 4)) * 8;   // first K of the lane's chunk, even j (odd: ^ 32)
+        {
+            const int64_t a_rows_left = p.M - m0 - a_row0;
+#pragma unroll
+            for (int j = 0; j < 2 * C::NA; ++j)
+                a_off[j] = a_rows_left > 8 * j ? (uint32_t)(((a_row0 + 8 * j) * (int)p.sAm + (a_u8 ^ (32 * (j & 1)))) * 2)
+                                               : G16_OOB;
+        }
         const int bn_krow0 = 8 * wave + lane_t / C::LPR;
         const __amdgpu_buffer_rsrc_t rsA = g16_rsrc(Ab), rsB = g16_rsrc(Bb);
         const uint32_t kstepB = B_KCONTIG ? 2u * G16_BK : (uint32_t)(2 * G16_BK * p.sBk);
 
-        // DMA copy j (0 .. NA-1 for A, NA .. NA+NB-1 for B) of K tile kt into
-        // stage st; lanes past K read zeros.
-        auto dma = [&](int kt, int st, auto jc) {
-            constexpr int j = decltype(jc)::value, jb = j - C::NA;
+        // A copy j (0 .. 2NA-1) of the K steps kt, kt+1 into the double stage
+        // at stage st (even); lanes past K read zeros.
+        auto dma_a = [&](int kt, int st, auto jc) {
+            constexpr int j = decltype(jc)::value;
             const int kleft = K32 - kt * G16_BK;
-            if constexpr (j < C::NA) {
-                g16_dma(rsA, smem + st * C::A_STAGE + (wave * C::NA + j) * 1024,
-                        a_u8 < kleft ? a_off[j] : G16_OOB, (uint32_t)kt * (2u * G16_BK));
-            } else if constexpr (B_KCONTIG) {
-                g16_dma(rsB, smem + C::B_BASE + st * C::B_STAGE + (wave * C::NB + jb) * 1024,
-                        a_u8 < kleft ? b_off[jb] : G16_OOB, (uint32_t)kt * kstepB);
+            g16_dma(rsA, smem + st * C::A_STAGE + (wave * 2 * C::NA + j) * 1024,
+                    (a_u8 ^ (32 * (j & 1))) < kleft ? a_off[j] : G16_OOB, (uint32_t)kt * (2u * G16_BK));
+        };
+        // B copy j (0 .. NB-1) of K step kt into stage st.
+        auto dma_b = [&](int kt, int st, auto jc) {
+            constexpr int j = decltype(jc)::value;
+            const int kleft = K32 - kt * G16_BK;
+            if constexpr (B_KCONTIG) {
+                g16_dma(rsB, smem + C::B_BASE + st * C::B_STAGE + (wave * C::NB + j) * 1024,
+                        b_u8 < kleft ? b_off[j] : G16_OOB, (uint32_t)kt * kstepB);
             } else {
-                g16_dma(rsB, smem + C::B_BASE + st * C::B_STAGE + (wave * C::NB + jb) * 1024,
-                        bn_krow0 + (1024 / C::RB) * jb < kleft ? b_off[jb] : G16_OOB, (uint32_t)kt * kstepB);
+                g16_dma(rsB, smem + C::B_BASE + st * C::B_STAGE + (wave * C::NB + j) * 1024,
+                        bn_krow0 + (1024 / C::RB) * j < kleft ? b_off[j] : G16_OOB, (uint32_t)kt * kstepB);
             }
         };
         // LDS read r of the fragments of stage ST into F: 0 .. 2IM-1 A
@@ -331,7 +334,7 @@ gemm_bf16_persistent(GemmParams p) {
             constexpr int ST = decltype(stc)::value, r = decltype(rc)::value;
             if constexpr (r < 2 * IM) {
                 constexpr int kk = r / IM, im = r % IM;
-                F.a[kk][im] = g16_read128<ST * C::A_STAGE + im * 2048>(a_fb[kk]);
+                F.a[kk][im] = g16_read128<(ST >> 1) * 2 * C::A_STAGE + im * 4096>(a_fb[ST & 1][kk]);
             } else if constexpr (B_KCONTIG) {
                 if constexpr (r < 2 * IM + 2 * IN) {
                     constexpr int kk = (r - 2 * IM) / IN, in = (r - 2 * IM) % IN;
@@ -386,19 +389,28 @@ gemm_bf16_persistent(GemmParams p) {
         G16Frags F0, F1;
         constexpr int NREAD = 2 * IM + (B_KCONTIG ? 2 : 4) * IN;
 
-        // One K step kt (stage ST = kt % 4): wait for step kt+1's copy and for
-        // the reads of step kt's fragments, barrier, then 32 MFMAs on
-        // step kt's fragments, each followed by one memory instruction: first
-        // the LDS reads of step kt+1's fragments, then the 8 copies of step
-        // kt+4 into stage ST (its data now lives in registers).  Copies and reads past
-        // the last step are harmless (zeros into an unused stage, reads of an
-        // unused stage) and keep the step a single straight-line block.
+        // One K step kt (stage ST = kt % 4): wait for step kt+1's copies and
+        // for the reads of step kt's fragments, barrier, then the MFMAs on
+        // step kt's fragments with the step's memory instructions spread
+        // between them: the LDS reads of step kt+1's fragments, B's copies of
+        // step kt+4 into stage ST (its data now lives in registers) and, at
+        // odd stages, A's copies of the pair kt+3, kt+4 into the double stage
+        // ST-1, ST (step kt+3's half was read before the previous barrier).
+        // A wave's copies, in issue order: at step j the A pair (j+3, j+4) if
+        // j is odd, then B of step j+4.  Step kt+1's data is complete once
+        // the copies issued after its last one are all that is outstanding:
+        // for odd kt, B of step kt+2 and kt+3 (2 NB copies, its A pair came at
+        // step kt-2); for even kt, also the pair issued at step kt-1 (its A
+        // and B came at step kt-3).  Copies and reads past the last step are
+        // harmless (zeros into an unused stage, reads of an unused stage) and
+        // keep the step a single straight-line block.
         auto step = [&](int kt, auto stc, auto firstc) {
             constexpr int ST = decltype(stc)::value;
             constexpr bool FIRST = decltype(firstc)::value;
             G16Frags& cur = (ST & 1) ? F1 : F0;
             G16Frags& nxt = (ST & 1) ? F0 : F1;
-            g16_wait_vm_lgkm0<2 * C::NDMA>();
+            if constexpr (ST & 1) g16_wait_vm_lgkm0<2 * C::NB>();
+            else                  g16_wait_vm_lgkm0<2 * C::NB + 2 * C::NA>();
             __builtin_amdgcn_s_barrier();
             fence_frags(cur);
             __builtin_amdgcn_sched_barrier(0);
@@ -413,36 +425,38 @@ gemm_bf16_persistent(GemmParams p) {
                 else
                     acc[im][in] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         as_bf16x8(cur.b[kk][in]), as_bf16x8(cur.a[kk][im]), c_in, 0, 0, 0);
-                if constexpr (BM == 256 && BN == 256) {
-                    constexpr int slot = g16_slot<B_KCONTIG>(i);
-                    if constexpr (slot >= 0 && slot < 32) {
-                        lds_read(nxt, std::integral_constant<int, (ST + 1) % 4>{}, std::integral_constant<int, slot>{});
-                    } else if constexpr (slot >= 32) {
-                        dma(kt + 4, ST, std::integral_constant<int, slot - 32>{});
+                // Read r after MFMA r * NMF / NREAD, copy d after
+                // (2d + 1) NMF / (2 NC): A copies (odd stages) first, then B.
+                g16_static_for<0, NREAD>([&](auto rc) {
+                    constexpr int r = decltype(rc)::value;
+                    if constexpr (r * C::NMF / NREAD == i)
+                        lds_read(nxt, std::integral_constant<int, (ST + 1) % 4>{}, rc);
+                });
+                constexpr int NCA = (ST & 1) ? 2 * C::NA : 0, NC = NCA + C::NB;
+                g16_static_for<0, NC>([&](auto dc) {
+                    constexpr int d = decltype(dc)::value;
+                    if constexpr ((2 * d + 1) * C::NMF / (2 * NC) == i) {
+                        if constexpr (d < NCA) dma_a(kt + 3, ST - 1, dc);
+                        else                   dma_b(kt + 4, ST, std::integral_constant<int, d - NCA>{});
                     }
-                } else {
-                    // Reads and copies spread evenly over the step's MFMAs: read r
-                    // after MFMA r * NMF / NREAD, copy d after (2d + 1) NMF / (2 NDMA).
-                    g16_static_for<0, NREAD>([&](auto rc) {
-                        constexpr int r = decltype(rc)::value;
-                        if constexpr (r * C::NMF / NREAD == i)
-                            lds_read(nxt, std::integral_constant<int, (ST + 1) % 4>{}, rc);
-                    });
-                    g16_static_for<0, C::NDMA>([&](auto dc) {
-                        constexpr int d = decltype(dc)::value;
-                        if constexpr ((2 * d + 1) * C::NMF / (2 * C::NDMA) == i) dma(kt + 4, ST, dc);
-                    });
-                }
+                });
                 __builtin_amdgcn_sched_barrier(0);
             });
         };
 
-        // Prologue: copies of steps 0..3 into stages 0..3, wait for step 0,
-        // read its fragments.
-        g16_static_for<0, 4>([&](auto sc) {
-            g16_static_for<0, C::NDMA>([&](auto jc) { dma(decltype(sc)::value, decltype(sc)::value, jc); });
-        });
-        g16_wait_vm_lgkm0<3 * C::NDMA>();
+        // Prologue: the copies of steps 0..3 in the steady state's order (as
+        // if issued by steps -4 .. -1: B0, A pair (0, 1), B1, B2, A pair
+        // (2, 3), B3), wait for step 0's, read its fragments.
+        auto dma_b_all = [&](auto sc) {
+            g16_static_for<0, C::NB>([&](auto jc) { dma_b(decltype(sc)::value, decltype(sc)::value, jc); });
+        };
+        dma_b_all(std::integral_constant<int, 0>{});
+        g16_static_for<0, 2 * C::NA>([&](auto jc) { dma_a(0, 0, jc); });
+        dma_b_all(std::integral_constant<int, 1>{});
+        dma_b_all(std::integral_constant<int, 2>{});
+        g16_static_for<0, 2 * C::NA>([&](auto jc) { dma_a(2, 2, jc); });
+        dma_b_all(std::integral_constant<int, 3>{});
+        g16_wait_vm_lgkm0<3 * C::NB + 2 * C::NA>();
         __builtin_amdgcn_s_barrier();
         g16_static_for<0, NREAD>([&](auto rc) { lds_read(F0, std::integral_constant<int, 0>{}, rc); });
 
