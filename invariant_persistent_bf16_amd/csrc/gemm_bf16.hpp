@@ -44,11 +44,14 @@
 //     row r sit at chunk c ^ f2(r), f2(r) = (r >> 1) & 7, so 16 lanes reading
 //     16 consecutive rows hit 16 distinct 16-byte bank groups.  Fragments
 //     are ds_read_b128.
-//   * a K-contiguous B: the same 128-byte rows and swizzle, in double stages
-//     that pair the steps the other way (stages 1-2 and 3-0: B's stages sit
-//     in the slot order 1, 2, 3, 0), filled at the even steps, so that every
-//     step issues one pair of copies, of A or of B (convolution GEMM 3 %
-//     faster than with 64-byte B rows).
+//   * a K-contiguous B, on the 256x256 and 192x256 tiles: the same 128-byte
+//     rows and swizzle, in double stages that pair the steps the other way
+//     (stages 1-2 and 3-0: B's stages sit in the slot order 1, 2, 3, 0),
+//     filled at the even steps, so that every step issues one pair of
+//     copies, of A or of B (convolution GEMM 3 % faster than with 64-byte B
+//     rows).  On the other tiles: LDS rows of 64 bytes (32 K values of one N
+//     column) per stage, copied one step at a time, the four 16-byte chunks
+//     of row r at chunk c ^ f(r), f(r) = (r >> 2) & 3.
 //   * an N-contiguous B (a [K, N] weight): LDS rows of 512 bytes (256 N values
 //     of one K row), chunk c of row k at c ^ 4(k & 3).  Fragments are built by
 //     two ds_read_b64_tr_b16 (gfx950's transposing LDS read: within a group of
@@ -188,6 +191,12 @@ __global__ void __launch_bounds__(G16_THREADS, 1)
 gemm_bf16_persistent(GemmParams p) {
     using C = G16Cfg<BM, BN, ONE_PER_CU>;
     constexpr int IM = C::IM, IN = C::IN;
+    // A K-contiguous B is copied in pairs of K steps on the 256-wide tiles of
+    // 192 or 256 rows; on the smaller tiles, where B is the larger share of a
+    // step's bytes, the shallower queue of the pairs cost more than the
+    // whole lines gained (128x128 tiles at M = 200, K = 4096: 37.8 -> 43.3
+    // us), and B is copied one step at a time in 64-byte rows.
+    constexpr bool BP = B_KCONTIG && BN == 256 && BM >= 192;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
 
     const int tid = threadIdx.x;
@@ -218,8 +227,9 @@ gemm_bf16_persistent(GemmParams p) {
         //  R0 = WROWS wm + lane%32, f2(r) = f2(R0); the step's half h of the
         //  row, chunk (4h + 2kk + lane/32) ^ f2(r) = x ^ 2kk ^ 4h with
         //  x = lane/32 ^ f2(R0).
-        //  K-contiguous B: the same in B's double stages (slot (s + 3) & 3 of
-        //  stage s; slots 2p, 2p + 1 form double stage p).
+        //  K-contiguous B in pairs: the same in B's double stages (slot
+        //  (s + 3) & 3 of stage s; slots 2p, 2p + 1 form double stage p); one
+        //  step at a time: 64-byte rows and f(r) (stage 0; stages add B_STAGE).
         //  N-contiguous B: K row kk*16 + 8(g/2) + 4hr + z (z = li/4, k&3 = z),
         //  chunk (16wn + 4in + y) ^ 4z = 16wn + 4(in ^ z) + y.
         const uint32_t lds0 = g16_lds_addr(smem);
@@ -231,7 +241,7 @@ gemm_bf16_persistent(GemmParams p) {
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) a_fb[h][kk] = lds0 + R0 * 128 + ((x ^ (2 * kk) ^ (4 * h)) << 4);
-            if constexpr (B_KCONTIG) {
+            if constexpr (BP) {
                 const int N0 = wn * C::WCOLS + (lane_t & 31);
                 const int xb = (lane_t >> 5) ^ ((N0 >> 1) & 7);
 #pragma unroll
@@ -239,6 +249,12 @@ gemm_bf16_persistent(GemmParams p) {
 #pragma unroll
                     for (int kk = 0; kk < 2; ++kk)
                         b_fb[2 * h + kk] = lds0 + C::B_BASE + N0 * 128 + ((xb ^ (2 * kk) ^ (4 * h)) << 4);
+            } else if constexpr (B_KCONTIG) {
+                const int N0 = wn * C::WCOLS + (lane_t & 31);
+                const int xb = (lane_t >> 5) ^ ((N0 >> 2) & 3);
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) b_fb[kk] = lds0 + C::B_BASE + N0 * 64 + ((xb ^ (2 * kk)) << 4);
+                b_fb[2] = b_fb[3] = 0;
             } else {
                 const int g = lane_t >> 4, li = lane_t & 15, z = li >> 2;
                 const int y = 2 * (g & 1) + ((li & 3) >> 1);
@@ -272,20 +288,30 @@ gemm_bf16_persistent(GemmParams p) {
         // (BM/4) w + 8j + lane/8; the lane writes physical chunk lane&7, i.e.
         // logical chunk (lane&7) ^ f2(row) = (lane&7) ^ (lane>>4) ^ 4(j&1)
         // (BM/4 is a multiple of 16).
-        // K-contiguous B: the same as A, with BN for BM.
+        // K-contiguous B in pairs: the same as A, with BN for BM.  One step at
+        // a time: copy j covers LDS rows (BN/4) w + 16j + lane/4; the lane
+        // writes physical chunk lane&3, i.e. logical chunk
+        // (lane&3) ^ f(row) = (lane&3) ^ ((lane>>4)&3).
         // N-contiguous B: copy j covers K rows 8w + 2j + lane/32; the lane writes
         // physical chunk lane&31 of that row, i.e. logical chunk
         // (lane&31) ^ 4(krow&3), columns clamped to the last valid 8.
-        uint32_t a_off[2 * C::NA], b_off[B_KCONTIG ? 2 * C::NB : C::NB];
+        uint32_t a_off[2 * C::NA], b_off[BP ? 2 * C::NB : C::NB];
+        const int b_u8 = ((lane_t & 3) ^ ((lane_t >> 4) & 3)) * 8;   // one-step K-contiguous B copies
         const int u8 = ((lane_t & 7) ^ (lane_t >> 4)) * 8;   // first K of a paired copy's lane chunk, even j (odd: ^ 32)
         {
-            if constexpr (B_KCONTIG) {
+            if constexpr (BP) {
                 const int b_row0 = (BN / 4) * wave + (lane_t >> 3);
                 const int64_t b_rows_left = p.N - n0 - b_row0;
 #pragma unroll
                 for (int j = 0; j < 2 * C::NB; ++j)
                     b_off[j] = b_rows_left > 8 * j ? (uint32_t)(((b_row0 + 8 * j) * (int)p.sBn + (u8 ^ (32 * (j & 1)))) * 2)
                                                    : G16_OOB;
+            } else if constexpr (B_KCONTIG) {
+                const int b_row0 = (BN / 4) * wave + (lane_t >> 2);
+                const int64_t b_rows_left = p.N - n0 - b_row0;
+#pragma unroll
+                for (int j = 0; j < C::NB; ++j)
+                    b_off[j] = b_rows_left > 16 * j ? (uint32_t)(((b_row0 + 16 * j) * (int)p.sBn + b_u8) * 2) : G16_OOB;
             } else {
                 const int ncl = (int)min<int64_t>(p.N - 8 - n0, BN - 8);
 #pragma unroll
@@ -316,12 +342,16 @@ gemm_bf16_persistent(GemmParams p) {
             g16_dma(rsA, smem + st * C::A_STAGE + (wave * 2 * C::NA + j) * 1024,
                     (u8 ^ (32 * (j & 1))) < kleft ? a_off[j] : G16_OOB, (uint32_t)kt * (2u * G16_BK));
         };
-        // N-contiguous B: copy j (0 .. NB-1) of K step kt into stage st.
+        // B copied one step at a time: copy j (0 .. NB-1) of K step kt into stage st.
         auto dma_b = [&](int kt, int st, auto jc) {
             constexpr int j = decltype(jc)::value;
             const int kleft = K32 - kt * G16_BK;
-            g16_dma(rsB, smem + C::B_BASE + st * C::B_STAGE + (wave * C::NB + j) * 1024,
-                    bn_krow0 + (1024 / C::RB) * j < kleft ? b_off[j] : G16_OOB, (uint32_t)kt * kstepB);
+            if constexpr (B_KCONTIG)
+                g16_dma(rsB, smem + C::B_BASE + st * C::B_STAGE + (wave * C::NB + j) * 1024,
+                        b_u8 < kleft ? b_off[j] : G16_OOB, (uint32_t)kt * kstepB);
+            else
+                g16_dma(rsB, smem + C::B_BASE + st * C::B_STAGE + (wave * C::NB + j) * 1024,
+                        bn_krow0 + (1024 / C::RB) * j < kleft ? b_off[j] : G16_OOB, (uint32_t)kt * kstepB);
         };
         // K-contiguous B: copy j (0 .. 2NB-1) of the pair of K steps kt, kt+1
         // (kt odd) into B's double stage `pair`.  B's stages sit in the slot
@@ -352,7 +382,10 @@ gemm_bf16_persistent(GemmParams p) {
             } else if constexpr (B_KCONTIG) {
                 if constexpr (r < 2 * IM + 2 * IN) {
                     constexpr int kk = (r - 2 * IM) / IN, in = (r - 2 * IM) % IN, slot = (ST + 3) & 3;
-                    F.b[kk][in] = g16_read128<(slot >> 1) * 2 * C::B_STAGE + in * 4096>(b_fb[2 * (slot & 1) + kk]);
+                    if constexpr (BP)
+                        F.b[kk][in] = g16_read128<(slot >> 1) * 2 * C::B_STAGE + in * 4096>(b_fb[2 * (slot & 1) + kk]);
+                    else
+                        F.b[kk][in] = g16_read128<ST * C::B_STAGE + in * 2048>(b_fb[kk]);
                 }
             } else {
                 constexpr int q = r - 2 * IM, kk = q / (2 * IN), in = (q % (2 * IN)) / 2, hr = q % 2;
@@ -410,16 +443,17 @@ gemm_bf16_persistent(GemmParams p) {
         // A's copies of the pair kt+3, kt+4 into the double stage ST-1, ST
         // (step kt+3's half was read before the previous barrier); an
         // N-contiguous B's copies of step kt+4 into stage ST (its data now
-        // lives in registers) at every stage, or at even stages a K-contiguous
-        // B's pair kt+3, kt+4 into its stages ST-1, ST.
+        // lives in registers) at every stage (a K-contiguous B on the smaller
+        // tiles likewise), or at even stages a paired B's pair kt+3, kt+4
+        // into its stages ST-1, ST.
         // A wave's copies, in issue order: at step j the A pair (j+3, j+4) if
-        // j is odd, then an N-contiguous B's copies of step j+4, or a
-        // K-contiguous B's pair (j+3, j+4) if j is even.  Step kt+1's data is
+        // j is odd, then B's copies of step j+4, or, for a paired B, its
+        // pair (j+3, j+4) if j is even.  Step kt+1's data is
         // complete once the copies issued after its last one are all that is
         // outstanding: for odd kt, B's copies of steps kt+2 and kt+3, or B's
         // pair issued at step kt-1 (2 NB copies; the A pair came at step
         // kt-2); for even kt, the A pair issued at step kt-1 and, with an
-        // N-contiguous B, B's copies of kt+2 and kt+3 (2 NA or 2 NB + 2 NA;
+        // B copied one step at a time, B's copies of kt+2 and kt+3 (2 NA or 2 NB + 2 NA;
         // the A pair came at step kt-3).  Copies and reads past the last step are
         // harmless (zeros into an unused stage, reads of an unused stage) and
         // keep the step a single straight-line block.
@@ -429,7 +463,7 @@ gemm_bf16_persistent(GemmParams p) {
             G16Frags& cur = (ST & 1) ? F1 : F0;
             G16Frags& nxt = (ST & 1) ? F0 : F1;
             if constexpr (ST & 1)          g16_wait_vm_lgkm0<2 * C::NB>();
-            else if constexpr (B_KCONTIG) g16_wait_vm_lgkm0<2 * C::NA>();
+            else if constexpr (BP)        g16_wait_vm_lgkm0<2 * C::NA>();
             else                          g16_wait_vm_lgkm0<2 * C::NB + 2 * C::NA>();
             __builtin_amdgcn_s_barrier();
             fence_frags(cur);
@@ -456,13 +490,13 @@ gemm_bf16_persistent(GemmParams p) {
                         lds_read(nxt, std::integral_constant<int, (ST + 1) % 4>{}, rc);
                 });
                 constexpr int NCA = (ST & 1) ? 2 * C::NA : 0;
-                constexpr int NCB = B_KCONTIG ? ((ST & 1) ? 0 : 2 * C::NB) : C::NB;
+                constexpr int NCB = BP ? ((ST & 1) ? 0 : 2 * C::NB) : C::NB;
                 constexpr int NC = NCA + NCB;
                 g16_static_for<0, NC>([&](auto dc) {
                     constexpr int d = decltype(dc)::value;
                     if constexpr ((2 * d + 1) * C::NMF / (2 * NC) == i) {
                         if constexpr (d < NCA)       dma_a(kt + 3, ST - 1, dc);
-                        else if constexpr (B_KCONTIG) dma_bp(kt + 3, 1 - ST / 2, std::integral_constant<int, d - NCA>{});
+                        else if constexpr (BP)        dma_bp(kt + 3, 1 - ST / 2, std::integral_constant<int, d - NCA>{});
                         else                          dma_b(kt + 4, ST, std::integral_constant<int, d - NCA>{});
                     }
                 });
@@ -472,10 +506,10 @@ gemm_bf16_persistent(GemmParams p) {
 
         // Prologue: the copies of steps 0..3 in the steady state's order (as
         // if issued by steps -4 .. -1), wait for step 0's, read its
-        // fragments.  N-contiguous B: B0, A pair (0, 1), B1, B2, A pair
-        // (2, 3), B3.  K-contiguous B: B pair (-1, 0), A pair (0, 1), B pair
+        // fragments.  B one step at a time: B0, A pair (0, 1), B1, B2, A pair
+        // (2, 3), B3.  Paired B: B pair (-1, 0), A pair (0, 1), B pair
         // (1, 2), A pair (2, 3).
-        if constexpr (B_KCONTIG) {
+        if constexpr (BP) {
             g16_static_for<0, 2 * C::NB>([&](auto jc) { dma_bp_first(jc); });
             g16_static_for<0, 2 * C::NA>([&](auto jc) { dma_a(0, 0, jc); });
             g16_static_for<0, 2 * C::NB>([&](auto jc) { dma_bp(1, 0, jc); });
