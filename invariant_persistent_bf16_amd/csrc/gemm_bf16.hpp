@@ -481,9 +481,9 @@ gemm_bf16_persistent(GemmParams p) {
                         as_bf16x8(cur.b[kk][in]), as_bf16x8(cur.a[kk][im]), c_in, 0, 0, 0);
                 // Read r after MFMA r * NMF / NREAD, copy d after
                 // (2d + 1) NMF / (2 NC): at odd stages A's pair (first), at
-                // even stages a K-contiguous B's pair kt+3, kt+4 (stages
-                // ST-1 and ST: B's double stage 1 - ST/2), and an N-contiguous
-                // B's copies of step kt+4 at every stage.
+                // even stages a paired B's pair kt+3, kt+4 (stages ST-1 and
+                // ST: B's double stage 1 - ST/2), or B's copies of step kt+4
+                // at every stage.
                 g16_static_for<0, NREAD>([&](auto rc) {
                     constexpr int r = decltype(rc)::value;
                     if constexpr (r * C::NMF / NREAD == i)
