@@ -43,7 +43,8 @@
 //     MI355X, most where A streams from HBM).  The eight 16-byte chunks of
 //     row r sit at chunk c ^ f2(r), f2(r) = (r >> 1) & 7, so 16 lanes reading
 //     16 consecutive rows hit 16 distinct 16-byte bank groups.  Fragments
-//     are ds_read_b128.
+//     are ds_read_b128.  The 128x128 tile copies A one step at a time, as
+//     the K-contiguous B below.
 //   * a K-contiguous B, on the 256x256 and 192x256 tiles: the same 128-byte
 //     rows and swizzle, in double stages that pair the steps the other way
 //     (stages 1-2 and 3-0: B's stages sit in the slot order 1, 2, 3, 0),
@@ -197,6 +198,10 @@ gemm_bf16_persistent(GemmParams p) {
     // whole lines gained (128x128 tiles at M = 200, K = 4096: 37.8 -> 43.3
     // us), and B is copied one step at a time in 64-byte rows.
     constexpr bool BP = B_KCONTIG && BN == 256 && BM >= 192;
+    // A is copied in pairs of K steps except on the 128x128 tile, whose
+    // single round of tiles at small M waits on the queue's depth (M = 200,
+    // K = 4096: 35.7 us one step at a time, 37.5 us in pairs).
+    constexpr bool AP = !(BM == 128 && BN == 128);
     __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
 
     const int tid = threadIdx.x;
@@ -236,11 +241,18 @@ gemm_bf16_persistent(GemmParams p) {
         uint32_t a_fb[2][2], b_fb[4];   // K-contiguous B: b_fb[2h + kk]
         {
             const int R0 = wm * C::WROWS + (lane_t & 31);
-            const int x = (lane_t >> 5) ^ ((R0 >> 1) & 7);
+            if constexpr (AP) {
+                const int x = (lane_t >> 5) ^ ((R0 >> 1) & 7);
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+                for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) a_fb[h][kk] = lds0 + R0 * 128 + ((x ^ (2 * kk) ^ (4 * h)) << 4);
+                    for (int kk = 0; kk < 2; ++kk) a_fb[h][kk] = lds0 + R0 * 128 + ((x ^ (2 * kk) ^ (4 * h)) << 4);
+            } else {
+                const int x = (lane_t >> 5) ^ ((R0 >> 2) & 3);
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) a_fb[0][kk] = lds0 + R0 * 64 + ((x ^ (2 * kk)) << 4);
+                a_fb[1][0] = a_fb[1][1] = 0;
+            }
             if constexpr (BP) {
                 const int N0 = wn * C::WCOLS + (lane_t & 31);
                 const int xb = (lane_t >> 5) ^ ((N0 >> 1) & 7);
@@ -295,7 +307,7 @@ gemm_bf16_persistent(GemmParams p) {
         // N-contiguous B: copy j covers K rows 8w + 2j + lane/32; the lane writes
         // physical chunk lane&31 of that row, i.e. logical chunk
         // (lane&31) ^ 4(krow&3), columns clamped to the last valid 8.
-        uint32_t a_off[2 * C::NA], b_off[BP ? 2 * C::NB : C::NB];
+        uint32_t a_off[AP ? 2 * C::NA : C::NA], b_off[BP ? 2 * C::NB : C::NB];
         const int b_u8 = ((lane_t & 3) ^ ((lane_t >> 4) & 3)) * 8;   // one-step K-contiguous B copies
         const int u8 = ((lane_t & 7) ^ (lane_t >> 4)) * 8;   // first K of a paired copy's lane chunk, even j (odd: ^ 32)
         {
@@ -322,13 +334,19 @@ gemm_bf16_persistent(GemmParams p) {
                 }
             }
         }
-        const int a_row0 = (BM / 4) * wave + (lane_t >> 3);
-        {
+        if constexpr (AP) {
+            const int a_row0 = (BM / 4) * wave + (lane_t >> 3);
             const int64_t a_rows_left = p.M - m0 - a_row0;
 #pragma unroll
             for (int j = 0; j < 2 * C::NA; ++j)
                 a_off[j] = a_rows_left > 8 * j ? (uint32_t)(((a_row0 + 8 * j) * (int)p.sAm + (u8 ^ (32 * (j & 1)))) * 2)
                                                : G16_OOB;
+        } else {
+            const int a_row0 = (BM / 4) * wave + (lane_t >> 2);
+            const int64_t a_rows_left = p.M - m0 - a_row0;
+#pragma unroll
+            for (int j = 0; j < C::NA; ++j)
+                a_off[j] = a_rows_left > 16 * j ? (uint32_t)(((a_row0 + 16 * j) * (int)p.sAm + b_u8) * 2) : G16_OOB;
         }
         const int bn_krow0 = 8 * wave + lane_t / C::LPR;
         const __amdgpu_buffer_rsrc_t rsA = g16_rsrc(Ab), rsB = g16_rsrc(Bb);
@@ -336,6 +354,15 @@ gemm_bf16_persistent(GemmParams p) {
 
         // A copy j (0 .. 2NA-1) of the K steps kt, kt+1 into the double stage
         // at stage st (even); lanes past K read zeros.
+        // One step at a time (the 128x128 tile): copy j (0 .. NA-1) of step kt
+        // into stage st, rows (BM/4) w + 16j + lane/4 of 64 bytes, as a
+        // K-contiguous B copied one step at a time.
+        auto dma_a1 = [&](int kt, int st, auto jc) {
+            constexpr int j = decltype(jc)::value;
+            const int kleft = K32 - kt * G16_BK;
+            g16_dma(rsA, smem + st * C::A_STAGE + (wave * C::NA + j) * 1024,
+                    b_u8 < kleft ? a_off[j] : G16_OOB, (uint32_t)kt * (2u * G16_BK));
+        };
         auto dma_a = [&](int kt, int st, auto jc) {
             constexpr int j = decltype(jc)::value;
             const int kleft = K32 - kt * G16_BK;
@@ -378,7 +405,8 @@ gemm_bf16_persistent(GemmParams p) {
             constexpr int ST = decltype(stc)::value, r = decltype(rc)::value;
             if constexpr (r < 2 * IM) {
                 constexpr int kk = r / IM, im = r % IM;
-                F.a[kk][im] = g16_read128<(ST >> 1) * 2 * C::A_STAGE + im * 4096>(a_fb[ST & 1][kk]);
+                if constexpr (AP) F.a[kk][im] = g16_read128<(ST >> 1) * 2 * C::A_STAGE + im * 4096>(a_fb[ST & 1][kk]);
+                else              F.a[kk][im] = g16_read128<ST * C::A_STAGE + im * 2048>(a_fb[0][kk]);
             } else if constexpr (B_KCONTIG) {
                 if constexpr (r < 2 * IM + 2 * IN) {
                     constexpr int kk = (r - 2 * IM) / IN, in = (r - 2 * IM) % IN, slot = (ST + 3) & 3;
@@ -462,9 +490,10 @@ gemm_bf16_persistent(GemmParams p) {
             constexpr bool FIRST = decltype(firstc)::value;
             G16Frags& cur = (ST & 1) ? F1 : F0;
             G16Frags& nxt = (ST & 1) ? F0 : F1;
-            if constexpr (ST & 1)          g16_wait_vm_lgkm0<2 * C::NB>();
-            else if constexpr (BP)        g16_wait_vm_lgkm0<2 * C::NA>();
-            else                          g16_wait_vm_lgkm0<2 * C::NB + 2 * C::NA>();
+            if constexpr (!AP)             g16_wait_vm_lgkm0<2 * C::NB + 2 * C::NA>();   // steps kt+2, kt+3
+            else if constexpr (ST & 1)     g16_wait_vm_lgkm0<2 * C::NB>();
+            else if constexpr (BP)         g16_wait_vm_lgkm0<2 * C::NA>();
+            else                           g16_wait_vm_lgkm0<2 * C::NB + 2 * C::NA>();
             __builtin_amdgcn_s_barrier();
             fence_frags(cur);
             __builtin_amdgcn_sched_barrier(0);
@@ -489,13 +518,14 @@ gemm_bf16_persistent(GemmParams p) {
                     if constexpr (r * C::NMF / NREAD == i)
                         lds_read(nxt, std::integral_constant<int, (ST + 1) % 4>{}, rc);
                 });
-                constexpr int NCA = (ST & 1) ? 2 * C::NA : 0;
+                constexpr int NCA = !AP ? C::NA : (ST & 1) ? 2 * C::NA : 0;
                 constexpr int NCB = BP ? ((ST & 1) ? 0 : 2 * C::NB) : C::NB;
                 constexpr int NC = NCA + NCB;
                 g16_static_for<0, NC>([&](auto dc) {
                     constexpr int d = decltype(dc)::value;
                     if constexpr ((2 * d + 1) * C::NMF / (2 * NC) == i) {
-                        if constexpr (d < NCA)       dma_a(kt + 3, ST - 1, dc);
+                        if constexpr (d < NCA && !AP) dma_a1(kt + 4, ST, dc);
+                        else if constexpr (d < NCA)   dma_a(kt + 3, ST - 1, dc);
                         else if constexpr (BP)        dma_bp(kt + 3, 1 - ST / 2, std::integral_constant<int, d - NCA>{});
                         else                          dma_b(kt + 4, ST, std::integral_constant<int, d - NCA>{});
                     }
@@ -508,8 +538,16 @@ gemm_bf16_persistent(GemmParams p) {
         // if issued by steps -4 .. -1), wait for step 0's, read its
         // fragments.  B one step at a time: B0, A pair (0, 1), B1, B2, A pair
         // (2, 3), B3.  Paired B: B pair (-1, 0), A pair (0, 1), B pair
-        // (1, 2), A pair (2, 3).
-        if constexpr (BP) {
+        // (1, 2), A pair (2, 3).  A and B one step at a time: A0 B0, A1 B1,
+        // A2 B2, A3 B3.
+        if constexpr (!AP) {
+            g16_static_for<0, 4>([&](auto sc) {
+                constexpr int st = decltype(sc)::value;
+                g16_static_for<0, C::NA>([&](auto jc) { dma_a1(st, st, jc); });
+                g16_static_for<0, C::NB>([&](auto jc) { dma_b(st, st, jc); });
+            });
+            g16_wait_vm_lgkm0<3 * C::NB + 3 * C::NA>();
+        } else if constexpr (BP) {
             g16_static_for<0, 2 * C::NB>([&](auto jc) { dma_bp_first(jc); });
             g16_static_for<0, 2 * C::NA>([&](auto jc) { dma_a(0, 0, jc); });
             g16_static_for<0, 2 * C::NB>([&](auto jc) { dma_bp(1, 0, jc); });
