@@ -1,7 +1,8 @@
 // Cross-lane steps of a wave's xor butterflies without the LDS crossbar:
 // DPP moves within rows of 16 lanes, v_permlane16_swap / v_permlane32_swap
-// across them.  Each gives exactly the partner value(s) of the
-// __shfl_xor(x, o) form it replaces, so the sums and maxima keep their bits.
+// across them.  Each step combines a lane's value with that of lane l ^ o,
+// the partner __shfl_xor(x, o) would read, so a butterfly built from them
+// adds (or takes maxima) in the same order, bit for bit.
 #pragma once
 
 #include "common.hpp"
