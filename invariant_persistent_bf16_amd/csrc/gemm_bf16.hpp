@@ -39,8 +39,9 @@
 //   * A: stages 0-1 and 2-3 form two double stages with LDS rows of 128
 //     bytes (64 K values: the pair's two steps), filled by copies of 8 rows x
 //     128 bytes issued at every other step, so each copy request covers whole
-//     128-byte lines of A (16 rows x 64 bytes per copy ran 3-8 % slower on
-//     MI355X, most where A streams from HBM).  The eight 16-byte chunks of
+//     128-byte lines of A (16 rows x 64 bytes per copy ran 1-5 % slower on
+//     MI355X: the addmm 3 %, the attention's P V, which streams A from HBM,
+//     5 %).  The eight 16-byte chunks of
 //     row r sit at chunk c ^ f2(r), f2(r) = (r >> 1) & 7, so 16 lanes reading
 //     16 consecutive rows hit 16 distinct 16-byte bank groups.  Fragments
 //     are ds_read_b128.  The 128x128 tile copies A one step at a time, as
