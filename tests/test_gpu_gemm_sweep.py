@@ -12,6 +12,8 @@ output row stride from its seed, forces every kernel with bi_bench_gemm_tile,
 and requires identical bits from all of them; the binary32 output is checked
 against the fp64 oracle on sampled rows of every slice.  Binary32 operands get
 the same treatment over their own kernels, with any K and transposed views.
+Short K (one to four K steps, both B layouts) crosses the edges of the copies
+that fetch two K steps at a time.
 """
 import numpy as np
 import pytest
@@ -113,3 +115,24 @@ def test_random_shape_every_f32_kernel_same_bits(seed):
     got = outs[0].cpu()
     for g in range(G):
         assert_parity(to64(got[g][pick]), oracle.mm(A[g], B[g], bias, rows=pick), f"{name} slice {g}")
+
+
+@pytest.mark.parametrize("K", [8, 16, 24, 32, 40, 64, 72, 96, 104])
+@pytest.mark.parametrize("kcontig", [False, True])
+def test_short_k_every_kernel_same_bits(K, kcontig):
+    # K steps 1 .. 4: a pair of K steps whose second half is past K, a first
+    # pair of a K-contiguous B that holds only step 0, and odd step counts,
+    # through every kernel; oracle parity on all rows.
+    G, M, N = 2, 300, 264
+    A = synth.randn((G, M, K), seed=K, dtype=torch.bfloat16)
+    B = (synth.randn((G, N, K), seed=K + 1, dtype=torch.bfloat16, scale=0.05).transpose(1, 2) if kcontig
+         else synth.randn((G, K, N), seed=K + 1, dtype=torch.bfloat16, scale=0.05))
+    bias = synth.randn((N,), seed=K + 2, dtype=torch.bfloat16, scale=0.1)
+    Ad, Bd, bd = A.to(DEV), B.to(DEV), bias.to(DEV)
+    outs = {t: bi_bench.gemm_tile(Ad, Bd, t, bias=bd, out_dtype=bi.BI_F32) for t in KERNELS}
+    torch.cuda.synchronize()
+    for t in KERNELS[1:]:
+        assert bitwise_equal(outs[t], outs[0]), f"K={K} kcontig={kcontig}: kernel {t} differs"
+    got = outs[0].cpu()
+    for g in range(G):
+        assert_parity(to64(got[g]), oracle.mm(A[g], B[g], bias), f"K={K} kcontig={kcontig} slice {g}")
