@@ -468,6 +468,14 @@ def invariance_cost(Wd, bd, x0, dq, dk, dv, Y):
     sink = torch.empty(65536, dtype=torch.int32, device=dev)
     tp = _time_ms(lambda: bi_bench.read_probe(dk, sink), iters=5)
     res["hbm_read_probe_GBps"] = round(dk.numel() * 2 / (tp * 1e-3) / 1e9, 1)
+    # The request shape of a GEMM's operand copies: 512 MiB of the KV buffer
+    # read as 2 KiB rows in tiles of 256 rows, 64 or 128 bytes per row
+    # and step (one K step of a 16-bit row, or a pair of steps).
+    nb = 512 << 20
+    buf = dk.view(-1)[: nb // dk.element_size()]
+    res["row_step_read_GBps"] = {
+        str(b): round(nb / (_time_ms(lambda b=b: bi_bench.row_step_read(buf, b, sink), iters=5) * 1e-3) / 1e9, 1)
+        for b in (64, 128)}
     return res
 
 

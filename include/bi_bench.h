@@ -185,6 +185,17 @@ int bi_bench_decode_attn_splitkv(int64_t B, int64_t H, int64_t S, int64_t D, con
 int bi_bench_read_probe(const void* p, size_t bytes, void* sink, void* stream);
 
 /*
+ * bi_bench_row_step_read — reads `bytes` (a non-zero multiple of 512 KiB,
+ * `p` 16-byte aligned) as a matrix of 2 KiB rows, in tiles of 256 rows, each
+ * tile swept in column steps of `step_bytes` (64 or 128) per row: the
+ * request shape of a GEMM's operand copies of one or two K steps.  One
+ * workgroup per CU (at most one per tile) loops over the tiles; each writes
+ * 256 reduction words to `sink` (at least 1024 * CUs bytes).  Errors:
+ * BI_ERR_NULL, BI_ERR_LAYOUT, BI_ERR_UNSUPPORTED (other step sizes).
+ */
+int bi_bench_row_step_read(const void* p, size_t bytes, int step_bytes, void* sink, void* stream);
+
+/*
  * bi_bench_wave_reduce — one wave of 64 lanes: lane l holds in[l] (binary32,
  * 64 values) and writes the library's wave-wide xor-butterfly sum to out[l]
  * and maximum to out[64 + l] (out: 128 values).  Exposes the reduction the

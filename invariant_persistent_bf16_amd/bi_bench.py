@@ -33,6 +33,7 @@ _SIGS = {
     "bi_bench_decode_attn_splits": (_int, [_i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _f32, _vp, _sz,
                                            _int, _int, _int, _vp]),
     "bi_bench_read_probe": (_int, [_vp, _sz, _vp, _vp]),
+    "bi_bench_row_step_read": (_int, [_vp, _sz, _int, _vp, _vp]),
     "bi_bench_wave_reduce": (_int, [_vp, _vp, _vp]),
     "bi_bench_decode_splitkv_policy": (_int, [_i64, _i64, _i64, _int]),
     "bi_bench_decode_splitkv_workspace_bytes": (_sz, [_i64, _i64, _i64, _int]),
@@ -177,6 +178,12 @@ def decode_attn_splits(q, k, v, scale, splits, out=None, out_dtype=_bi.BI_F32, w
 def read_probe(buf, sink, stream=None):
     _check("bi_bench_read_probe", lib().bi_bench_read_probe(
         _p(buf), buf.numel() * buf.element_size(), _p(sink), _stream(stream)))
+
+
+def row_step_read(buf, step_bytes, sink, stream=None):
+    """Read buf (a multiple of 512 KiB) as 2 KiB rows in tiles of 256, step_bytes (64 or 128) per row and step."""
+    _check("bi_bench_row_step_read", lib().bi_bench_row_step_read(
+        _p(buf), buf.numel() * buf.element_size(), int(step_bytes), _p(sink), _stream(stream)))
 
 
 def addmm_events(bias, A, B, start, stop, out=None, out_dtype=None, stream=None):

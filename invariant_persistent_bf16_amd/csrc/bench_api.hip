@@ -133,6 +133,35 @@ __global__ void read_probe_kernel(const u32x4_t* __restrict__ p, int64_t n16, ui
     if (threadIdx.x == 0) sink[blockIdx.x] = acc;
 }
 
+// Read shape of a GEMM's A copies: a matrix of 2 KiB rows read in tiles of
+// 256 rows, each tile swept in column steps of BYTES bytes per row (lanes
+// BYTES/16 to a row), four steps' loads in flight per thread, a persistent
+// grid over the tiles.
+template <int BYTES>
+__global__ void __launch_bounds__(256) row_step_probe_kernel(const u32x4_t* __restrict__ p, int64_t tiles,
+                                                             uint32_t* __restrict__ sink) {
+    constexpr int LPR = BYTES / 16;          // lanes per row in one step
+    constexpr int PER = LPR;                 // 16-byte pieces per thread and step (256 rows x LPR / 256)
+    constexpr int STEPS = 2048 / BYTES;
+    const int tid = threadIdx.x;
+    uint32_t acc = 0;
+    for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+        const u32x4_t* base = p + t * (256 * 128);   // 256 rows x 128 pieces
+#pragma unroll 4
+        for (int st = 0; st < STEPS; ++st) {
+            u32x4_t v[PER];
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                const int q = tid + 256 * i, row = q / LPR, c = q % LPR;
+                v[i] = __builtin_nontemporal_load(base + row * 128 + st * LPR + c);
+            }
+#pragma unroll
+            for (int i = 0; i < PER; ++i) acc ^= v[i][0] ^ v[i][3];
+        }
+    }
+    sink[blockIdx.x * 256 + tid] = acc;
+}
+
 // One wave: the shared xor-butterfly sum and maximum of in[0 .. 63].
 __global__ void __launch_bounds__(64) wave_reduce_kernel(const float* __restrict__ in, float* __restrict__ out) {
     const int l = threadIdx.x;
@@ -429,6 +458,24 @@ int bi_bench_read_probe(const void* p, size_t bytes, void* sink, void* stream) {
     const int grid = (int)std::min<int64_t>(std::max<int64_t>(1, cdiv(n16, 256)), std::min(65536, 16 * cus));
     hipLaunchKernelGGL(read_probe_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream,
                        (const u32x4_t*)p, n16, (uint32_t*)sink);
+    return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_LAUNCH;
+}
+
+int bi_bench_row_step_read(const void* p, size_t bytes, int step_bytes, void* sink, void* stream) {
+    if (!p || !sink) return BI_ERR_NULL;
+    constexpr size_t TILE = 256 * 2048;
+    if (bytes == 0 || bytes % TILE || ((uintptr_t)p % 16)) return BI_ERR_LAYOUT;
+    int cus = 0;
+    int rc = device_cu_count(&cus);
+    if (rc != BI_OK) return rc;
+    const int64_t tiles = (int64_t)(bytes / TILE);
+    const int grid = (int)std::min<int64_t>(tiles, cus);
+    const hipStream_t st = (hipStream_t)stream;
+    switch (step_bytes) {
+        case 64:  hipLaunchKernelGGL(row_step_probe_kernel<64>, dim3(grid), dim3(256), 0, st, (const u32x4_t*)p, tiles, (uint32_t*)sink); break;
+        case 128: hipLaunchKernelGGL(row_step_probe_kernel<128>, dim3(grid), dim3(256), 0, st, (const u32x4_t*)p, tiles, (uint32_t*)sink); break;
+        default: return BI_ERR_UNSUPPORTED;
+    }
     return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_LAUNCH;
 }
 

@@ -124,6 +124,30 @@ def test_read_probe_runs():
     torch.cuda.synchronize()
 
 
+def test_row_step_read_runs_and_reduces_the_same_data():
+    # The same 2 MiB (four tiles) read in 64- and 128-byte row steps:
+    # the xor of a workgroup's 256 words covers the same pieces whatever the
+    # step, and equals that of the pieces computed on the host.
+    gen = torch.Generator().manual_seed(3)
+    host = torch.randint(0, 1 << 30, ((1 << 21) // 4,), dtype=torch.int32, generator=gen)
+    buf = host.to(DEV)
+    sinks = []
+    for b in (64, 128):
+        sink = torch.zeros(256 * 256, dtype=torch.int32, device=DEV)
+        bi_bench.row_step_read(buf, b, sink)
+        sinks.append(sink)
+    torch.cuda.synchronize()
+    words = [np.bitwise_xor.reduce(x.cpu().numpy().reshape(256, 256), axis=1) for x in sinks]
+    assert all(np.array_equal(words[0], w) for w in words[1:])
+    pieces = host.numpy().reshape(4, -1, 4)            # tile, 16-byte piece, word
+    want = np.bitwise_xor.reduce(pieces[:, :, 0] ^ pieces[:, :, 3], axis=1)
+    assert np.array_equal(words[0][:4], want)
+    with pytest.raises(Exception):
+        bi_bench.row_step_read(buf, 96, sinks[0])
+    with pytest.raises(Exception):
+        bi_bench.row_step_read(buf[:1000], 64, sinks[0])
+
+
 @pytest.mark.parametrize("M", [1, 200, 2048])
 def test_addmm_events_same_bits_and_kernel_time(M):
     # bi_bench_addmm_events is bi_addmm with events attached to the GEMM
